@@ -1,0 +1,216 @@
+"""Block-manager model: the oracle for block tables, refcounts, the free list,
+slot mapping and copy-on-write pairs.
+
+Test infrastructure only (see oracle/__init__.py).  A plain Python model of
+what the pages describe; the product's C++ block manager is checked against it
+operation by operation, bit for bit.
+
+Sources (named by address, sections as the pages number them):
+  [5688vip]       5688vip.com, "4、PagedAttention：显存管理、分页机制、块大小选择"
+  [n1n]           explore.n1n.ai, "PagedAttention 对比传统 KV 缓存：vLLM 如何重塑
+                  LLM 推理的 GPU 显存管理"
+  [lpnh-2758356]  lpnh.cn/news/2758356, sections 1-5
+  [lpnh-1824136]  lpnh.cn/news/1824136, sections 1-4
+
+Rules modelled:
+  * The pool starts as every physical id 0..N-1 on a free list; allocation
+    takes the id at the END of that list and fails (returns None) when the
+    list is empty ([n1n] code example under "实现逻辑代码示例").
+  * A sequence is given blocks for its current tokens only; a new block is
+    appended to its table when its last block is full or it has none
+    ([5688vip] 分页机制; [n1n] 工作原理; [lpnh-2758356] 3.1).
+  * Each allocated block carries a reference count set to 1; releasing a
+    sequence walks its table, decrements each count and returns blocks that
+    reach 0 to the free list ([lpnh-2758356] 3.2).
+  * Forking shares the parent's blocks: the child's table points at the same
+    ids and each count grows by one ([lpnh-2758356] 4.2, first step).
+  * Writing into a shared block that still has free slots copies it first:
+    allocate, copy the whole block, decrement the old count, repoint the
+    table entry ([lpnh-2758356] 4.2, second and third steps).  A shared block
+    that is already full is never copied: the next token simply gets a fresh
+    block ([lpnh-2758356] 4.2, the closing remark on when COW fires).
+  * Slot of logical position p: table[p // B] * B + p % B ([5688vip]
+    分页机制 figure; [lpnh-2758356] 2.2).
+
+Readings where the pages leave a step open (also listed in the design doc):
+  * Fill level is tracked per sequence (its length) rather than per block;
+    for an unshared block the two agree, and for a shared block the
+    per-sequence length is what decides whether the writer's next slot is
+    free.
+  * Any operation that runs out of blocks changes nothing and reports OOM.
+  * A batch of appends is processed in the order given; samples that share a
+    block therefore copy one after another until the last holder finds a
+    count of 1 and writes in place.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence, Tuple
+
+
+class OOM(Exception):
+    """No free block was available; the model state is unchanged."""
+
+
+class StateError(Exception):
+    """Unknown sequence, duplicate id, or a block that is not free."""
+
+
+@dataclass
+class _Seq:
+    table: List[int] = field(default_factory=list)
+    length: int = 0
+
+
+class BlockManagerModel:
+    def __init__(self, num_blocks: int, block_size: int):
+        if num_blocks < 0 or block_size <= 0:
+            raise ValueError("num_blocks >= 0 and block_size > 0 required")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.free: List[int] = list(range(num_blocks))
+        self.refcount: List[int] = [0] * num_blocks
+        self.seqs: Dict[int, _Seq] = {}
+
+    # -- allocation ---------------------------------------------------------
+    def _alloc(self) -> Optional[int]:
+        if not self.free:
+            return None
+        b = self.free.pop()
+        self.refcount[b] = 1
+        return b
+
+    def blocks_for(self, n_tokens: int) -> int:
+        return -(-n_tokens // self.block_size)
+
+    # -- sequence operations ------------------------------------------------
+    def add_sequence(self, seq: int, n_tokens: int) -> List[int]:
+        """Allocate blocks for a new sequence of n_tokens; return its slots."""
+        if seq in self.seqs:
+            raise StateError(f"sequence {seq} exists")
+        if n_tokens < 0:
+            raise ValueError("n_tokens must be >= 0")
+        need = self.blocks_for(n_tokens)
+        if need > len(self.free):
+            raise OOM()
+        s = _Seq()
+        for _ in range(need):
+            s.table.append(self._alloc())
+        s.length = n_tokens
+        self.seqs[seq] = s
+        return [self.slot(seq, p) for p in range(n_tokens)]
+
+    def set_table(self, seq: int, blocks: Sequence[int], n_tokens: int) -> None:
+        """Give a new sequence an explicit table (ids must be free)."""
+        if seq in self.seqs:
+            raise StateError(f"sequence {seq} exists")
+        blocks = [int(b) for b in blocks]
+        if len(blocks) != self.blocks_for(n_tokens):
+            raise ValueError("table length must be ceil(n_tokens / block_size)")
+        if len(set(blocks)) != len(blocks):
+            raise StateError("duplicate block id in table")
+        free_set = set(self.free)
+        for b in blocks:
+            if not (0 <= b < self.num_blocks) or b not in free_set:
+                raise StateError(f"block {b} is not free")
+        taken = set(blocks)
+        self.free = [b for b in self.free if b not in taken]
+        for b in blocks:
+            self.refcount[b] = 1
+        self.seqs[seq] = _Seq(table=list(blocks), length=n_tokens)
+
+    def fork(self, parent: int, child: int) -> None:
+        if parent not in self.seqs:
+            raise StateError(f"unknown sequence {parent}")
+        if child in self.seqs:
+            raise StateError(f"sequence {child} exists")
+        p = self.seqs[parent]
+        for b in p.table:
+            self.refcount[b] += 1
+        self.seqs[child] = _Seq(table=list(p.table), length=p.length)
+
+    def append_token(self, seq: int) -> Tuple[int, Optional[Tuple[int, int]]]:
+        """Reserve the slot for the sequence's next token.
+
+        Returns (slot, cow) where cow is (src, dst) when the shared last
+        block had to be copied, else None.  Raises OOM with no change."""
+        if seq not in self.seqs:
+            raise StateError(f"unknown sequence {seq}")
+        s = self.seqs[seq]
+        B = self.block_size
+        n = s.length
+        cow = None
+        if n % B == 0:
+            # no block yet, or the last one is full: take a fresh block
+            b = self._alloc()
+            if b is None:
+                raise OOM()
+            s.table.append(b)
+        else:
+            last = s.table[-1]
+            if self.refcount[last] > 1:
+                b = self._alloc()
+                if b is None:
+                    raise OOM()
+                cow = (last, b)
+                self.refcount[last] -= 1
+                s.table[-1] = b
+        s.length = n + 1
+        return self.slot(seq, n), cow
+
+    def free_sequence(self, seq: int) -> None:
+        if seq not in self.seqs:
+            raise StateError(f"unknown sequence {seq}")
+        s = self.seqs.pop(seq)
+        for b in s.table:
+            self.refcount[b] -= 1
+            if self.refcount[b] == 0:
+                self.free.append(b)
+
+    # -- queries ------------------------------------------------------------
+    def slot(self, seq: int, pos: int) -> int:
+        s = self.seqs[seq]
+        B = self.block_size
+        if not 0 <= pos < len(s.table) * B:
+            raise IndexError(pos)
+        return s.table[pos // B] * B + pos % B
+
+    def table(self, seq: int) -> List[int]:
+        return list(self.seqs[seq].table)
+
+    def length(self, seq: int) -> int:
+        return self.seqs[seq].length
+
+    def tables(self, seqs: Sequence[int], max_blocks: int) -> Tuple[List[List[int]], List[int]]:
+        rows, lens = [], []
+        for q in seqs:
+            t = self.seqs[q].table
+            if len(t) > max_blocks:
+                raise ValueError("max_blocks too small")
+            rows.append(t + [-1] * (max_blocks - len(t)))
+            lens.append(self.seqs[q].length)
+        return rows, lens
+
+    def num_free(self) -> int:
+        return len(self.free)
+
+    def check_invariants(self) -> None:
+        """Counts equal the number of tables holding each block; free ids
+        have count 0; every id is either free or held."""
+        held: Dict[int, int] = {}
+        for s in self.seqs.values():
+            if len(set(s.table)) != len(s.table):
+                raise AssertionError("duplicate id within a table")
+            if len(s.table) != self.blocks_for(s.length):
+                raise AssertionError("table length != ceil(len / B)")
+            for b in s.table:
+                held[b] = held.get(b, 0) + 1
+        for b in range(self.num_blocks):
+            if self.refcount[b] != held.get(b, 0):
+                raise AssertionError(f"refcount[{b}]={self.refcount[b]} held={held.get(b, 0)}")
+        if len(set(self.free)) != len(self.free):
+            raise AssertionError("duplicate id on the free list")
+        if set(self.free) & set(held):
+            raise AssertionError("a held block is on the free list")
+        if len(self.free) + len(held) != self.num_blocks:
+            raise AssertionError("free + held != num_blocks")
