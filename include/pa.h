@@ -1,0 +1,255 @@
+/*
+ * pa.h -- C ABI of the paged-KV-cache hot path for AMD Instinct MI355X
+ * (gfx950).  Library: paged_kv_cache_390_amd/libpa.so.
+ *
+ * Sources cited below (pages named by address, sections as they number them):
+ *   [5688vip]       5688vip.com, "4、PagedAttention：显存管理、分页机制、块大小选择"
+ *   [n1n]           explore.n1n.ai, "PagedAttention 对比传统 KV 缓存：vLLM 如何重塑
+ *                   LLM 推理的 GPU 显存管理"
+ *   [lpnh-2758356]  lpnh.cn/news/2758356 (block mapping, on-demand allocation,
+ *                   copy-on-write), sections 1-5
+ *   [lpnh-1824136]  lpnh.cn/news/1824136 (the SOSP 2023 paper and vLLM),
+ *                   sections 1-4
+ *
+ * Conventions shared by every GPU call
+ *   - Cache layout: one K and one V tensor per layer, each
+ *     [num_blocks, num_kv_heads, block_size, head_dim], fp16, contiguous.
+ *     A physical block id indexes every layer's tensors, so one block table
+ *     serves all layers ([lpnh-2758356] 2.1: per-block shape block_size x
+ *     kv heads x head_dim, layers with their own block sets of one size).
+ *   - Token position p of a sequence lives at slot table[p / B] * B + p % B,
+ *     i.e. block table[p / B], row p % B ([5688vip] 分页机制 figure;
+ *     [lpnh-2758356] 2.2).
+ *   - All device buffers belong to the caller; the library never allocates
+ *     device memory.  Pointers marked "device" must be device-accessible;
+ *     every other pointer is host memory.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ *     the null stream).  The call returns once the kernels are enqueued.
+ *   - Argument errors are found before anything is enqueued and leave every
+ *     output untouched.  Device-resident indices (slots, table entries, copy
+ *     pairs) cannot be checked without a device-to-host copy; instead the
+ *     kernels skip any that fall outside the pool, so a bad index is never
+ *     dereferenced (see each call for what the output then holds).
+ *   - dtype: PA_DTYPE_F16 is the only element type.
+ *   - head_dim in {16, 32, 64, 128, 256}; block_size in {1, 2, 4, 8, 16, 32,
+ *     64, 128} (PA_ERR_UNSUPPORTED otherwise).
+ *
+ * Every function returns PA_OK (0) or a negative PA_ERR_* code, except where
+ * stated.  pa_last_error() gives a message for the calling thread's last
+ * failure.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    PA_OK = 0,
+    PA_COW = 1,               /* append: a copy-on-write pair was produced   */
+    PA_ERR_INVALID = -1,      /* null pointer, bad size or inconsistent dims */
+    PA_ERR_UNSUPPORTED = -2,  /* dtype, head_dim or block_size not built     */
+    PA_ERR_HIP = -3,          /* the HIP runtime reported an error           */
+    PA_ERR_OOM = -4,          /* block manager: no free block                */
+    PA_ERR_STATE = -5         /* block manager: unknown / duplicate sequence,
+                                 block not free                              */
+};
+
+enum { PA_DTYPE_F16 = 0 };
+
+/* Message for the calling thread's most recent failed call ("" if none). */
+const char *pa_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Slot-mapped cache write ("reshape and cache").
+ * The new tokens' K and V vectors are written into the blocks their tables
+ * assign ([lpnh-1824136] 3.1: results are scattered back into the proper
+ * blocks; [5688vip] 分页机制: a token goes into the current block while it
+ * has room).
+ *
+ *   key, value     device, fp16, token t head h at element
+ *                  t * kv_token_stride + h * head_dim (head_dim contiguous)
+ *   kv_token_stride elements between consecutive tokens (>= Hkv * head_dim)
+ *   slot_mapping   device, int64 [num_tokens]; token t goes to block
+ *                  slot / block_size, row slot % block_size.  A negative
+ *                  slot, or one >= num_blocks * block_size, is skipped.
+ *                  Slots within one call must be distinct.
+ *   k_cache, v_cache  device, fp16 [num_blocks, num_kv_heads, block_size,
+ *                  head_dim]; updated in place, bit-exact copies.
+ * num_tokens == 0 enqueues nothing.
+ * ------------------------------------------------------------------------ */
+int pa_reshape_and_cache(const void *key, const void *value,
+                         int64_t kv_token_stride,
+                         const int64_t *slot_mapping, int32_t num_tokens,
+                         void *k_cache, void *v_cache, int32_t num_blocks,
+                         int32_t num_kv_heads, int32_t block_size,
+                         int32_t head_dim, int32_t dtype, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Single-query decode attention over the paged cache.
+ * Each sequence's new token attends to all of its cached K/V, read through
+ * its block table ([lpnh-1824136] 2.2 and 3.2 step 4: the kernel looks up
+ * the table and reads history K/V from scattered blocks; [lpnh-2758356] 2.2:
+ * the result is that of ordinary attention over the logically contiguous
+ * K/V).  The pages give no formula; computed is scaled dot-product softmax
+ * attention, out = softmax(scale * K q) V over positions [0, n), with
+ * fp32 accumulation and fp16 (round to nearest even) output.
+ *
+ *   out            device, fp16 [num_seqs, num_heads, head_dim], written
+ *   q              device, fp16 [num_seqs, num_heads, head_dim]
+ *   k_cache, v_cache  device, fp16 [num_blocks, num_kv_heads, block_size,
+ *                  head_dim]
+ *   block_tables   device, int32 [num_seqs, max_blocks_per_seq]; entries past
+ *                  ceil(n / block_size) are never read
+ *   context_lens   device, int32 [num_seqs]; n for each sequence, including
+ *                  the token just written.  n == 0 gives an all-zero row.
+ *   num_heads      query heads; num_heads % num_kv_heads == 0 and query head
+ *                  h reads KV head h / (num_heads / num_kv_heads)
+ *   scale          multiplies q.k (1/sqrt(head_dim) in the usual model)
+ *   max_context_len  host-known upper bound on every n; it sizes the grid so
+ *                  that no device-to-host read is needed.  A row whose n
+ *                  exceeds it, or exceeds max_blocks_per_seq * block_size,
+ *                  comes out as NaN.
+ *   partition_size tokens per context partition, a multiple of 128 (0 picks
+ *                  a default).  Sequences longer than one partition are split
+ *                  across workgroups and merged by a second kernel.
+ *   workspace      device scratch of at least pa_decode_workspace_size()
+ *                  bytes, or NULL when that size is 0.  Contents on entry are
+ *                  ignored; calls sharing a workspace must be stream-ordered.
+ * Table entries outside [0, num_blocks) are skipped: their tokens take no
+ * part in the softmax.
+ * ------------------------------------------------------------------------ */
+int pa_decode(void *out, const void *q, const void *k_cache,
+              const void *v_cache, const int32_t *block_tables,
+              int32_t max_blocks_per_seq, const int32_t *context_lens,
+              int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+              float scale, int32_t max_context_len, int32_t partition_size,
+              void *workspace, size_t workspace_bytes, int32_t dtype,
+              void *stream);
+
+/* Bytes of workspace pa_decode needs for these sizes (0 when every sequence
+ * fits one partition).  partition_size as for pa_decode (0 = default).
+ * Returns (size_t)-1 for invalid arguments. */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                int32_t head_dim, int32_t max_context_len,
+                                int32_t partition_size);
+
+/* The partition size pa_decode uses when given 0. */
+int32_t pa_decode_default_partition(int32_t head_dim, int32_t block_size);
+
+/* ------------------------------------------------------------------------
+ * Whole-block copies for copy-on-write.
+ * A writer holding a shared block that still has free rows gets a new block
+ * holding a copy of the shared one ([lpnh-2758356] 4.2, third step; 4.3 on
+ * the bandwidth this costs).
+ *
+ *   k_caches, v_caches  HOST arrays of num_layers device pointers, each a
+ *                  cache tensor of num_blocks blocks of block_elems fp16
+ *   src_dst_pairs  device, int64 [num_pairs, 2]; row i copies block
+ *                  pairs[i][0] onto block pairs[i][1] in every layer, K and V.
+ *                  Destinations must be distinct and never also a source (a
+ *                  source may repeat).  A pair with an id outside
+ *                  [0, num_blocks) is skipped.
+ *   block_elems    elements per block = num_kv_heads * block_size * head_dim
+ * num_pairs == 0 or num_layers == 0 enqueues nothing.
+ * ------------------------------------------------------------------------ */
+int pa_copy_blocks(void *const *k_caches, void *const *v_caches,
+                   int32_t num_layers, const int64_t *src_dst_pairs,
+                   int32_t num_pairs, int32_t num_blocks, int64_t block_elems,
+                   int32_t dtype, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Host block manager: free list, reference counts, per-sequence tables.
+ * Host memory only; every call takes an internal lock, so calls from
+ * several threads are serialised ([lpnh-2758356] 4.3: count updates must be
+ * atomic).
+ *
+ * Rules ([n1n] 实现逻辑代码示例; [5688vip] 分页机制; [lpnh-2758356] 3.1, 3.2, 4.2):
+ *   - the pool starts as ids 0..num_blocks-1 on a free list; an allocation
+ *     takes the id at its end; a freed id is pushed on its end;
+ *   - a new block is appended to a table only when the sequence has none or
+ *     its last block is full;
+ *   - every allocated block has a count of holders; fork adds one per block;
+ *   - appending into a shared block (count > 1) that still has free rows
+ *     first copies it: a new block replaces it in this table, the old count
+ *     drops by one and the pair (old, new) is reported for pa_copy_blocks;
+ *     a shared block that is full is never copied;
+ *   - freeing a sequence drops each of its blocks' counts and returns blocks
+ *     whose count reaches 0.
+ * Any call that fails (OOM included) leaves the state unchanged, except the
+ * batched append, which applies the appends before the failing one.
+ * ------------------------------------------------------------------------ */
+typedef struct pa_bm pa_bm;
+
+/* NULL on bad sizes or out of host memory. */
+pa_bm *pa_bm_create(int32_t num_blocks, int32_t block_size);
+void pa_bm_destroy(pa_bm *bm);
+
+/* New sequence with n_tokens tokens: ceil(n_tokens / B) blocks taken from
+ * the free list in logical order.  slots_out (may be NULL) receives the
+ * n_tokens slots.  PA_ERR_STATE if seq exists, PA_ERR_OOM if short of
+ * blocks. */
+int pa_bm_add_sequence(pa_bm *bm, int64_t seq, int32_t n_tokens,
+                       int64_t *slots_out);
+
+/* New sequence with an explicit table: nblk == ceil(n_tokens / B) distinct
+ * ids, each currently free; they leave the free list (the rest keep their
+ * order) with a count of 1. */
+int pa_bm_set_table(pa_bm *bm, int64_t seq, const int32_t *blocks,
+                    int32_t nblk, int32_t n_tokens);
+
+/* child shares every block of parent (counts + 1) and its length. */
+int pa_bm_fork(pa_bm *bm, int64_t parent, int64_t child);
+
+/* Reserve the slot of seq's next token.  Returns PA_OK, or PA_COW when the
+ * shared last block had to be copied (then *cow_src / *cow_dst hold the
+ * pair; otherwise they are set to -1).  Output pointers may be NULL. */
+int pa_bm_append_token(pa_bm *bm, int64_t seq, int64_t *slot_out,
+                       int64_t *cow_src, int64_t *cow_dst);
+
+/* Batched append, in the order given.  slots_out[n]; cow_pairs_out receives
+ * up to n (src, dst) rows and *num_cow_out their count; *num_done_out the
+ * number of appends applied.  Stops at the first failure and returns its
+ * code (the appends before it stay applied). */
+int pa_bm_append_tokens(pa_bm *bm, const int64_t *seqs, int32_t n,
+                        int64_t *slots_out, int64_t *cow_pairs_out,
+                        int32_t *num_cow_out, int32_t *num_done_out);
+
+/* Release seq: counts - 1, ids reaching 0 pushed on the free list in
+ * logical order. */
+int pa_bm_free_sequence(pa_bm *bm, int64_t seq);
+
+/* Pack tables of the given sequences into tables_out[n, max_blocks] (padding
+ * -1) and their lengths into lens_out[n] (may be NULL).  PA_ERR_INVALID if a
+ * table is longer than max_blocks. */
+int pa_bm_get_tables(pa_bm *bm, const int64_t *seqs, int32_t n,
+                     int32_t *tables_out, int32_t max_blocks,
+                     int32_t *lens_out);
+
+/* Slots of positions [pos_begin, pos_begin + count) of seq; every position
+ * must lie inside its table (< table length * B). */
+int pa_bm_get_slots(pa_bm *bm, int64_t seq, int32_t pos_begin, int32_t count,
+                    int64_t *slots_out);
+
+/* Holders of block blk (0 if free); -1 if blk is outside the pool. */
+int32_t pa_bm_refcount(pa_bm *bm, int32_t blk);
+/* Number of free blocks. */
+int32_t pa_bm_num_free(pa_bm *bm);
+/* Copies min(count, cap) free ids, bottom of the list first, into out;
+ * returns count. */
+int32_t pa_bm_free_list(pa_bm *bm, int32_t *out, int32_t cap);
+/* Length of seq, or -1 if unknown. */
+int32_t pa_bm_seq_len(pa_bm *bm, int64_t seq);
+/* Table length of seq, or -1 if unknown. */
+int32_t pa_bm_seq_blocks(pa_bm *bm, int64_t seq);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,299 @@
+// Host block manager: free list, per-block holder counts and per-sequence
+// block tables.  Builds what the GPU calls consume: int32 tables, int32
+// lengths, int64 slots and int64 copy-on-write pairs.
+//
+// Sources (pages named by address, sections as they number them):
+//   [5688vip]       5688vip.com, "4、PagedAttention：显存管理、分页机制、块大小选择",
+//                   section 分页机制 (append a block when the last one is full)
+//   [n1n]           explore.n1n.ai, "PagedAttention 对比传统 KV 缓存", section
+//                   实现逻辑代码示例 (free list popped from its end; failure
+//                   when it is empty)
+//   [lpnh-2758356]  lpnh.cn/news/2758356: 3.1 (grow on demand), 3.2 (status,
+//                   count and address per block; release walks the table),
+//                   4.2 (fork shares blocks; writing into a shared block that
+//                   is not full copies it; a full one is never copied), 4.3
+//                   (count updates must be atomic)
+//
+// Design: the state is a vector of counts, a vector used as the free stack
+// and a hash map from sequence id to (table, length).  Every public call
+// validates first, then mutates, so a failing call changes nothing.  One
+// mutex serialises calls.
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+struct Seq {
+    std::vector<int32_t> table;
+    int64_t len = 0;
+};
+
+}  // namespace
+
+struct pa_bm {
+    int32_t num_blocks;
+    int32_t block_size;
+    std::vector<int32_t> free_stack;   // allocation pops from the back
+    std::vector<int32_t> count;        // holders per block
+    std::unordered_map<int64_t, Seq> seqs;
+    std::mutex mu;
+
+    int64_t blocks_for(int64_t n) const { return (n + block_size - 1) / block_size; }
+
+    int32_t pop_free() {
+        int32_t b = free_stack.back();
+        free_stack.pop_back();
+        count[b] = 1;
+        return b;
+    }
+
+    int64_t slot_of(const Seq& s, int64_t pos) const {
+        return (int64_t)s.table[pos / block_size] * block_size + pos % block_size;
+    }
+
+    // Append one token; assumes seq exists.  Fails with OOM before mutating.
+    int append(Seq& s, int64_t* slot, int64_t* src, int64_t* dst) {
+        *src = -1;
+        *dst = -1;
+        const int64_t n = s.len;
+        int rc = PA_OK;
+        if (n % block_size == 0) {
+            // no block yet, or the last block is full: a fresh block
+            if (free_stack.empty()) return PA_ERR_OOM;
+            s.table.push_back(pop_free());
+        } else {
+            const int32_t last = s.table.back();
+            if (count[last] > 1) {
+                // shared and not full: copy on write
+                if (free_stack.empty()) return PA_ERR_OOM;
+                const int32_t fresh = pop_free();
+                count[last] -= 1;
+                s.table.back() = fresh;
+                *src = last;
+                *dst = fresh;
+                rc = PA_COW;
+            }
+        }
+        s.len = n + 1;
+        *slot = slot_of(s, n);
+        return rc;
+    }
+};
+
+extern "C" {
+
+pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size) {
+    if (num_blocks < 0 || block_size <= 0) {
+        pa::set_error("pa_bm_create: num_blocks >= 0 and block_size > 0 required");
+        return nullptr;
+    }
+    pa_bm* bm = new (std::nothrow) pa_bm();
+    if (!bm) {
+        pa::set_error("pa_bm_create: out of host memory");
+        return nullptr;
+    }
+    try {
+        bm->num_blocks = num_blocks;
+        bm->block_size = block_size;
+        bm->free_stack.resize(num_blocks);
+        for (int32_t i = 0; i < num_blocks; ++i) bm->free_stack[i] = i;
+        bm->count.assign(num_blocks, 0);
+    } catch (...) {
+        delete bm;
+        pa::set_error("pa_bm_create: out of host memory");
+        return nullptr;
+    }
+    return bm;
+}
+
+void pa_bm_destroy(pa_bm* bm) { delete bm; }
+
+int pa_bm_add_sequence(pa_bm* bm, int64_t seq, int32_t n_tokens, int64_t* slots_out) {
+    if (!bm || n_tokens < 0) return pa::fail(PA_ERR_INVALID, "pa_bm_add_sequence: bad argument");
+    std::lock_guard<std::mutex> g(bm->mu);
+    if (bm->seqs.count(seq)) return pa::fail(PA_ERR_STATE, "pa_bm_add_sequence: sequence %lld exists", (long long)seq);
+    const int64_t need = bm->blocks_for(n_tokens);
+    if (need > (int64_t)bm->free_stack.size())
+        return pa::fail(PA_ERR_OOM, "pa_bm_add_sequence: need %lld blocks, %zu free", (long long)need, bm->free_stack.size());
+    Seq s;
+    s.table.reserve(need);
+    for (int64_t i = 0; i < need; ++i) s.table.push_back(bm->pop_free());
+    s.len = n_tokens;
+    if (slots_out)
+        for (int64_t p = 0; p < n_tokens; ++p) slots_out[p] = bm->slot_of(s, p);
+    bm->seqs.emplace(seq, std::move(s));
+    return PA_OK;
+}
+
+int pa_bm_set_table(pa_bm* bm, int64_t seq, const int32_t* blocks, int32_t nblk, int32_t n_tokens) {
+    if (!bm || n_tokens < 0 || nblk < 0 || (nblk > 0 && !blocks))
+        return pa::fail(PA_ERR_INVALID, "pa_bm_set_table: bad argument");
+    std::lock_guard<std::mutex> g(bm->mu);
+    if (nblk != bm->blocks_for(n_tokens))
+        return pa::fail(PA_ERR_INVALID, "pa_bm_set_table: %d blocks given, %lld needed", nblk, (long long)bm->blocks_for(n_tokens));
+    if (bm->seqs.count(seq)) return pa::fail(PA_ERR_STATE, "pa_bm_set_table: sequence %lld exists", (long long)seq);
+    std::unordered_set<int32_t> taken;
+    for (int32_t i = 0; i < nblk; ++i) {
+        const int32_t b = blocks[i];
+        if (b < 0 || b >= bm->num_blocks || bm->count[b] != 0 || !taken.insert(b).second)
+            return pa::fail(PA_ERR_STATE, "pa_bm_set_table: block %d is not free (or repeated)", b);
+    }
+    // a block with count 0 is on the free list; drop the taken ones, keep order
+    bm->free_stack.erase(std::remove_if(bm->free_stack.begin(), bm->free_stack.end(),
+                                        [&](int32_t b) { return taken.count(b) != 0; }),
+                         bm->free_stack.end());
+    Seq s;
+    s.table.assign(blocks, blocks + nblk);
+    s.len = n_tokens;
+    for (int32_t b : s.table) bm->count[b] = 1;
+    bm->seqs.emplace(seq, std::move(s));
+    return PA_OK;
+}
+
+int pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
+    if (!bm) return pa::fail(PA_ERR_INVALID, "pa_bm_fork: null manager");
+    std::lock_guard<std::mutex> g(bm->mu);
+    auto it = bm->seqs.find(parent);
+    if (it == bm->seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_fork: unknown parent %lld", (long long)parent);
+    if (bm->seqs.count(child)) return pa::fail(PA_ERR_STATE, "pa_bm_fork: sequence %lld exists", (long long)child);
+    Seq c = it->second;
+    for (int32_t b : c.table) bm->count[b] += 1;
+    bm->seqs.emplace(child, std::move(c));
+    return PA_OK;
+}
+
+int pa_bm_append_token(pa_bm* bm, int64_t seq, int64_t* slot_out, int64_t* cow_src, int64_t* cow_dst) {
+    if (!bm) return pa::fail(PA_ERR_INVALID, "pa_bm_append_token: null manager");
+    std::lock_guard<std::mutex> g(bm->mu);
+    auto it = bm->seqs.find(seq);
+    if (it == bm->seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_append_token: unknown sequence %lld", (long long)seq);
+    int64_t slot, src, dst;
+    const int rc = bm->append(it->second, &slot, &src, &dst);
+    if (rc == PA_ERR_OOM) return pa::fail(PA_ERR_OOM, "pa_bm_append_token: no free block");
+    if (slot_out) *slot_out = slot;
+    if (cow_src) *cow_src = src;
+    if (cow_dst) *cow_dst = dst;
+    return rc;
+}
+
+int pa_bm_append_tokens(pa_bm* bm, const int64_t* seqs, int32_t n, int64_t* slots_out,
+                        int64_t* cow_pairs_out, int32_t* num_cow_out, int32_t* num_done_out) {
+    if (num_cow_out) *num_cow_out = 0;
+    if (num_done_out) *num_done_out = 0;
+    if (!bm || n < 0 || (n > 0 && (!seqs || !slots_out || !cow_pairs_out)))
+        return pa::fail(PA_ERR_INVALID, "pa_bm_append_tokens: bad argument");
+    std::lock_guard<std::mutex> g(bm->mu);
+    int32_t ncow = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        auto it = bm->seqs.find(seqs[i]);
+        if (it == bm->seqs.end())
+            return pa::fail(PA_ERR_STATE, "pa_bm_append_tokens: unknown sequence %lld", (long long)seqs[i]);
+        int64_t src, dst;
+        const int rc = bm->append(it->second, &slots_out[i], &src, &dst);
+        if (rc == PA_ERR_OOM) return pa::fail(PA_ERR_OOM, "pa_bm_append_tokens: no free block at entry %d", i);
+        if (rc == PA_COW) {
+            cow_pairs_out[2 * ncow] = src;
+            cow_pairs_out[2 * ncow + 1] = dst;
+            ++ncow;
+            if (num_cow_out) *num_cow_out = ncow;
+        }
+        if (num_done_out) *num_done_out = i + 1;
+    }
+    return PA_OK;
+}
+
+int pa_bm_free_sequence(pa_bm* bm, int64_t seq) {
+    if (!bm) return pa::fail(PA_ERR_INVALID, "pa_bm_free_sequence: null manager");
+    std::lock_guard<std::mutex> g(bm->mu);
+    auto it = bm->seqs.find(seq);
+    if (it == bm->seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_free_sequence: unknown sequence %lld", (long long)seq);
+    for (int32_t b : it->second.table) {
+        bm->count[b] -= 1;
+        if (bm->count[b] == 0) bm->free_stack.push_back(b);
+    }
+    bm->seqs.erase(it);
+    return PA_OK;
+}
+
+int pa_bm_get_tables(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* tables_out,
+                     int32_t max_blocks, int32_t* lens_out) {
+    if (!bm || n < 0 || max_blocks < 0 || (n > 0 && (!seqs || (!tables_out && max_blocks > 0))))
+        return pa::fail(PA_ERR_INVALID, "pa_bm_get_tables: bad argument");
+    std::lock_guard<std::mutex> g(bm->mu);
+    for (int32_t i = 0; i < n; ++i) {
+        auto it = bm->seqs.find(seqs[i]);
+        if (it == bm->seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_get_tables: unknown sequence %lld", (long long)seqs[i]);
+        if ((int64_t)it->second.table.size() > max_blocks)
+            return pa::fail(PA_ERR_INVALID, "pa_bm_get_tables: table of %lld has %zu blocks > %d",
+                            (long long)seqs[i], it->second.table.size(), max_blocks);
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        const Seq& s = bm->seqs.find(seqs[i])->second;
+        int32_t* row = tables_out + (int64_t)i * max_blocks;
+        const size_t k = s.table.size();
+        if (k) std::memcpy(row, s.table.data(), k * sizeof(int32_t));
+        for (int64_t j = (int64_t)k; j < max_blocks; ++j) row[j] = -1;
+        if (lens_out) lens_out[i] = (int32_t)s.len;
+    }
+    return PA_OK;
+}
+
+int pa_bm_get_slots(pa_bm* bm, int64_t seq, int32_t pos_begin, int32_t count, int64_t* slots_out) {
+    if (!bm || pos_begin < 0 || count < 0 || (count > 0 && !slots_out))
+        return pa::fail(PA_ERR_INVALID, "pa_bm_get_slots: bad argument");
+    std::lock_guard<std::mutex> g(bm->mu);
+    auto it = bm->seqs.find(seq);
+    if (it == bm->seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_get_slots: unknown sequence %lld", (long long)seq);
+    const Seq& s = it->second;
+    if ((int64_t)pos_begin + count > (int64_t)s.table.size() * bm->block_size)
+        return pa::fail(PA_ERR_INVALID, "pa_bm_get_slots: positions beyond the table");
+    for (int32_t i = 0; i < count; ++i) slots_out[i] = bm->slot_of(s, (int64_t)pos_begin + i);
+    return PA_OK;
+}
+
+int32_t pa_bm_refcount(pa_bm* bm, int32_t blk) {
+    if (!bm) return -1;
+    std::lock_guard<std::mutex> g(bm->mu);
+    if (blk < 0 || blk >= bm->num_blocks) return -1;
+    return bm->count[blk];
+}
+
+int32_t pa_bm_num_free(pa_bm* bm) {
+    if (!bm) return -1;
+    std::lock_guard<std::mutex> g(bm->mu);
+    return (int32_t)bm->free_stack.size();
+}
+
+int32_t pa_bm_free_list(pa_bm* bm, int32_t* out, int32_t cap) {
+    if (!bm) return -1;
+    std::lock_guard<std::mutex> g(bm->mu);
+    const int32_t n = (int32_t)bm->free_stack.size();
+    const int32_t k = std::min(n, std::max(cap, 0));
+    if (out && k) std::memcpy(out, bm->free_stack.data(), (size_t)k * sizeof(int32_t));
+    return n;
+}
+
+int32_t pa_bm_seq_len(pa_bm* bm, int64_t seq) {
+    if (!bm) return -1;
+    std::lock_guard<std::mutex> g(bm->mu);
+    auto it = bm->seqs.find(seq);
+    return it == bm->seqs.end() ? -1 : (int32_t)it->second.len;
+}
+
+int32_t pa_bm_seq_blocks(pa_bm* bm, int64_t seq) {
+    if (!bm) return -1;
+    std::lock_guard<std::mutex> g(bm->mu);
+    auto it = bm->seqs.find(seq);
+    return it == bm->seqs.end() ? -1 : (int32_t)it->second.table.size();
+}
+
+}  // extern "C"

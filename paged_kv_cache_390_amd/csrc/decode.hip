@@ -1,0 +1,522 @@
+// Single-query paged decode attention for gfx950 (CDNA4).
+//
+// What is computed: for every sequence s and query head h, the new token's
+// query attends to the sequence's n cached keys/values, found through its
+// block table; paging is invisible to the result, which is plain softmax
+// attention over the logically contiguous K/V (lpnh.cn/news/1824136, 2.2 and
+// 3.2 step 4; lpnh.cn/news/2758356, 2.2; the formula itself is not on the
+// pages and is taken as textbook scaled dot-product attention).
+//
+// Design (MI355X first; the pages describe no kernel):
+//  * Decode with one query per KV head is a GEMV: about one flop per byte of
+//    K/V, far below the HBM ridge, so the work runs on VALU, not MFMA, and
+//    every choice serves HBM streaming.
+//  * Grid: one 256-thread workgroup (4 wave64s) per (context partition,
+//    query head, sequence).  A partition is partition_size consecutive
+//    tokens; sequences longer than one partition are split so that long
+//    contexts still spread over all 256 CUs, and a second kernel merges the
+//    partial softmax states.  Sequences that fit one partition are finished
+//    by the first kernel directly.
+//  * Lane mapping: a token's head_dim fp16 values are 2*D bytes, read by
+//    D/8 lanes with one 16-byte load each, so one wave load moves 1 KiB of
+//    consecutive rows of a block's [block_size, head_dim] slab -- fully
+//    coalesced however the blocks are scattered.  A wave step issues 4 such
+//    loads for K and 4 for V before any math, keeping 8 KiB in flight per
+//    wave.  Steps are dealt round-robin to the 4 waves.
+//  * q.k: the lane's 8 fp16 products are summed with v_dot2_f32_f16 (fp32
+//    accumulate) and the D/8-lane partial sums are combined with DPP
+//    row/quad permutations (no LDS traffic).
+//  * Softmax: online (running max m and sum l, in base-2 units with log2(e)
+//    folded into the scale), kept separately per token row of the wave, so
+//    the inner loop needs no cross-row communication; the 4 x (64*8/D) row
+//    states of a workgroup are merged once through LDS at the end.
+//  * Masking uses selects, never a multiply by zero, so garbage or NaN in
+//    the unused rows of a tail block cannot leak; loads of masked rows are
+//    not issued at all.
+//  * The block table is read with wave-uniform (scalar) loads whenever the
+//    rows of one wave load share a block (head_dim * block_size >= 512
+//    elements); otherwise each lane looks up its own block.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // one 16-byte load
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kLoadsPerStep = 4;          // 16-byte loads per lane per step, each for K and V
+constexpr int kPartitionQuantum = 128;    // partition_size granularity (a multiple of every step)
+constexpr int kDefaultPartition = 512;
+constexpr double kLog2e = 1.4426950408889634073599246810019;
+
+// DPP controls (GFX9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7-i within each 8
+constexpr int kDppRowMirror = 0x140;      // lane i <- lane 15-i within each 16
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of G lanes; every lane of a group ends with the
+// same bits (each stage adds two equal-bit partial sums in swapped order).
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (G >= 2) v += dpp<kDppQuadXor1>(v);
+    if constexpr (G >= 4) v += dpp<kDppQuadXor2>(v);
+    if constexpr (G >= 8) v += dpp<kDppRowHalfMirror>(v);
+    if constexpr (G >= 16) v += dpp<kDppRowMirror>(v);
+    if constexpr (G >= 32) v += __shfl_xor(v, 16);
+    return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+struct Frag {
+    half2_t h[4];
+};
+
+__device__ __forceinline__ Frag as_frag(u32x4 u) { return __builtin_bit_cast(Frag, u); }
+
+// Static geometry of one (head_dim, block_size) instance.
+template <int D, int B>
+struct Geo {
+    static constexpr int LPT = D / 8;                   // lanes per token row (16 B each)
+    static constexpr int TPL = 64 / LPT;                // token rows per wave load
+    static constexpr int CH = TPL * kLoadsPerStep;      // tokens per wave step
+    static constexpr bool kUniform = TPL <= B;          // a load's rows share one block
+    static constexpr int NT = !kUniform ? kLoadsPerStep : (B >= CH ? 1 : CH / B);   // table reads per step
+    static constexpr int LPB = B >= CH ? kLoadsPerStep : B / TPL;   // loads per table read (uniform case)
+    static constexpr int64_t SLAB = (int64_t)B * D;     // elements of one (block, head) slab
+};
+
+// The K/V fragments of one step plus the validity of each load's row.
+struct StepBuf {
+    u32x4 k[kLoadsPerStep];
+    u32x4 v[kLoadsPerStep];
+    bool valid[kLoadsPerStep];
+};
+
+// Online-softmax state of one token row (identical in its D/8 lanes).
+struct RowState {
+    float m, l, acc[8];
+};
+
+template <int D>
+__device__ __forceinline__ void consume(RowState& r, const StepBuf& b, const Frag& qf, float scale_log2) {
+    constexpr int LPT = D / 8;
+    float sc[kLoadsPerStep];
+#pragma unroll
+    for (int j = 0; j < kLoadsPerStep; ++j) {
+        const Frag kh = as_frag(b.k[j]);
+        float a = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a = __builtin_amdgcn_fdot2(qf.h[i], kh.h[i], a, false);
+        sc[j] = a;
+    }
+#pragma unroll
+    for (int j = 0; j < kLoadsPerStep; ++j) sc[j] = group_sum<LPT>(sc[j]);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kLoadsPerStep; ++j) {
+        sc[j] = b.valid[j] ? sc[j] * scale_log2 : -INFINITY;
+        mx = fmaxf(mx, sc[j]);
+    }
+    const float m_new = fmaxf(r.m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(r.m - m_use);
+    r.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.acc[i] *= alpha;
+#pragma unroll
+    for (int j = 0; j < kLoadsPerStep; ++j) {
+        const float p = fast_exp2(sc[j] - m_use);
+        r.l += p;
+        // a masked row was loaded as zeros (tail) or from a clamped block
+        // (skipped id): select, so its values never reach the sum
+        const Frag vh = as_frag(b.v[j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float v0 = b.valid[j] ? (float)vh.h[i].x : 0.f;
+            const float v1 = b.valid[j] ? (float)vh.h[i].y : 0.f;
+            r.acc[2 * i] = fmaf(p, v0, r.acc[2 * i]);
+            r.acc[2 * i + 1] = fmaf(p, v1, r.acc[2 * i + 1]);
+        }
+    }
+    r.m = m_new;
+}
+
+template <int D, int B>
+__global__ void __launch_bounds__(kThreads)
+decode_partition_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
+                        const _Float16* __restrict__ q, const _Float16* __restrict__ k_cache,
+                        const _Float16* __restrict__ v_cache, const int32_t* __restrict__ tables,
+                        int32_t max_blocks, const int32_t* __restrict__ lens, int32_t num_heads,
+                        int32_t num_kv_heads, int32_t num_blocks, float scale_log2, int32_t part_size,
+                        int32_t num_parts, int64_t len_cap) {
+    using G = Geo<D, B>;
+    constexpr int LPT = G::LPT;
+    constexpr int TPL = G::TPL;
+    constexpr int CH = G::CH;
+    constexpr int NT = G::NT;
+    constexpr int NSTATE = kWaves * TPL;        // softmax states per workgroup
+
+    const int part = blockIdx.x;
+    const int h = blockIdx.y;
+    const int s = blockIdx.z;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform by construction
+    const int row = lane / LPT;
+    const int col = lane % LPT;
+
+    const int32_t n_raw = lens[s];
+    const bool bad_len = n_raw < 0 || (int64_t)n_raw > len_cap;
+    const int n = bad_len ? 0 : n_raw;
+    const int start = part * part_size;
+    if (part > 0 && start >= n) return;
+    const int end = min(start + part_size, n);
+    const int kvh = h / (num_heads / num_kv_heads);
+
+    const Frag qf = as_frag(*reinterpret_cast<const u32x4*>(q + ((int64_t)s * num_heads + h) * D + col * 8));
+
+    const int32_t* trow = tables + (int64_t)s * max_blocks;
+    const _Float16* kbase = k_cache + (int64_t)kvh * G::SLAB;
+    const _Float16* vbase = v_cache + (int64_t)kvh * G::SLAB;
+    const int64_t blk_stride = (int64_t)num_kv_heads * G::SLAB;
+
+    RowState r;
+    r.m = -INFINITY;
+    r.l = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.acc[i] = 0.f;
+
+    const int ntok = end > start ? end - start : 0;
+    const int nfull = ntok / CH;               // steps whose CH tokens are all < end
+    const bool tail = ntok % CH != 0;
+
+    // ---- full steps: unconditional loads, table prefetched one step ahead
+    if constexpr (G::kUniform) {
+        int32_t tnext[NT];                     // table entries of the next step to issue
+        auto fetch = [&](int st, int32_t (&t)[NT]) {
+#pragma unroll
+            for (int k = 0; k < NT; ++k) t[k] = trow[(start + st * CH) / B + k];
+        };
+        auto issue = [&](StepBuf& b, int st) {
+            const int t0 = start + st * CH;
+            int32_t cur[NT];
+#pragma unroll
+            for (int k = 0; k < NT; ++k) cur[k] = tnext[k];
+            const int nx = st + kWaves;
+            if (nx < nfull) fetch(nx, tnext);
+#pragma unroll
+            for (int k = 0; k < NT; ++k) {
+                const bool ok = (uint32_t)cur[k] < (uint32_t)num_blocks;
+                const int64_t blk = ok ? cur[k] : 0;   // a skipped id reads block 0, masked below
+#pragma unroll
+                for (int u = 0; u < G::LPB; ++u) {
+                    const int j = k * G::LPB + u;
+                    const int rowoff = (B >= CH ? t0 % B : 0) + u * TPL;
+                    const int64_t off = blk * blk_stride + (int64_t)rowoff * D + lane * 8;
+                    b.k[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off));
+                    b.v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + off));
+                    b.valid[j] = ok;
+                }
+            }
+        };
+        if (wave < nfull) {
+            fetch(wave, tnext);
+            StepBuf A, Bf;
+            int st = wave;
+            issue(A, st);
+            for (;;) {
+                int nx = st + kWaves;
+                if (nx >= nfull) { consume<D>(r, A, qf, scale_log2); break; }
+                issue(Bf, nx);
+                consume<D>(r, A, qf, scale_log2);
+                st = nx;
+                nx = st + kWaves;
+                if (nx >= nfull) { consume<D>(r, Bf, qf, scale_log2); break; }
+                issue(A, nx);
+                consume<D>(r, Bf, qf, scale_log2);
+                st = nx;
+            }
+        }
+    } else {
+        // rows of one load lie in several blocks: every lane looks up its own
+        for (int st = wave; st < nfull; st += kWaves) {
+            const int t0 = start + st * CH;
+            StepBuf b;
+#pragma unroll
+            for (int j = 0; j < kLoadsPerStep; ++j) {
+                const int t = t0 + j * TPL + row;
+                const int32_t phys = trow[t / B];
+                const bool ok = (uint32_t)phys < (uint32_t)num_blocks;
+                const int64_t off = (int64_t)(ok ? phys : 0) * blk_stride + (int64_t)(t % B) * D + col * 8;
+                b.k[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off));
+                b.v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + off));
+                b.valid[j] = ok;
+            }
+            consume<D>(r, b, qf, scale_log2);
+        }
+    }
+
+    // ---- the partial last step: per-row masks, loads of masked rows skipped
+    if (tail && wave == nfull % kWaves) {
+        const int t0 = start + nfull * CH;
+        StepBuf b;
+#pragma unroll
+        for (int j = 0; j < kLoadsPerStep; ++j) {
+            const int t = t0 + j * TPL + row;
+            const bool in = t < end;
+            const int tc = in ? t : end - 1;   // keeps the table index inside the sequence
+            const int32_t phys = trow[tc / B];
+            const bool ok = (uint32_t)phys < (uint32_t)num_blocks;
+            b.valid[j] = in && ok;
+            b.k[j] = u32x4{0, 0, 0, 0};
+            b.v[j] = u32x4{0, 0, 0, 0};
+            if (b.valid[j]) {
+                const int64_t off = (int64_t)phys * blk_stride + (int64_t)(tc % B) * D + col * 8;
+                b.k[j] = *reinterpret_cast<const u32x4*>(kbase + off);
+                b.v[j] = *reinterpret_cast<const u32x4*>(vbase + off);
+            }
+        }
+        consume<D>(r, b, qf, scale_log2);
+    }
+    const float m = r.m, l = r.l;
+    const float* acc = r.acc;
+
+    // Merge the NSTATE row states of the workgroup.  State k = wave*TPL+row
+    // owns s_acc[k*D .. k*D+D); this lane's 8 values sit at (wave*64+lane)*8.
+    __shared__ float s_m[NSTATE];
+    __shared__ float s_l[NSTATE];
+    __shared__ __attribute__((aligned(16))) float s_acc[NSTATE * D];
+    {
+        float4* dst = reinterpret_cast<float4*>(s_acc + (wave * 64 + lane) * 8);
+        dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        if (col == 0) {
+            s_m[wave * TPL + row] = m;
+            s_l[wave * TPL + row] = l;
+        }
+    }
+    __syncthreads();
+
+    float M = -INFINITY;
+#pragma unroll 8
+    for (int k = 0; k < NSTATE; ++k) M = fmaxf(M, s_m[k]);
+
+    const int64_t head_row = (int64_t)s * num_heads + h;
+    const int nparts = (n + part_size - 1) / part_size;
+    for (int d = threadIdx.x; d < D; d += kThreads) {
+        float L = 0.f, o = 0.f;
+#pragma unroll 8
+        for (int k = 0; k < NSTATE; ++k) {
+            const float mk = s_m[k];
+            const float w = mk == -INFINITY ? 0.f : fast_exp2(mk - M);
+            L = fmaf(w, s_l[k], L);
+            o = fmaf(w, s_acc[k * D + d], o);
+        }
+        if (bad_len) {
+            out[head_row * D + d] = (_Float16)NAN;
+        } else if (nparts <= 1) {
+            out[head_row * D + d] = L > 0.f ? (_Float16)(o / L) : (_Float16)0.f;
+        } else {
+            const int64_t slot = head_row * num_parts + part;
+            ws_acc[slot * D + d] = o;
+            if (d == 0) {
+                ws_ml[2 * slot] = M;
+                ws_ml[2 * slot + 1] = L;
+            }
+        }
+    }
+}
+
+// Merge the partitions of every sequence longer than one partition.
+template <int D>
+__global__ void __launch_bounds__(D < 64 ? 64 : D)
+decode_reduce_kernel(_Float16* __restrict__ out, const float* __restrict__ ws_ml,
+                     const float* __restrict__ ws_acc, const int32_t* __restrict__ lens,
+                     int32_t num_heads, int32_t part_size, int32_t num_parts, int64_t len_cap) {
+    const int h = blockIdx.x;
+    const int s = blockIdx.y;
+    const int32_t n = lens[s];
+    if (n < 0 || (int64_t)n > len_cap) return;   // written as NaN by the first kernel
+    const int np = (n + part_size - 1) / part_size;
+    if (np <= 1) return;
+    const int64_t head_row = (int64_t)s * num_heads + h;
+    const int64_t base = head_row * num_parts;
+    float M = -INFINITY;
+    for (int p = 0; p < np; ++p) M = fmaxf(M, ws_ml[2 * (base + p)]);
+    for (int d = threadIdx.x; d < D; d += blockDim.x) {
+        float L = 0.f, o = 0.f;
+        for (int p = 0; p < np; ++p) {
+            const float mp = ws_ml[2 * (base + p)];
+            const float w = mp == -INFINITY ? 0.f : fast_exp2(mp - M);
+            L = fmaf(w, ws_ml[2 * (base + p) + 1], L);
+            o = fmaf(w, ws_acc[(base + p) * D + d], o);
+        }
+        out[head_row * D + d] = L > 0.f ? (_Float16)(o / L) : (_Float16)0.f;
+    }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_head_dim(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
+
+bool supported_block_size(int32_t b) {
+    return b == 1 || b == 2 || b == 4 || b == 8 || b == 16 || b == 32 || b == 64 || b == 128;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Layout {
+    int32_t part_size;
+    int32_t num_parts;
+    size_t ml_bytes;
+    size_t total;
+};
+
+Layout workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t max_context_len,
+                        int32_t part_size) {
+    Layout L{};
+    L.part_size = part_size;
+    const int64_t np = max_context_len > 0 ? ((int64_t)max_context_len + part_size - 1) / part_size : 1;
+    L.num_parts = (int32_t)(np > 0 ? np : 1);
+    if (L.num_parts <= 1) return L;
+    const size_t rows = (size_t)num_seqs * num_heads * L.num_parts;
+    L.ml_bytes = align_up(rows * 2 * sizeof(float), 256);
+    L.total = L.ml_bytes + align_up(rows * head_dim * sizeof(float), 256);
+    return L;
+}
+
+using MainFn = void (*)(_Float16*, float*, float*, const _Float16*, const _Float16*, const _Float16*,
+                        const int32_t*, int32_t, const int32_t*, int32_t, int32_t, int32_t, float, int32_t,
+                        int32_t, int64_t);
+using ReduceFn = void (*)(_Float16*, const float*, const float*, const int32_t*, int32_t, int32_t, int32_t,
+                          int64_t);
+
+template <int D>
+MainFn pick_main(int32_t b) {
+    switch (b) {
+        case 1: return decode_partition_kernel<D, 1>;
+        case 2: return decode_partition_kernel<D, 2>;
+        case 4: return decode_partition_kernel<D, 4>;
+        case 8: return decode_partition_kernel<D, 8>;
+        case 16: return decode_partition_kernel<D, 16>;
+        case 32: return decode_partition_kernel<D, 32>;
+        case 64: return decode_partition_kernel<D, 64>;
+        case 128: return decode_partition_kernel<D, 128>;
+        default: return nullptr;
+    }
+}
+
+MainFn pick_main(int32_t d, int32_t b) {
+    switch (d) {
+        case 16: return pick_main<16>(b);
+        case 32: return pick_main<32>(b);
+        case 64: return pick_main<64>(b);
+        case 128: return pick_main<128>(b);
+        case 256: return pick_main<256>(b);
+        default: return nullptr;
+    }
+}
+
+ReduceFn pick_reduce(int32_t d) {
+    switch (d) {
+        case 16: return decode_reduce_kernel<16>;
+        case 32: return decode_reduce_kernel<32>;
+        case 64: return decode_reduce_kernel<64>;
+        case 128: return decode_reduce_kernel<128>;
+        case 256: return decode_reduce_kernel<256>;
+        default: return nullptr;
+    }
+}
+
+}  // namespace
+
+extern "C" int32_t pa_decode_default_partition(int32_t head_dim, int32_t block_size) {
+    (void)head_dim;
+    (void)block_size;
+    return kDefaultPartition;
+}
+
+extern "C" size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                           int32_t max_context_len, int32_t partition_size) {
+    if (num_seqs < 0 || num_heads <= 0 || !supported_head_dim(head_dim) || max_context_len < 0 ||
+        partition_size < 0 || partition_size % kPartitionQuantum != 0)
+        return (size_t)-1;
+    const int32_t p = partition_size ? partition_size : kDefaultPartition;
+    return workspace_layout(num_seqs, num_heads, head_dim, max_context_len, p).total;
+}
+
+extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                         float scale, int32_t max_context_len, int32_t partition_size, void* workspace,
+                         size_t workspace_bytes, int32_t dtype, void* stream) {
+    if (dtype != PA_DTYPE_F16) return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: dtype %d", dtype);
+    if (!supported_head_dim(head_dim)) return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d", head_dim);
+    if (!supported_block_size(block_size))
+        return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d", block_size);
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
+        num_blocks <= 0 || max_blocks_per_seq < 0 || max_context_len < 0 || partition_size < 0)
+        return pa::fail(PA_ERR_INVALID, "pa_decode: bad sizes (S=%d H=%d Hkv=%d NB=%d W=%d max_len=%d P=%d)",
+                        num_seqs, num_heads, num_kv_heads, num_blocks, max_blocks_per_seq, max_context_len,
+                        partition_size);
+    if (partition_size % kPartitionQuantum != 0)
+        return pa::fail(PA_ERR_INVALID, "pa_decode: partition_size %d is not a multiple of %d", partition_size,
+                        kPartitionQuantum);
+    if (num_seqs > 65535 || num_heads > 65535)
+        return pa::fail(PA_ERR_INVALID, "pa_decode: num_seqs and num_heads must be <= 65535");
+    if (!std::isfinite(scale)) return pa::fail(PA_ERR_INVALID, "pa_decode: scale is not finite");
+    if (num_seqs == 0) return PA_OK;
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+        return pa::fail(PA_ERR_INVALID, "pa_decode: null pointer");
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+        return pa::fail(PA_ERR_INVALID, "pa_decode: out, q and caches must be 16-byte aligned");
+
+    const int32_t p = partition_size ? partition_size : kDefaultPartition;
+    const Layout L = workspace_layout(num_seqs, num_heads, head_dim, max_context_len, p);
+    if (L.total > 0) {
+        if (!workspace) return pa::fail(PA_ERR_INVALID, "pa_decode: workspace of %zu bytes required", L.total);
+        if (workspace_bytes < L.total)
+            return pa::fail(PA_ERR_INVALID, "pa_decode: workspace %zu < %zu bytes", workspace_bytes, L.total);
+        if (!aligned16(workspace)) return pa::fail(PA_ERR_INVALID, "pa_decode: workspace must be 16-byte aligned");
+    }
+    const int64_t len_cap_tables = (int64_t)max_blocks_per_seq * block_size;
+    const int64_t len_cap_grid = (int64_t)L.num_parts * p;
+    const int64_t len_cap = len_cap_tables < len_cap_grid ? len_cap_tables : len_cap_grid;
+
+    float* ws_ml = L.total ? static_cast<float*>(workspace) : nullptr;
+    float* ws_acc = L.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + L.ml_bytes) : nullptr;
+    const float scale_log2 = (float)((double)scale * kLog2e);
+    auto st = static_cast<hipStream_t>(stream);
+
+    MainFn main_fn = pick_main(head_dim, block_size);
+    hipLaunchKernelGGL(main_fn, dim3((unsigned)L.num_parts, (unsigned)num_heads, (unsigned)num_seqs),
+                       dim3(kThreads), 0, st, static_cast<_Float16*>(out), ws_ml, ws_acc,
+                       static_cast<const _Float16*>(q), static_cast<const _Float16*>(k_cache),
+                       static_cast<const _Float16*>(v_cache), block_tables, max_blocks_per_seq, context_lens,
+                       num_heads, num_kv_heads, num_blocks, scale_log2, p, L.num_parts, len_cap);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "pa_decode: %s", hipGetErrorString(e));
+    if (L.num_parts > 1) {
+        const unsigned threads = head_dim < 64 ? 64u : (unsigned)head_dim;
+        hipLaunchKernelGGL(pick_reduce(head_dim), dim3((unsigned)num_heads, (unsigned)num_seqs), dim3(threads), 0,
+                           st, static_cast<_Float16*>(out), (const float*)ws_ml, (const float*)ws_acc,
+                           context_lens, num_heads, p, L.num_parts, len_cap);
+        e = hipGetLastError();
+        if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "pa_decode: %s", hipGetErrorString(e));
+    }
+    return PA_OK;
+}

@@ -1,0 +1,223 @@
+"""GPU parity of pa_decode (through the C ABI) against the oracle.
+
+Caches for the small cases are built on the host by the oracle (model slots +
+oracle scatter, NaN in every unused slot) and uploaded, so these tests isolate
+the decode kernels.  The full-size cases use the product's own block manager
+and scatter and check every intermediate bit for bit against the oracle's."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_390_amd as pa
+import workloads
+from gpu_common import assert_attention_close, bits, device, poisoned_cache, say
+from oracle.block_manager import BlockManagerModel
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_cache(case):
+    """Place the case's contiguous K/V into a NaN-poisoned pool with the
+    model's slots and the oracle's scatter."""
+    m = BlockManagerModel(case.num_blocks, case.block_size)
+    for s, (n, t) in enumerate(zip(case.lens, case.tables)):
+        m.set_table(s, t, n)
+    slots = np.array([m.slot(s, p) for s, n in enumerate(case.lens) for p in range(n)], dtype=np.int64)
+    kc = poisoned_cache(case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim)
+    vc = kc.copy()
+    oracle.reshape_and_cache(case.k_tokens, case.v_tokens, slots, kc, vc)
+    width = max(1, max(len(t) for t in case.tables))
+    rows, lens = m.tables(range(len(case.lens)), width)
+    return kc, vc, np.array(rows, dtype=np.int32), np.array(lens, dtype=np.int32)
+
+
+def _gpu_decode(dev, q, kc, vc, tables, lens, scale, partition_size=0, max_context_len=None):
+    S, H, D = q.shape
+    out = torch.full((S, H, D), float("nan"), dtype=torch.float16, device=dev)
+    pa.pa_decode(out, torch.from_numpy(q).to(dev), torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev),
+                 torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), scale,
+                 partition_size=partition_size, max_context_len=max_context_len)
+    torch.cuda.synchronize()
+    return out
+
+
+EDGE_LENS = [0, 1, 2, 3, 7, 15, 16, 17, 31, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257,
+             511, 512, 513, 777, 1024, 1031]
+
+GEOMETRIES = [  # (head_dim, block_size)
+    (128, 16), (128, 1), (128, 2), (128, 4), (128, 8), (128, 32), (128, 64), (128, 128),
+    (64, 16), (64, 4), (256, 16), (256, 128), (32, 2), (32, 64), (16, 4), (16, 1),
+]
+
+
+@pytest.mark.parametrize("D,B", GEOMETRIES)
+@pytest.mark.parametrize("P", [0, 128])
+@pytest.mark.parametrize("H,Hkv", [(2, 2), (4, 1)])
+def test_decode_edge_lengths_match_oracle(D, B, P, H, Hkv):
+    dev = device()
+    case = workloads.random_case(D * 1000 + B + P + H, EDGE_LENS, H, Hkv, D, B)
+    kc, vc, tables, lens = _oracle_cache(case)
+    say(f"decode D={D} B={B} P={P} H={H}/{Hkv} NB={case.num_blocks}")
+    out = _gpu_decode(dev, case.q, kc, vc, tables, lens, case.scale, partition_size=P)
+    ref = oracle.decode(case.q, kc, vc, tables, lens, case.scale)
+    assert_attention_close(out, ref, f"D={D} B={B} P={P}")
+    assert np.all(bits(out)[0] == 0)                       # n == 0 row is exactly zero
+
+
+def test_single_token_is_exact():
+    dev = device()
+    case = workloads.random_case(5, [1] * 8, 4, 2, 128, 16)
+    kc, vc, tables, lens = _oracle_cache(case)
+    out = _gpu_decode(dev, case.q, kc, vc, tables, lens, case.scale)
+    for s in range(8):
+        want = np.repeat(case.v_tokens[s], 2, axis=0)      # query heads 2k, 2k+1 read KV head k
+        assert np.array_equal(bits(out)[s], want.view(np.uint16))
+
+
+def test_tiny_workload_end_to_end():
+    """4 sequences of lengths 1/5/12/50, block size 4, one holding the page's
+    table [7, 3, 1]: product block manager, two scatters (history, then each
+    sequence's newest token), decode -- all against the oracle."""
+    dev = device()
+    w = workloads.tiny(seed=0)
+    S, B = len(w.lens), w.block_size
+    bm = pa.BlockManager(w.num_blocks, B)
+    m = BlockManagerModel(w.num_blocks, B)
+    for s, (n, t) in enumerate(zip(w.lens, w.tables)):
+        bm.set_table(s, t, n)
+        m.set_table(s, t, n)
+    assert bm.table(2) == [7, 3, 1]
+    hist, last, hist_tok, last_tok = [], [], [], []
+    for s, n in enumerate(w.lens):
+        sl = bm.get_slots(s, 0, n)
+        assert sl.tolist() == [m.slot(s, p) for p in range(n)]
+        hist += sl[:-1].tolist()
+        last.append(int(sl[-1]))
+        hist_tok += list(range(w.seq_start[s], w.seq_start[s] + n - 1))
+        last_tok.append(w.seq_start[s] + n - 1)
+    kc_h = poisoned_cache(w.num_blocks, w.num_kv_heads, B, w.head_dim)
+    vc_h = kc_h.copy()
+    kc, vc = torch.from_numpy(kc_h).to(dev), torch.from_numpy(vc_h).to(dev)
+    for idx, slots in ((hist_tok, hist), (last_tok, last)):
+        key = np.ascontiguousarray(w.k_tokens[idx])
+        val = np.ascontiguousarray(w.v_tokens[idx])
+        sl = np.array(slots, dtype=np.int64)
+        pa.pa_reshape_and_cache(torch.from_numpy(key).to(dev), torch.from_numpy(val).to(dev),
+                                torch.from_numpy(sl).to(dev), kc, vc)
+        oracle.reshape_and_cache(key, val, sl, kc_h, vc_h)
+    tables, lens = bm.get_tables(range(S), 13)
+    out = torch.empty((S, w.num_heads, w.head_dim), dtype=torch.float16, device=dev)
+    pa.pa_decode(out, torch.from_numpy(w.q).to(dev), kc, vc, torch.from_numpy(tables).to(dev),
+                 torch.from_numpy(lens).to(dev), w.scale, B)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(kc), bits(kc_h)) and np.array_equal(bits(vc), bits(vc_h))
+    ref = oracle.decode(w.q, kc_h, vc_h, tables, lens, w.scale)
+    assert_attention_close(out, ref, "tiny")
+    flat = oracle.attention_contig(w.q, w.k_tokens, w.v_tokens, w.seq_start, np.array(w.lens, np.int32), w.scale)
+    assert np.array_equal(ref, flat)
+    assert np.array_equal(bits(out)[0], np.repeat(w.v_tokens[0], 1, axis=0).view(np.uint16))   # n == 1
+
+
+def test_deterministic_and_blind_to_physical_placement():
+    dev = device()
+    case = workloads.random_case(9, [1000, 37, 513, 2048, 5], 8, 8, 128, 16, spare_blocks=40)
+    kc, vc, tables, lens = _oracle_cache(case)
+    a = _gpu_decode(dev, case.q, kc, vc, tables, lens, case.scale)
+    b = _gpu_decode(dev, case.q, kc, vc, tables, lens, case.scale)
+    assert np.array_equal(bits(a), bits(b))
+    sigma = np.random.default_rng(3).permutation(case.num_blocks)   # relabel every block
+    kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+    kc2[sigma] = kc
+    vc2[sigma] = vc
+    t2 = np.where(tables >= 0, sigma[np.maximum(tables, 0)], -1).astype(np.int32)
+    c = _gpu_decode(dev, case.q, kc2, vc2, t2, lens, case.scale)
+    assert np.array_equal(bits(a), bits(c))
+
+
+def test_rows_longer_than_the_bound_are_nan_and_others_unaffected():
+    dev = device()
+    case = workloads.random_case(11, [100, 300, 40], 2, 2, 128, 16)
+    kc, vc, tables, lens = _oracle_cache(case)
+    out = _gpu_decode(dev, case.q, kc, vc, tables, lens, case.scale, partition_size=128, max_context_len=256)
+    ref = oracle.decode(case.q, kc, vc, tables, lens, case.scale)
+    ref[1] = np.nan
+    assert_attention_close(out, ref, "bounded")
+
+
+def test_table_entries_outside_the_pool_are_skipped():
+    dev = device()
+    case = workloads.random_case(12, [64, 80], 2, 2, 128, 16)
+    kc, vc, tables, lens = _oracle_cache(case)
+    bad = tables.copy()
+    bad[0, 1] = case.num_blocks + 5          # tokens 16..31 of sequence 0 drop out
+    bad[1, 4] = -7                           # tokens 64..79 of sequence 1 drop out
+    out = _gpu_decode(dev, case.q, kc, vc, bad, lens, case.scale)
+    keep0 = [p for p in range(64) if not 16 <= p < 32]
+    keep1 = list(range(64))
+    k = np.concatenate([case.k_tokens[keep0], case.k_tokens[64:64 + 64]])
+    v = np.concatenate([case.v_tokens[keep0], case.v_tokens[64:64 + 64]])
+    ref = oracle.attention_contig(case.q, np.ascontiguousarray(k), np.ascontiguousarray(v),
+                                  np.array([0, 48], np.int64), np.array([48, 64], np.int32), case.scale)
+    assert len(keep1) == 64
+    assert_attention_close(out, ref, "skipped ids")
+
+
+@pytest.mark.parametrize("P", [0, 256])
+def test_llama7b_decode_full_size(P):
+    """64 sequences, 32 heads x 128, B=16, n ~ U[1, 2048], pool of 8192 blocks
+    filled N(0, 1), tables from one permutation; the new token of every
+    sequence is written by the product's scatter, then decoded."""
+    dev = device()
+    w = workloads.llama7b_decode(seed=0)
+    S, B, NB = len(w.lens), w.block_size, w.num_blocks
+    say(f"llama7b: NB={NB} sum n={int(w.lens.sum())} P={P}")
+    kc, vc = w.pool(0, dev)
+    kc_h, vc_h = kc.cpu().numpy(), vc.cpu().numpy()          # oracle inputs, before any kernel
+    q, key, val = w.new_tokens(0, dev)
+    q_h, key_h, val_h = q.cpu().numpy(), key.cpu().numpy(), val.cpu().numpy()
+
+    bm = pa.BlockManager(NB, B)
+    m = BlockManagerModel(NB, B)
+    slots = np.empty(S, dtype=np.int64)
+    for s, n in enumerate(w.lens.tolist()):
+        t = w.perm_tables[s, :workloads.ceil_div(n, B)]
+        bm.set_table(s, t, n)
+        m.set_table(s, t.tolist(), n)
+        slots[s] = bm.get_slots(s, n - 1, 1)[0]
+        assert slots[s] == m.slot(s, n - 1)
+    width = w.perm_tables.shape[1]
+    tables, lens = bm.get_tables(range(S), width)
+    rows, lens_m = m.tables(range(S), width)
+    assert np.array_equal(tables, np.array(rows, np.int32)) and lens.tolist() == lens_m
+
+    pa.pa_reshape_and_cache(key, val, torch.from_numpy(slots).to(dev), kc, vc)
+    out = torch.empty((S, w.num_heads, w.head_dim), dtype=torch.float16, device=dev)
+    pa.pa_decode(out, q, kc, vc, torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), w.scale, B,
+                 partition_size=P)
+    torch.cuda.synchronize()
+
+    oracle.reshape_and_cache(key_h, val_h, slots, kc_h, vc_h)
+    assert torch.equal(kc.view(torch.int16), torch.from_numpy(kc_h.view(np.int16)).to(dev))
+    assert torch.equal(vc.view(torch.int16), torch.from_numpy(vc_h.view(np.int16)).to(dev))
+    ref = oracle.decode(q_h, kc_h, vc_h, tables, lens, w.scale)
+    assert_attention_close(out, ref, f"llama7b P={P}")
+
+
+def test_long_context_split_partitions():
+    """16 sequences x 4096 tokens, 32 x 128 heads, B=16, 512-token partitions
+    (8 per sequence) merged by the reduce kernel; two of the 32 layers."""
+    dev = device()
+    w = workloads.long_context(seed=0)
+    S = len(w.lens)
+    tables = np.ascontiguousarray(w.perm_tables)
+    for layer in (0, 31):
+        kc, vc = w.pool(layer, dev)
+        q = workloads._torch_normal_f16((S, w.num_heads, w.head_dim), w.seed, dev, 40_000 + layer)
+        out = torch.empty_like(q)
+        pa.pa_decode(out, q, kc, vc, torch.from_numpy(tables).to(dev), torch.from_numpy(w.lens).to(dev),
+                     w.scale, w.block_size, max_context_len=4096, partition_size=512)
+        torch.cuda.synchronize()
+        ref = oracle.decode(q.cpu().numpy(), kc.cpu().numpy(), vc.cpu().numpy(), tables, w.lens, w.scale)
+        assert_attention_close(out, ref, f"long layer {layer}")
+        del kc, vc

@@ -263,3 +263,26 @@ def block_manager_ops(seed: int, n_ops: int, max_seqs: int = 6,
         else:
             ops.append(("free", int(rng.integers(0, max(next_id, 1)))))
     return ops
+
+
+def random_case(seed: int, lens, num_heads: int, num_kv_heads: int, head_dim: int,
+                block_size: int, spare_blocks: int = 3) -> Tiny:
+    """Arbitrary lengths: contiguous fp16 N(0, 1) K/V per sequence, q, and
+    tables dealt from one random permutation of a pool with `spare_blocks`
+    ids left over."""
+    rng = _rng(seed, 7)
+    lens = [int(n) for n in lens]
+    nbs = [ceil_div(n, block_size) for n in lens]
+    nb = sum(nbs) + spare_blocks
+    perm = rng.permutation(nb)
+    tables, at = [], 0
+    for k in nbs:
+        tables.append([int(b) for b in perm[at:at + k]])
+        at += k
+    total = sum(lens)
+    k = rng.standard_normal((total, num_kv_heads, head_dim), dtype=np.float32).astype(np.float16)
+    v = rng.standard_normal((total, num_kv_heads, head_dim), dtype=np.float32).astype(np.float16)
+    q = rng.standard_normal((len(lens), num_heads, head_dim), dtype=np.float32).astype(np.float16)
+    seq_start = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64) if lens else np.zeros(0, np.int64)
+    return Tiny(block_size, nb, num_heads, num_kv_heads, head_dim, lens, tables, k, v,
+                seq_start, q, 1.0 / math.sqrt(head_dim))
