@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-KV-cache hot path on one MI355X.
+
+Default workload: Llama-2-7B-shaped decode -- 64 sequences, 32 query heads =
+32 KV heads of dim 128, fp16 KV, block_size 16, context lengths uniform on
+[1, 2048], tables from a random permutation of a pool of 64 * 128 blocks --
+with the cache of all 32 layers resident in HBM (one 2 GiB K+V pool per
+layer, 64 GiB in total), so that no decode finds its K/V in a cache level.
+
+One step = one decode iteration over the whole path:
+  host   the C++ block manager appends one token to every sequence (a new
+         block when the last one is full) and packs tables / lengths / slots;
+  H2D    the packed arrays go to the device (pinned, asynchronous);
+  per layer (x32)
+         pa_reshape_and_cache writes the new token's K/V,
+         pa_decode runs attention for all 64 sequences.
+
+Printed: one JSON line.  `value` is KV GB/s over the whole step (bytes of
+cached K/V that decode must read, summed over layers, divided by wall time per
+step); `roofline` is the decode call alone, timed with HIP events on the
+launch stream; `cpu_baseline` times the fp64 oracle on one layer of the same
+workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="llama7b", choices=["llama7b", "long", "copy"])
+    p.add_argument("--layers", type=int, default=32)
+    p.add_argument("--batch", type=int, default=64)
+    p.add_argument("--block-size", type=int, default=16)
+    p.add_argument("--partition", type=int, default=0, help="decode partition size (0 = library default)")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the oracle timing")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="approximate oracle CPU time budget")
+    return p.parse_args()
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("decode.hip",):
+        with open(os.path.join(ROOT, "paged_kv_cache_390_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kv_bytes_per_launch: float):
+    """HBM bytes per decode call from the committed PMC summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "decode_llama7b_pmc.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except Exception:
+        return None
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_decode_call")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the decode path shards by sequence or KV head with no exchange, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        sys.exit("bench.py: --steps >= 1 and --warmup >= 0 required")
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_390_amd as pa
+    import workloads
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py: no GPU visible")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pa.lib()                                     # fail loudly if the HIP library is missing
+
+    if args.workload == "copy":
+        return copy_bench(args, dev)
+
+    L = args.layers
+    B = args.block_size
+    K, W = args.steps, args.warmup
+    if args.workload == "llama7b":
+        w = workloads.llama7b_decode(seed=args.seed, num_seqs=args.batch, block_size=B)
+        wl_name = "llama2-7b-decode"
+        ctx_desc = "U[1,2048]"
+    else:
+        w = workloads.long_context(seed=args.seed, num_seqs=16, block_size=B)
+        wl_name = "long-context-decode"
+        ctx_desc = "4096"
+    S, H, Hkv, D, NB = len(w.lens), w.num_heads, w.num_kv_heads, w.head_dim, w.num_blocks
+    grow = W + K + 1
+    width = workloads.ceil_div(int(w.lens.max()) + grow, B)
+
+    # ---- pools for every layer (inputs resident in HBM before timing)
+    log(f"[bench] {wl_name}: S={S} H={H} Hkv={Hkv} D={D} B={B} NB={NB}/layer layers={L} "
+        f"pool {2 * NB * Hkv * B * D * 2 / 2**30:.1f} GiB/layer")
+    t = time.perf_counter()
+    kcs, vcs = [], []
+    for l in range(L):
+        k, v = w.pool(l, dev)
+        kcs.append(k)
+        vcs.append(v)
+    torch.cuda.synchronize()
+    log(f"[bench] pools generated in {time.perf_counter() - t:.1f}s")
+    oracle_pool = (kcs[0].cpu().numpy(), vcs[0].cpu().numpy()) if args.cpu_baseline else None
+
+    q, key, val = w.new_tokens(0, dev)
+
+    # ---- block manager: the pages' tables (a permutation of the pool), n - 1 tokens cached
+    bm = pa.BlockManager(NB, B)
+    for s, n in enumerate(w.lens.tolist()):
+        bm.set_table(s, w.perm_tables[s, :workloads.ceil_div(n - 1, B)], n - 1)
+    seqs = np.arange(S, dtype=np.int64)
+    part = args.partition
+    ws_bytes = pa.pa_decode_workspace_size(S, H, D, width * B, part)
+    workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    nbuf = 2
+    h_tables = [torch.empty((S, width), dtype=torch.int32).pin_memory() for _ in range(nbuf)]
+    h_lens = [torch.empty(S, dtype=torch.int32).pin_memory() for _ in range(nbuf)]
+    h_slots = [torch.empty(S, dtype=torch.int64).pin_memory() for _ in range(nbuf)]
+    d_tables = torch.empty((S, width), dtype=torch.int32, device=dev)
+    d_lens = torch.empty(S, dtype=torch.int32, device=dev)
+    d_slots = torch.empty(S, dtype=torch.int64, device=dev)
+    copied = [None] * nbuf
+    out = torch.empty((S, H, D), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    kv_per_token = 2 * Hkv * D * 2           # K and V, fp16, one layer
+
+    def step(i, ev=None):
+        b = i % nbuf
+        if copied[b] is not None:
+            copied[b].synchronize()          # the pinned buffer's previous upload has been consumed
+        slots, pairs = bm.append_tokens(seqs)
+        assert len(pairs) == 0
+        bm.get_tables(seqs, width, out=h_tables[b].numpy(), lens_out=h_lens[b].numpy())
+        h_slots[b].numpy()[:] = slots
+        ctx = int(h_lens[b].numpy().astype(np.int64).sum())
+        d_tables.copy_(h_tables[b], non_blocking=True)
+        d_lens.copy_(h_lens[b], non_blocking=True)
+        d_slots.copy_(h_slots[b], non_blocking=True)
+        e = torch.cuda.Event()
+        e.record(stream)
+        copied[b] = e
+        for l in range(L):
+            pa.pa_reshape_and_cache(key, val, d_slots, kcs[l], vcs[l])
+            if ev is not None:
+                ev[l][0].record(stream)
+            pa.pa_decode(out, q, kcs[l], vcs[l], d_tables, d_lens, w.scale, B, max_context_len=width * B,
+                         partition_size=part, workspace=workspace)
+            if ev is not None:
+                ev[l][1].record(stream)
+        return ctx
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(L)]
+              for _ in range(K)]
+    ctx_sum = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        ctx_sum += step(W + i, events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    wall = t1 - t0
+    ms_per_step = wall / K * 1e3
+    kv_bytes_total = ctx_sum * kv_per_token * L          # over the K timed steps
+    value = kv_bytes_total / wall / 1e9
+    dec_ms = [events[i][l][0].elapsed_time(events[i][l][1]) for i in range(K) for l in range(L)]
+    dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
+    kv_per_launch = ctx_sum / K * kv_per_token
+    achieved = kv_per_launch / dec_avg_s / 1e9
+    tokens_per_s_layer = S * L / (wall / K)
+    log(f"[bench] step {ms_per_step:.3f} ms ({L} layers); decode call avg {dec_avg_s * 1e6:.1f} us "
+        f"= {achieved:.0f} GB/s ({100 * achieved / HBM_PEAK_GBS:.1f}% of peak); "
+        f"min {min(dec_ms) * 1e3:.1f} us max {max(dec_ms) * 1e3:.1f} us")
+
+    # ---- oracle on the host cores, same workload (layer 0, one decode)
+    cpu = None
+    if args.cpu_baseline:
+        import oracle
+        threads = oracle.default_threads()
+        tables, lens = bm.get_tables(seqs, width)
+        q_h = q.cpu().numpy()
+        kc_h, vc_h = oracle_pool
+        reps, spent, kv_done = 0, 0.0, 0
+        while reps == 0 or (spent < args.cpu_seconds and reps < 8):
+            c0 = time.perf_counter()
+            oracle.decode(q_h, kc_h, vc_h, tables, lens, w.scale, nthreads=threads)
+            spent += time.perf_counter() - c0
+            kv_done += int(lens.astype(np.int64).sum()) * kv_per_token
+            reps += 1
+        cpu = {"value": round(kv_done / spent / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"{reps} x one layer's decode of the same batch ({S} seqs x {H} heads, "
+                         f"{int(lens.sum())} cached tokens), fp64 C oracle, {spent:.1f} s"}
+        log(f"[bench] cpu oracle: {cpu['value']} GB/s on {threads} threads ({spent:.1f}s)")
+
+    traffic = traffic_from_profiles(kv_per_launch)
+    line = {
+        "metric": "paged-decode achieved KV GB/s (% of HBM peak) + tokens/s per layer, bs=16",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s_per_layer": round(tokens_per_s_layer, 1),
+        "decode_only": {"GB_s": round(achieved, 2), "pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
+                        "tokens_per_s_per_layer": round(S / dec_avg_s, 1), "us_per_call": round(dec_avg_s * 1e6, 2)},
+        "config": {"workload": wl_name, "batch": S, "block_size": B, "num_heads": H, "num_kv_heads": Hkv,
+                   "head_dim": D, "context": ctx_desc, "layers_resident": L, "pool_blocks_per_layer": NB,
+                   "partition_size": part or pa.pa_decode_default_partition(D, B),
+                   "step": "host append+tables, H2D, per layer reshape_and_cache + decode"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def copy_bench(args, dev):
+    """Block copies of known size through pa_copy_blocks: a plain streaming
+    copy (every byte read once and written once) used as the same-box
+    bandwidth reference and as the calibration kernel for the HBM byte
+    counters."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_390_amd as pa
+
+    NB, Hkv, B, D = 8192, 32, 16, 128
+    npairs = 4096
+    k = torch.zeros((NB, Hkv, B, D), dtype=torch.float16, device=dev)
+    v = torch.zeros_like(k)
+    perm = np.random.default_rng(args.seed).permutation(NB)
+    pairs = torch.from_numpy(np.stack([perm[:npairs], perm[npairs:2 * npairs]], 1).astype(np.int64)).to(dev)
+    block_bytes = Hkv * B * D * 2
+    moved = 2 * npairs * block_bytes            # K and V blocks, each read once and written once
+    for _ in range(args.warmup):
+        pa.pa_copy_blocks([k], [v], pairs)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev:
+        a.record()
+        pa.pa_copy_blocks([k], [v], pairs)
+        b.record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    avg = sum(ms) / len(ms) / 1e3
+    gbs = 2 * moved / avg / 1e9               # read + write
+    log(f"[bench] copy: {npairs} pairs x 2 x {block_bytes // 1024} KiB, {moved / 2**30:.2f} GiB read + "
+        f"written per call, avg {avg * 1e6:.1f} us = {gbs:.0f} GB/s (read+write)")
+    print(json.dumps({"metric": "block-copy GB/s (read+write)", "value": round(gbs, 2), "unit": "GB/s",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+                      "bytes_read_per_call": moved, "bytes_written_per_call": moved,
+                      "us_per_call": round(avg * 1e6, 2),
+                      "config": {"workload": "copy-blocks", "pairs": npairs, "block_bytes": block_bytes}}),
+          flush=True)
+
+
+if __name__ == "__main__":
+    main()
