@@ -32,12 +32,12 @@ def _oracle_cache(case):
     return kc, vc, np.array(rows, dtype=np.int32), np.array(lens, dtype=np.int32)
 
 
-def _gpu_decode(dev, q, kc, vc, tables, lens, scale, partition_size=0, max_context_len=None):
+def _gpu_decode(dev, q, kc, vc, tables, lens, scale, partition_size=0, max_context_len=None, workspace=None):
     S, H, D = q.shape
     out = torch.full((S, H, D), float("nan"), dtype=torch.float16, device=dev)
     pa.pa_decode(out, torch.from_numpy(q).to(dev), torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev),
                  torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), scale,
-                 partition_size=partition_size, max_context_len=max_context_len)
+                 partition_size=partition_size, max_context_len=max_context_len, workspace=workspace)
     torch.cuda.synchronize()
     return out
 
@@ -135,6 +135,31 @@ def test_deterministic_and_blind_to_physical_placement():
     assert np.array_equal(bits(a), bits(c))
 
 
+def test_workspace_reused_across_calls_of_different_sizes():
+    """One workspace serves calls of different sizes and partition counts
+    (its contents on entry are ignored).  Outputs start as NaN, so a row
+    whose merge never ran would show; repeated calls agree bit for bit."""
+    dev = device()
+    ws = torch.zeros(pa.pa_decode_workspace_size(8, 8, 128, 4096, 128), dtype=torch.uint8, device=dev)
+    cases = [([1000, 37, 513, 2048, 5, 129, 256, 4000], 8, 8),
+             ([300, 1], 4, 4),
+             ([4096, 4096, 4096], 8, 2),
+             ([129, 7, 1000, 2222], 8, 1)]
+    for i, (lens_i, H, Hkv) in enumerate(cases):
+        case = workloads.random_case(40 + i, lens_i, H, Hkv, 128, 16)
+        kc, vc, tables, lens = _oracle_cache(case)
+        say(f"workspace reuse case {i}: lens={lens_i} H={H}/{Hkv}")
+        out = _gpu_decode(dev, case.q, kc, vc, tables, lens, case.scale, partition_size=128,
+                          max_context_len=4096, workspace=ws)
+        ref = oracle.decode(case.q, kc, vc, tables, lens, case.scale)
+        assert_attention_close(out, ref, f"reuse {i}")
+        if i == 0:
+            for _ in range(10):
+                again = _gpu_decode(dev, case.q, kc, vc, tables, lens, case.scale, partition_size=128,
+                                    max_context_len=4096, workspace=ws)
+                assert np.array_equal(bits(again), bits(out))
+
+
 def test_rows_longer_than_the_bound_are_nan_and_others_unaffected():
     dev = device()
     case = workloads.random_case(11, [100, 300, 40], 2, 2, 128, 16)
@@ -206,7 +231,8 @@ def test_llama7b_decode_full_size(P):
 
 def test_long_context_split_partitions():
     """16 sequences x 4096 tokens, 32 x 128 heads, B=16, 512-token partitions
-    (8 per sequence) merged by the reduce kernel; two of the 32 layers."""
+    (8 per sequence) merged in-kernel by the last workgroup of each row; two
+    of the 32 layers."""
     dev = device()
     w = workloads.long_context(seed=0)
     S = len(w.lens)
