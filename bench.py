@@ -47,9 +47,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="llama7b", choices=["llama7b", "long", "copy"])
+    p.add_argument("--workload", default="llama7b", choices=["llama7b", "gqa", "long", "copy"],
+                   help="llama7b: the Llama-2-7B decode batch (default); gqa: 64 query heads over 8 KV "
+                        "heads (matrix-core kernel); long: 16 x 4096 tokens; copy: block-copy calibration")
     p.add_argument("--layers", type=int, default=32)
-    p.add_argument("--batch", type=int, default=64)
+    p.add_argument("--batch", type=int, default=0, help="sequences (0: 64 for llama7b, 256 for gqa)")
     p.add_argument("--block-size", type=int, default=16)
     p.add_argument("--partition", type=int, default=0, help="decode partition size (0 = library default)")
     p.add_argument("--seed", type=int, default=0)
@@ -59,25 +61,28 @@ def parse():
     return p.parse_args()
 
 
-def kernel_source_hash() -> str:
+KERNEL_SOURCES = {"llama7b": ("decode.hip",), "gqa": ("decode.hip", "decode_gqa.hip")}
+
+
+def kernel_source_hash(workload: str) -> str:
     h = hashlib.sha256()
-    for f in ("decode.hip",):
+    for f in KERNEL_SOURCES.get(workload, ("decode.hip",)):
         with open(os.path.join(ROOT, "paged_kv_cache_390_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(kv_bytes_per_launch: float):
-    """HBM bytes per decode call from the committed PMC summary, if it was
-    taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "decode_llama7b_pmc.json")
+def traffic_from_profiles(workload: str):
+    """HBM bytes per decode call from the committed PMC summary of this
+    workload, if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
     try:
         d = json.load(open(path))
     except Exception:
         return None
-    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+    if d.get("kernel_source_sha256_16") != kernel_source_hash(workload):
         return None
     return d.get("hbm_bytes_per_decode_call")
 
@@ -110,8 +115,12 @@ def main():
     B = args.block_size
     K, W = args.steps, args.warmup
     if args.workload == "llama7b":
-        w = workloads.llama7b_decode(seed=args.seed, num_seqs=args.batch, block_size=B)
+        w = workloads.llama7b_decode(seed=args.seed, num_seqs=args.batch or 64, block_size=B)
         wl_name = "llama2-7b-decode"
+        ctx_desc = "U[1,2048]"
+    elif args.workload == "gqa":
+        w = workloads.gqa_decode(seed=args.seed, num_seqs=args.batch or 256, block_size=B)
+        wl_name = "gqa-64q-8kv-decode"
         ctx_desc = "U[1,2048]"
     else:
         w = workloads.long_context(seed=args.seed, num_seqs=16, block_size=B)
@@ -142,7 +151,7 @@ def main():
         bm.set_table(s, w.perm_tables[s, :workloads.ceil_div(n - 1, B)], n - 1)
     seqs = np.arange(S, dtype=np.int64)
     part = args.partition
-    ws_bytes = pa.pa_decode_workspace_size(S, H, D, width * B, part)
+    ws_bytes = pa.pa_decode_workspace_size(S, H, Hkv, D, B, width * B, part)
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     nbuf = 2
@@ -230,7 +239,7 @@ def main():
                          f"{int(lens.sum())} cached tokens), fp64 C oracle, {spent:.1f} s"}
         log(f"[bench] cpu oracle: {cpu['value']} GB/s on {threads} threads ({spent:.1f}s)")
 
-    traffic = traffic_from_profiles(kv_per_launch)
+    traffic = traffic_from_profiles(args.workload)
     line = {
         "metric": "paged-decode achieved KV GB/s (% of HBM peak) + tokens/s per layer, bs=16",
         "value": round(value, 2),
@@ -250,7 +259,7 @@ def main():
                         "tokens_per_s_per_layer": round(S / dec_avg_s, 1), "us_per_call": round(dec_avg_s * 1e6, 2)},
         "config": {"workload": wl_name, "batch": S, "block_size": B, "num_heads": H, "num_kv_heads": Hkv,
                    "head_dim": D, "context": ctx_desc, "layers_resident": L, "pool_blocks_per_layer": NB,
-                   "partition_size": part or pa.pa_decode_default_partition(D, B),
+                   "partition_size": part or pa.pa_decode_default_partition(S, H, Hkv, D, B, width * B),
                    "step": "host append+tables, H2D, per layer reshape_and_cache + decode"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},

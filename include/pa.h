@@ -108,7 +108,11 @@ int pa_reshape_and_cache(const void *key, const void *value,
  *   context_lens   device, int32 [num_seqs]; n for each sequence, including
  *                  the token just written.  n == 0 gives an all-zero row.
  *   num_heads      query heads; num_heads % num_kv_heads == 0 and query head
- *                  h reads KV head h / (num_heads / num_kv_heads)
+ *                  h reads KV head h / (num_heads / num_kv_heads).  When 2 to
+ *                  16 query heads share a KV head and head_dim is 128, the
+ *                  products run on the matrix cores (one workgroup reads each
+ *                  K/V block once for the whole group); otherwise on the
+ *                  vector ALUs, one workgroup per query head.
  *   scale          multiplies q.k (1/sqrt(head_dim) in the usual model)
  *   max_context_len  host-known upper bound on every n; it sizes the grid so
  *                  that no device-to-host read is needed.  A row whose n
@@ -136,11 +140,18 @@ int pa_decode(void *out, const void *q, const void *k_cache,
  * fits one partition).  partition_size as for pa_decode (0 = default).
  * Returns (size_t)-1 for invalid arguments. */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
-                                int32_t head_dim, int32_t max_context_len,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                int32_t block_size, int32_t max_context_len,
                                 int32_t partition_size);
 
-/* The partition size pa_decode uses when given 0. */
-int32_t pa_decode_default_partition(int32_t head_dim, int32_t block_size);
+/* The partition size pa_decode uses when given 0: the longest of 2048,
+ * 1024, 512 and 256 tokens that still gives the launch at least four
+ * workgroups per resident workgroup slot of the kernel that serves these
+ * shapes.  -1 for invalid arguments. */
+int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_heads,
+                                    int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t block_size,
+                                    int32_t max_context_len);
 
 /* ------------------------------------------------------------------------
  * Whole-block copies for copy-on-write.

@@ -63,8 +63,8 @@ def lib() -> ctypes.CDLL:
         "pa_reshape_and_cache": ([P, P, i64, P, i32, P, P, i32, i32, i32, i32, i32, P], ctypes.c_int),
         "pa_decode": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P, sz, i32, P],
                       ctypes.c_int),
-        "pa_decode_workspace_size": ([i32, i32, i32, i32, i32], sz),
-        "pa_decode_default_partition": ([i32, i32], i32),
+        "pa_decode_workspace_size": ([i32, i32, i32, i32, i32, i32, i32], sz),
+        "pa_decode_default_partition": ([i32, i32, i32, i32, i32, i32], i32),
         "pa_copy_blocks": ([P, P, i32, P, i32, i32, i64, i32, P], ctypes.c_int),
         "pa_bm_create": ([i32, i32], P),
         "pa_bm_destroy": ([P], None),
@@ -158,16 +158,22 @@ def pa_reshape_and_cache(key, value, slot_mapping, k_cache, v_cache) -> None:
                                       _stream(k_cache.device)), "pa_reshape_and_cache")
 
 
-def pa_decode_workspace_size(num_seqs: int, num_heads: int, head_dim: int,
-                             max_context_len: int, partition_size: int = 0) -> int:
-    n = lib().pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len, partition_size)
+def pa_decode_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                             block_size: int, max_context_len: int, partition_size: int = 0) -> int:
+    n = lib().pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                       max_context_len, partition_size)
     if n == ctypes.c_size_t(-1).value:
         raise PAError(PA_ERR_INVALID, "pa_decode_workspace_size: invalid arguments")
     return n
 
 
-def pa_decode_default_partition(head_dim: int, block_size: int) -> int:
-    return lib().pa_decode_default_partition(head_dim, block_size)
+def pa_decode_default_partition(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                                block_size: int, max_context_len: int) -> int:
+    p = lib().pa_decode_default_partition(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                          max_context_len)
+    if p < 0:
+        raise PAError(PA_ERR_INVALID, "pa_decode_default_partition: invalid arguments")
+    return p
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
@@ -199,7 +205,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float
     W = block_tables.shape[1]
     if max_context_len is None:
         max_context_len = W * B
-    need = pa_decode_workspace_size(S, H, D, max_context_len, partition_size)
+    need = pa_decode_workspace_size(S, H, Hkv, D, B, max_context_len, partition_size)
     ws_ptr, ws_bytes = 0, 0
     if need:
         if workspace is None:

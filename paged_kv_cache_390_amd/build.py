@@ -17,7 +17,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpa.so")
 
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
-HIP_SOURCES = ["decode.hip", "cache_ops.hip"]
+HIP_SOURCES = ["decode.hip", "decode_gqa.hip", "cache_ops.hip"]
 CXX_SOURCES = ["block_manager.cpp", "status.cpp"]
 
 HIPCC_FLAGS = [
@@ -27,6 +27,10 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+# per-source extra hipcc flags: the grouped-query kernel keeps its matrix-core
+# accumulators in VGPRs (the online softmax reads and rescales them every tile;
+# in AGPRs each access would add a copy)
+HIP_EXTRA = {"decode_gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
@@ -54,7 +58,7 @@ def build(verbose: bool = False, extra_hip_flags=()) -> str:
     for src in HIP_SOURCES:
         o = os.path.join(OBJ, src + ".o")
         objs.append(o)
-        jobs.append([hipcc, *HIPCC_FLAGS, *extra_hip_flags, "-I", INCLUDE, "-I", CSRC, "-c",
+        jobs.append([hipcc, *HIPCC_FLAGS, *HIP_EXTRA.get(src, []), *extra_hip_flags, "-I", INCLUDE, "-I", CSRC, "-c",
                      os.path.join(CSRC, src), "-o", o])
     for src in CXX_SOURCES:
         o = os.path.join(OBJ, src + ".o")

@@ -48,6 +48,7 @@
 #include <cmath>
 #include <cstdint>
 
+#include "decode_internal.h"
 #include "pa.h"
 #include "pa_internal.h"
 
@@ -60,7 +61,6 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kLoadsPerStep = 4;          // 16-byte loads per lane per step, each for K and V
 constexpr int kPartitionQuantum = 128;    // partition_size granularity (a multiple of every step)
-constexpr int kDefaultPartition = 512;
 constexpr double kLog2e = 1.4426950408889634073599246810019;
 
 // DPP controls (GFX9 encoding).
@@ -448,20 +448,55 @@ ReduceFn pick_reduce(int32_t d) {
     }
 }
 
-}  // namespace
-
-extern "C" int32_t pa_decode_default_partition(int32_t head_dim, int32_t block_size) {
-    (void)head_dim;
-    (void)block_size;
-    return kDefaultPartition;
+// Default partition: the longest of 2048 / 1024 / 512 / 256 tokens that
+// still gives at least four workgroups per resident workgroup slot
+// (256 CUs x 4 for the one-query-per-head kernel, x 2 for the grouped-query
+// kernel, whose registers allow two per CU).  Longer partitions mean fewer
+// partial states to write and merge; enough workgroups keep every CU busy
+// through the drain.  Measured on 64 x 32-head and 256 x 8-KV-head batches
+// with U[1, 2048] contexts.
+int32_t default_partition(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t max_context_len) {
+    const int32_t group = num_kv_heads > 0 ? num_heads / num_kv_heads : 1;
+    const bool mfma = pa::gqa_mfma_supported(head_dim, block_size, group);
+    const int64_t rows = (int64_t)num_seqs * (mfma ? num_kv_heads : num_heads);
+    const int64_t slots = 256LL * (mfma ? 2 : 4);
+    const int32_t cands[] = {2048, 1024, 512, 256};
+    for (int32_t p : cands) {
+        // full partitions of a longest sequence: the bound may exceed every
+        // actual length, so a partial last partition is not counted on
+        const int64_t parts = max_context_len / p > 0 ? max_context_len / p : 1;
+        if (rows * parts >= 4 * slots) return p;
+    }
+    return 256;
 }
 
-extern "C" size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                                           int32_t max_context_len, int32_t partition_size) {
-    if (num_seqs < 0 || num_heads <= 0 || !supported_head_dim(head_dim) || max_context_len < 0 ||
-        partition_size < 0 || partition_size % kPartitionQuantum != 0)
+bool bad_geometry(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                  int32_t max_context_len, int32_t partition_size) {
+    return num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
+           !supported_head_dim(head_dim) || max_context_len < 0 || partition_size < 0 ||
+           partition_size % kPartitionQuantum != 0;
+}
+
+}  // namespace
+
+extern "C" int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t block_size, int32_t max_context_len) {
+    if (bad_geometry(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, 0) ||
+        !supported_block_size(block_size))
+        return -1;
+    return default_partition(num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_context_len);
+}
+
+extern "C" size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int32_t block_size, int32_t max_context_len,
+                                           int32_t partition_size) {
+    if (bad_geometry(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size) ||
+        !supported_block_size(block_size))
         return (size_t)-1;
-    const int32_t p = partition_size ? partition_size : kDefaultPartition;
+    const int32_t p = partition_size ? partition_size
+                                     : default_partition(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                                         max_context_len);
     return workspace_layout(num_seqs, num_heads, head_dim, max_context_len, p).total;
 }
 
@@ -492,7 +527,9 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const vo
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return pa::fail(PA_ERR_INVALID, "pa_decode: out, q and caches must be 16-byte aligned");
 
-    const int32_t p = partition_size ? partition_size : kDefaultPartition;
+    const int32_t p = partition_size ? partition_size
+                                     : default_partition(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                                         max_context_len);
     const Layout L = workspace_layout(num_seqs, num_heads, head_dim, max_context_len, p);
     if (L.total > 0) {
         if (!workspace) return pa::fail(PA_ERR_INVALID, "pa_decode: workspace of %zu bytes required", L.total);
@@ -512,13 +549,24 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const vo
     const float scale_log2 = (float)((double)scale * kLog2e);
     auto st = static_cast<hipStream_t>(stream);
 
-    MainFn main_fn = pick_main(head_dim, block_size);
-    hipLaunchKernelGGL(main_fn, dim3((unsigned)num_heads, (unsigned)num_seqs, (unsigned)L.num_parts),
-                       dim3(kThreads), 0, st, static_cast<_Float16*>(out), ws_ml, ws_acc,
-                       static_cast<const _Float16*>(q), static_cast<const _Float16*>(k_cache),
-                       static_cast<const _Float16*>(v_cache), block_tables, max_blocks_per_seq, context_lens,
-                       num_heads, num_kv_heads, num_blocks, scale_log2, p, L.num_parts, len_cap);
-    hipError_t e = hipGetLastError();
+    const int32_t group = num_heads / num_kv_heads;
+    hipError_t e;
+    if (pa::gqa_mfma_supported(head_dim, block_size, group)) {
+        // several query heads per KV head: the products are contractions -> matrix cores
+        pa::DecodeLaunch a{static_cast<_Float16*>(out), ws_ml, ws_acc, static_cast<const _Float16*>(q),
+                           static_cast<const _Float16*>(k_cache), static_cast<const _Float16*>(v_cache),
+                           block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads,
+                           num_blocks, block_size, scale_log2, p, L.num_parts, len_cap, st};
+        e = pa::launch_gqa_mfma(a);
+    } else {
+        MainFn main_fn = pick_main(head_dim, block_size);
+        hipLaunchKernelGGL(main_fn, dim3((unsigned)num_heads, (unsigned)num_seqs, (unsigned)L.num_parts),
+                           dim3(kThreads), 0, st, static_cast<_Float16*>(out), ws_ml, ws_acc,
+                           static_cast<const _Float16*>(q), static_cast<const _Float16*>(k_cache),
+                           static_cast<const _Float16*>(v_cache), block_tables, max_blocks_per_seq, context_lens,
+                           num_heads, num_kv_heads, num_blocks, scale_log2, p, L.num_parts, len_cap);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "pa_decode: %s", hipGetErrorString(e));
     if (L.num_parts > 1) {
         const unsigned threads = head_dim < 64 ? 64u : (unsigned)head_dim;

@@ -1,0 +1,394 @@
+// Grouped-query paged decode attention on the CDNA4 matrix cores (gfx950).
+//
+// What is computed is the same as for every other pa_decode shape: each
+// query head attends to its sequence's n cached keys/values through the
+// block table, textbook softmax attention over the logically contiguous K/V
+// (lpnh.cn/news/1824136, 2.2 and 3.2 step 4; lpnh.cn/news/2758356, 2.1 for
+// the KV-head dimension of a block).  This kernel serves the case where g =
+// num_heads / num_kv_heads query heads share one KV head (2 <= g <= 16,
+// head_dim 128): then every K/V element read from HBM meets g queries, and
+// the two products are small dense contractions,
+//     S^T[t, q] = sum_d K[t, d] Q[q, d]        (16 tokens x 16 queries x 128)
+//     O[q, d]  += sum_t P[q, t] V[t, d]         (16 queries x 128 x 16 tokens)
+// which run on v_mfma_f32_16x16x16_f16 (fp16 inputs, fp32 accumulation).
+// The kernel is still HBM-bound: about 4g flops per 2 bytes of K/V, far
+// below the matrix cores' ridge, so the design serves the loads.
+//
+// Layout (one 256-thread workgroup = 4 wave64s per (KV head, sequence,
+// context partition); KV head fastest in the grid so every XCD streams the
+// same bytes; a wave step is one 16-token tile, steps dealt round-robin to
+// the waves, three tiles in flight per wave when a tile lies in one block):
+//  * MFMA 16x16x16 lane layout: A[m][k] is held by lane m + 16*(k/4),
+//    B[k][n] by lane n + 16*(k/4), C[m][n] by lane n + 16*(m/4).
+//  * QK: A = K tile (m = token), B = Q^T (n = query head of the group,
+//    zero-padded past g).  The contraction index k is mapped onto head_dim so
+//    that lane (m, j) reads 64 contiguous bytes of token m's row with four
+//    16-byte loads -- for load u, d = 8*(4u + j) .. +7 -- and each half of a
+//    load is one MFMA operand: no register shuffles.
+//  * The result S^T lands with lane (n, j) holding tokens 4j..4j+3 of query
+//    n: exactly the A-operand layout of P for the PV product, so the online
+//    softmax (running max / sum per query, base 2, log2(e) folded into the
+//    scale) runs in place and P goes to the matrix core as fp16.
+//  * PV: B = V tile.  Output column n of d-tile c is mapped to d = 8n + c, so
+//    lane (n, j) loads 16 contiguous bytes (d = 8n .. 8n+7) of tokens
+//    4j..4j+3 -- four 16-byte loads that together read every V row whole --
+//    and element c of the four loads is the B operand of d-tile c.
+//  * Masking by select: a token past the context, or behind a table entry
+//    outside the pool, gets S = -inf and V = 0, so NaN in unused rows cannot
+//    reach the sums (0 * NaN would).
+//  * Normalisation uses the same fp16-rounded weights the matrix core saw,
+//    so each output is an exact convex combination of V rows up to fp32
+//    rounding.
+//  * The 4 waves' (m, l, O) are merged through LDS; rows split over several
+//    partitions leave (m, l, O) in the workspace for the shared reduce
+//    kernel, in the same layout as the one-query-per-KV-head kernel.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "decode_internal.h"
+
+namespace {
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;                // head_dim served here
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kTile = 16;              // tokens per wave step
+constexpr int kQkSteps = kD / 16;      // MFMAs per QK tile (k = 16 each)
+constexpr int kDTiles = kD / 16;       // output column tiles of 16
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ half8_t as_h8(u32x4 u) { return __builtin_bit_cast(half8_t, u); }
+
+// One 16-token tile as this lane holds it.
+struct Tile {
+    u32x4 k[4];        // K row (token l%16), d = 8*(4u + l/16) .. +7
+    u32x4 v[4];        // V rows (tokens 4*(l/16) + i), d = 8*(l%16) .. +7
+    bool valid[4];     // tokens 4*(l/16) + i: inside the context and the pool
+};
+
+struct Softmax {
+    float m, l;        // running max (base 2) and sum of query l%16
+    float4_t o[kDTiles];   // O[query 4*(l/16) + i][d = 8*(l%16) + c] in o[c][i]
+};
+
+// Tile loads when a tile lies inside one block (B >= 16): `phys` is the
+// block's table entry, read ahead by the caller with a scalar load.
+template <int B>
+__device__ __forceinline__ void load_tile_block(Tile& t, int t0, int end, int32_t phys,
+                                                const _Float16* __restrict__ kbase,
+                                                const _Float16* __restrict__ vbase, int64_t blk_stride,
+                                                int32_t num_blocks, int lane) {
+    const int n = lane & 15;
+    const int j = lane >> 4;
+    const bool ok = (uint32_t)phys < (uint32_t)num_blocks;
+    const int64_t base = (int64_t)(ok ? phys : 0) * blk_stride + (int64_t)(t0 % B) * kD;
+    // rows past the context are read from the same block and masked later
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        t.k[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + base + n * kD + 8 * (4 * u + j)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        t.valid[i] = ok && t0 + 4 * j + i < end;
+        t.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + base + (4 * j + i) * kD + 8 * n));
+    }
+}
+
+// Tile loads when a tile spans several blocks (B < 16): every row looks up
+// its own table entry.
+template <int B>
+__device__ __forceinline__ void load_tile_rows(Tile& t, int t0, int end, const int32_t* __restrict__ trow,
+                                               const _Float16* __restrict__ kbase,
+                                               const _Float16* __restrict__ vbase, int64_t blk_stride,
+                                               int32_t num_blocks, int lane) {
+    const int n = lane & 15;
+    const int j = lane >> 4;
+    {
+        const int tk = t0 + n;
+        const int tc = tk < end ? tk : end - 1;        // keeps the table index inside the sequence
+        const int32_t phys = trow[tc / B];
+        const bool ok = (uint32_t)phys < (uint32_t)num_blocks;
+        const int64_t row = (int64_t)(ok ? phys : 0) * blk_stride + (int64_t)(tc % B) * kD;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            t.k[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + row + 8 * (4 * u + j)));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tv = t0 + 4 * j + i;
+        const int tc = tv < end ? tv : end - 1;
+        const int32_t phys = trow[tc / B];
+        const bool ok = (uint32_t)phys < (uint32_t)num_blocks;
+        t.valid[i] = tv < end && ok;
+        const int64_t row = (int64_t)(ok ? phys : 0) * blk_stride + (int64_t)(tc % B) * kD;
+        t.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + row + 8 * n));
+    }
+}
+
+__device__ __forceinline__ void consume_tile(Softmax& st, const Tile& t, const half4_t (&qb)[kQkSteps],
+                                             float scale_log2, int lane) {
+    const int j = lane >> 4;
+    // S^T = K Q^T: lane holds S^T[token 4j+i][query l%16]
+    float4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kQkSteps; ++c) {
+        const half8_t kk = as_h8(t.k[c >> 1]);
+        const half4_t a = (c & 1) ? half4_t{kk[4], kk[5], kk[6], kk[7]} : half4_t{kk[0], kk[1], kk[2], kk[3]};
+        s = __builtin_amdgcn_mfma_f32_16x16x16f16(a, qb[c], s, 0, 0, 0);
+    }
+    // online softmax of query l%16 over the tile's 16 tokens (4 per lane, 4 lanes)
+    float sc[4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        sc[i] = t.valid[i] ? s[i] * scale_log2 : -INFINITY;
+        mt = fmaxf(mt, sc[i]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(st.m, mt);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(st.m - m_use);
+    half4_t p;
+    float lt = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        p[i] = (_Float16)fast_exp2(sc[i] - m_use);
+        lt += (float)p[i];                     // the weights the matrix core sees
+    }
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    st.l = st.l * alpha + lt;
+    st.m = m_new;
+    // Rescale O rows (queries 4j+i) by their query's alpha, held by lane
+    // 4j+i -- only when some running max moved: once the maxima settle most
+    // tiles skip it, and skipping a multiply by exactly 1 changes no bit.
+    if (__any(alpha != 1.f)) {
+        float ar[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ar[i] = __shfl(alpha, 4 * j + i);
+#pragma unroll
+        for (int c = 0; c < kDTiles; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) st.o[c][i] *= ar[i];
+    }
+    // O += P V per d-tile.  Rows of masked tokens may hold anything (NaN in
+    // an unused tail row): in a tile with any masked row they are zeroed by
+    // select first, since a zero weight times NaN is still NaN.
+    auto pv = [&](const u32x4 (&v)[4]) {
+        const half8_t v0 = as_h8(v[0]), v1 = as_h8(v[1]), v2 = as_h8(v[2]), v3 = as_h8(v[3]);
+#pragma unroll
+        for (int c = 0; c < kDTiles; ++c) {
+            const half4_t b = {v0[c], v1[c], v2[c], v3[c]};
+            st.o[c] = __builtin_amdgcn_mfma_f32_16x16x16f16(p, b, st.o[c], 0, 0, 0);
+        }
+    };
+    if (__all(t.valid[0] && t.valid[1] && t.valid[2] && t.valid[3])) {
+        pv(t.v);
+    } else {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const u32x4 vz[4] = {t.valid[0] ? t.v[0] : z, t.valid[1] ? t.v[1] : z, t.valid[2] ? t.v[2] : z,
+                             t.valid[3] ? t.v[3] : z};
+        pv(vz);
+    }
+}
+
+template <int B>
+__global__ void __launch_bounds__(kThreads)
+decode_gqa_mfma_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
+                       const _Float16* __restrict__ q, const _Float16* __restrict__ k_cache,
+                       const _Float16* __restrict__ v_cache, const int32_t* __restrict__ tables,
+                       int32_t max_blocks, const int32_t* __restrict__ lens, int32_t num_heads,
+                       int32_t num_kv_heads, int32_t num_blocks, float scale_log2, int32_t part_size,
+                       int32_t num_parts, int64_t len_cap) {
+    const int kvh = blockIdx.x;
+    const int s = blockIdx.y;
+    const int part = blockIdx.z;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = num_heads / num_kv_heads;
+
+    const int32_t n_raw = lens[s];
+    const bool bad_len = n_raw < 0 || (int64_t)n_raw > len_cap;
+    const int n = bad_len ? 0 : n_raw;
+    const int start = part * part_size;
+    if (part > 0 && start >= n) return;
+    const int end = min(start + part_size, n);
+    const int np = (n + part_size - 1) / part_size;
+
+    // Q^T operands: lane (query l%16, group j) holds d = 8*(4u + j) + 4*(c&1) + 0..3 for c = 2u + (c&1)
+    half4_t qb[kQkSteps];
+    {
+        const int qi = lane & 15;
+        const int j = lane >> 4;
+        const bool live = qi < g;
+        const _Float16* qrow = q + ((int64_t)s * num_heads + (int64_t)kvh * g + (live ? qi : 0)) * kD;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const half8_t h = as_h8(live ? *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * u + j)) : z);
+            qb[2 * u] = half4_t{h[0], h[1], h[2], h[3]};
+            qb[2 * u + 1] = half4_t{h[4], h[5], h[6], h[7]};
+        }
+    }
+
+    const int32_t* trow = tables + (int64_t)s * max_blocks;
+    const int64_t slab = (int64_t)B * kD;
+    const _Float16* kbase = k_cache + (int64_t)kvh * slab;
+    const _Float16* vbase = v_cache + (int64_t)kvh * slab;
+    const int64_t blk_stride = (int64_t)num_kv_heads * slab;
+
+    Softmax st;
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int c = 0; c < kDTiles; ++c) st.o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    const int ntok = end > start ? end - start : 0;
+    const int nsteps = (ntok + kTile - 1) / kTile;
+    if (wave < nsteps) {
+        Tile A, Bt;
+        if constexpr (B >= kTile) {
+            // One table entry per tile, read with scalar loads a tile ahead of
+            // its use; three tiles in flight per wave (A, Bt, C rotate).
+            Tile C;
+            auto entry = [&](int stp) { return trow[(start + stp * kTile) / B]; };
+            auto issue = [&](Tile& t, int stp, int32_t phys) {
+                load_tile_block<B>(t, start + stp * kTile, end, phys, kbase, vbase, blk_stride, num_blocks, lane);
+            };
+            int stp = wave;
+            issue(A, stp, entry(stp));
+            if (stp + kWaves < nsteps) issue(Bt, stp + kWaves, entry(stp + kWaves));
+            int32_t tnext = stp + 2 * kWaves < nsteps ? entry(stp + 2 * kWaves) : 0;
+            // before each consume: the tile 2 steps ahead is issued, the entry 3 steps ahead read
+            auto advance = [&](Tile& t, int st) {
+                const int ahead = st + 2 * kWaves;
+                if (ahead < nsteps) {
+                    const int32_t cur = tnext;
+                    tnext = ahead + kWaves < nsteps ? entry(ahead + kWaves) : 0;
+                    issue(t, ahead, cur);
+                }
+            };
+            for (;;) {
+                advance(C, stp);
+                consume_tile(st, A, qb, scale_log2, lane);
+                stp += kWaves;
+                if (stp >= nsteps) break;
+                advance(A, stp);
+                consume_tile(st, Bt, qb, scale_log2, lane);
+                stp += kWaves;
+                if (stp >= nsteps) break;
+                advance(Bt, stp);
+                consume_tile(st, C, qb, scale_log2, lane);
+                stp += kWaves;
+                if (stp >= nsteps) break;
+            }
+        } else {
+            int stp = wave;
+            load_tile_rows<B>(A, start + stp * kTile, end, trow, kbase, vbase, blk_stride, num_blocks, lane);
+            for (;;) {
+                int nx = stp + kWaves;
+                if (nx >= nsteps) { consume_tile(st, A, qb, scale_log2, lane); break; }
+                load_tile_rows<B>(Bt, start + nx * kTile, end, trow, kbase, vbase, blk_stride, num_blocks, lane);
+                consume_tile(st, A, qb, scale_log2, lane);
+                stp = nx;
+                nx = stp + kWaves;
+                if (nx >= nsteps) { consume_tile(st, Bt, qb, scale_log2, lane); break; }
+                load_tile_rows<B>(A, start + nx * kTile, end, trow, kbase, vbase, blk_stride, num_blocks, lane);
+                consume_tile(st, Bt, qb, scale_log2, lane);
+                stp = nx;
+            }
+        }
+    }
+
+    // Merge the 4 waves.  s_o[w][q][d] holds wave w's unnormalised output.
+    __shared__ float s_m[kWaves][16];
+    __shared__ float s_l[kWaves][16];
+    __shared__ float s_o[kWaves][16][kD];
+    {
+        const int ncol = lane & 15;
+        const int j = lane >> 4;
+        if (j == 0) {
+            s_m[wave][ncol] = st.m;
+            s_l[wave][ncol] = st.l;
+        }
+#pragma unroll
+        for (int c = 0; c < kDTiles; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s_o[wave][4 * j + i][8 * ncol + c] = st.o[c][i];
+    }
+    __syncthreads();
+
+    for (int idx = threadIdx.x; idx < g * kD; idx += kThreads) {
+        const int qi = idx / kD;
+        const int d = idx - qi * kD;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][qi]);
+        float L = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float mw = s_m[w][qi];
+            const float wt = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+            L = fmaf(wt, s_l[w][qi], L);
+            o = fmaf(wt, s_o[w][qi][d], o);
+        }
+        const int64_t head_row = (int64_t)s * num_heads + (int64_t)kvh * g + qi;
+        if (bad_len) {
+            out[head_row * kD + d] = (_Float16)NAN;
+        } else if (np <= 1) {
+            out[head_row * kD + d] = L > 0.f ? (_Float16)(o / L) : (_Float16)0.f;
+        } else {
+            const int64_t slot = head_row * num_parts + part;
+            ws_acc[slot * kD + d] = o;
+            if (d == 0) {
+                ws_ml[2 * slot] = M;
+                ws_ml[2 * slot + 1] = L;
+            }
+        }
+    }
+}
+
+using GqaFn = void (*)(_Float16*, float*, float*, const _Float16*, const _Float16*, const _Float16*,
+                       const int32_t*, int32_t, const int32_t*, int32_t, int32_t, int32_t, float, int32_t,
+                       int32_t, int64_t);
+
+GqaFn pick(int32_t b) {
+    switch (b) {
+        case 1: return decode_gqa_mfma_kernel<1>;
+        case 2: return decode_gqa_mfma_kernel<2>;
+        case 4: return decode_gqa_mfma_kernel<4>;
+        case 8: return decode_gqa_mfma_kernel<8>;
+        case 16: return decode_gqa_mfma_kernel<16>;
+        case 32: return decode_gqa_mfma_kernel<32>;
+        case 64: return decode_gqa_mfma_kernel<64>;
+        case 128: return decode_gqa_mfma_kernel<128>;
+        default: return nullptr;
+    }
+}
+
+}  // namespace
+
+namespace pa {
+
+bool gqa_mfma_supported(int32_t head_dim, int32_t block_size, int32_t group) {
+    return head_dim == kD && group >= 2 && group <= 16 && pick(block_size) != nullptr;
+}
+
+hipError_t launch_gqa_mfma(const DecodeLaunch& a) {
+    GqaFn fn = pick(a.block_size);
+    hipLaunchKernelGGL(fn, dim3((unsigned)a.num_kv_heads, (unsigned)a.num_seqs, (unsigned)a.num_parts),
+                       dim3(kThreads), 0, a.stream, a.out, a.ws_ml, a.ws_acc, a.q, a.k_cache, a.v_cache,
+                       a.tables, a.max_blocks, a.lens, a.num_heads, a.num_kv_heads, a.num_blocks, a.scale_log2,
+                       a.part_size, a.num_parts, a.len_cap);
+    return hipGetLastError();
+}
+
+}  // namespace pa

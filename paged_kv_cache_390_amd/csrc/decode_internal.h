@@ -1,0 +1,39 @@
+// Launch interface shared by the decode kernels of the library (not part of
+// the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pa {
+
+// Everything one pa_decode partition-kernel launch needs; pointers are
+// device pointers, the workspace pointers null when no sequence is split.
+struct DecodeLaunch {
+    _Float16* out;
+    float* ws_ml;
+    float* ws_acc;
+    const _Float16* q;
+    const _Float16* k_cache;
+    const _Float16* v_cache;
+    const int32_t* tables;
+    int32_t max_blocks;
+    const int32_t* lens;
+    int32_t num_seqs;
+    int32_t num_heads;
+    int32_t num_kv_heads;
+    int32_t num_blocks;
+    int32_t block_size;
+    float scale_log2;
+    int32_t part_size;
+    int32_t num_parts;
+    int64_t len_cap;
+    hipStream_t stream;
+};
+
+// Grouped-query decode on the matrix cores: head_dim 128, 2 <= group <= 16.
+bool gqa_mfma_supported(int32_t head_dim, int32_t block_size, int32_t group);
+hipError_t launch_gqa_mfma(const DecodeLaunch& a);
+
+}  // namespace pa

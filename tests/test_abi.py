@@ -74,13 +74,32 @@ def test_decode_with_no_sequences_is_a_no_op():
 
 def test_workspace_size():
     L = pa.lib()
-    assert L.pa_decode_workspace_size(64, 32, 128, 512, 512) == 0        # one partition
-    n = L.pa_decode_workspace_size(64, 32, 128, 2048, 512)
+    assert L.pa_decode_workspace_size(64, 32, 32, 128, 16, 512, 512) == 0        # one partition
+    n = L.pa_decode_workspace_size(64, 32, 32, 128, 16, 2048, 512)
     rows = 64 * 32 * 4
     assert n >= rows * (128 + 2) * 4 and n % 256 == 0
-    assert L.pa_decode_workspace_size(64, 32, 100, 2048, 512) == ctypes.c_size_t(-1).value
-    assert L.pa_decode_workspace_size(64, 32, 128, 2048, 100) == ctypes.c_size_t(-1).value
-    assert L.pa_decode_default_partition(128, 16) % 128 == 0
+    assert L.pa_decode_workspace_size(64, 32, 32, 100, 16, 2048, 512) == ctypes.c_size_t(-1).value
+    assert L.pa_decode_workspace_size(64, 32, 32, 128, 16, 2048, 100) == ctypes.c_size_t(-1).value
+    assert L.pa_decode_workspace_size(64, 32, 5, 128, 16, 2048, 512) == ctypes.c_size_t(-1).value
+    assert L.pa_decode_workspace_size(64, 32, 32, 128, 3, 2048, 512) == ctypes.c_size_t(-1).value
+
+
+def test_default_partition_keeps_the_gpu_busy():
+    """The longest of 2048/1024/512/256 tokens with >= 4 workgroups per
+    resident slot (1024 slots for one query per KV head, 512 for groups of
+    2..16 at head_dim 128), counting full partitions of the longest
+    sequence; 256 when even that is not reached."""
+    L = pa.lib()
+    assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2048) == 1024      # 2048 rows x 2
+    assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2112) == 1024
+    assert L.pa_decode_default_partition(256, 64, 8, 128, 16, 2048) == 2048     # grouped: 2048 rows x 1
+    assert L.pa_decode_default_partition(64, 64, 8, 128, 16, 2048) == 512       # 512 rows x 4
+    assert L.pa_decode_default_partition(16, 32, 32, 128, 16, 4096) == 512      # 512 rows x 8
+    assert L.pa_decode_default_partition(1, 8, 8, 128, 16, 1000) == 256
+    assert L.pa_decode_default_partition(64, 32, 32, 64, 16, 2048) == 1024      # head_dim 64: vector kernel
+    assert L.pa_decode_default_partition(64, 32, 7, 128, 16, 2048) == -1
+    for args in [(64, 32, 32, 128, 16, 2048), (256, 64, 8, 128, 16, 2048), (1, 8, 8, 128, 16, 1000)]:
+        assert L.pa_decode_default_partition(*args) % 128 == 0
 
 
 def test_reshape_rejects_bad_arguments():

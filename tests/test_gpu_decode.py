@@ -140,7 +140,7 @@ def test_workspace_reused_across_calls_of_different_sizes():
     (its contents on entry are ignored).  Outputs start as NaN, so a row
     whose merge never ran would show; repeated calls agree bit for bit."""
     dev = device()
-    ws = torch.zeros(pa.pa_decode_workspace_size(8, 8, 128, 4096, 128), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(pa.pa_decode_workspace_size(8, 8, 1, 128, 16, 4096, 128), dtype=torch.uint8, device=dev)
     cases = [([1000, 37, 513, 2048, 5, 129, 256, 4000], 8, 8),
              ([300, 1], 4, 4),
              ([4096, 4096, 4096], 8, 2),

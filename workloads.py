@@ -137,6 +137,20 @@ def llama7b_decode(seed: int = 0, num_seqs: int = 64, max_len: int = 2048,
                       perm.reshape(num_seqs, width), 1.0 / math.sqrt(head_dim), seed, layers)
 
 
+def gqa_decode(seed: int = 0, num_seqs: int = 256, max_len: int = 2048, block_size: int = 16,
+               num_heads: int = 64, num_kv_heads: int = 8, head_dim: int = 128,
+               layers: int = 1, min_len: int = 1) -> PoolDecode:
+    """Grouped-query decode: 8 query heads share each of 8 KV heads (the
+    attention shape of the 70B-class model the lpnh.cn/news/1824136 page
+    sizes in section 1.1), otherwise drawn like llama7b_decode.  256
+    sequences put about 1 GB of K/V behind one layer's decode, as in the
+    Llama-2-7B batch."""
+    w = llama7b_decode(seed=seed, num_seqs=num_seqs, max_len=max_len, block_size=block_size,
+                       num_heads=num_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                       layers=layers, min_len=min_len)
+    return w
+
+
 def long_context(seed: int = 0, num_seqs: int = 16, ctx: int = 4096,
                  block_size: int = 16, num_heads: int = 32, num_kv_heads: int = 32,
                  head_dim: int = 128, layers: int = 32) -> PoolDecode:
