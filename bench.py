@@ -47,9 +47,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="llama7b", choices=["llama7b", "gqa", "long", "copy"],
+    p.add_argument("--workload", default="llama7b", choices=["llama7b", "gqa", "long", "copy", "swap"],
                    help="llama7b: the Llama-2-7B decode batch (default); gqa: 64 query heads over 8 KV "
-                        "heads (matrix-core kernel); long: 16 x 4096 tokens; copy: block-copy calibration")
+                        "heads (matrix-core kernel); long: 16 x 4096 tokens; copy: block-copy calibration; "
+                        "swap: block swaps between HBM and pinned host memory")
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--batch", type=int, default=0, help="sequences (0: 64 for llama7b, 256 for gqa)")
     p.add_argument("--block-size", type=int, default=16)
@@ -110,6 +111,8 @@ def main():
 
     if args.workload == "copy":
         return copy_bench(args, dev)
+    if args.workload == "swap":
+        return swap_bench(args, dev)
 
     L = args.layers
     B = args.block_size
@@ -306,6 +309,60 @@ def copy_bench(args, dev):
                       "us_per_call": round(avg * 1e6, 2),
                       "config": {"workload": "copy-blocks", "pairs": npairs, "block_bytes": block_bytes}}),
           flush=True)
+
+
+def swap_bench(args, dev):
+    """Swap a batch of 16 sequences x 2048 tokens (Llama-2-7B heads, B=16)
+    out to pinned host memory and back, over --layers layers (default here
+    4: 2 GiB each way).  Timed with HIP events around each pa_swap_blocks
+    call; the host block manager's bookkeeping and the pairs' upload sit
+    outside the events.  GB/s per direction against PCIe 5.0 x16 (64 GB/s
+    per direction)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_390_amd as pa
+
+    L = args.layers if args.layers != 32 else 4
+    S, n, Hkv, B, D = 16, 2048, 32, 16, 128
+    need = S * n // B
+    NB, NH = need + 64, need + 64
+    log(f"[bench] swap: {S} x {n} tokens, {L} layers, {2 * L} caches of {NB} blocks x {Hkv * B * D * 2 // 1024} KiB")
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    caches = [torch.randn((NB, Hkv, B, D), generator=g, device=dev, dtype=torch.float16) for _ in range(2 * L)]
+    hosts = [torch.empty((NH, Hkv, B, D), dtype=torch.float16).pin_memory() for _ in range(2 * L)]
+    bm = pa.BlockManager(NB, B, NH)
+    for s in range(S):
+        bm.add_sequence(s, n)
+    seqs = list(range(S))
+    moved = need * len(caches) * Hkv * B * D * 2        # bytes per direction: every block of every cache
+    t_out, t_in = [], []
+    for it in range(args.warmup + args.steps):
+        pout = torch.from_numpy(bm.swap_out(seqs)).to(dev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        pa.pa_swap_blocks(caches, hosts, pout, pa.PA_SWAP_OUT)
+        b.record()
+        pin = torch.from_numpy(bm.swap_in(seqs)).to(dev)
+        c, d = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c.record()
+        pa.pa_swap_blocks(caches, hosts, pin, pa.PA_SWAP_IN)
+        d.record()
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            t_out.append(a.elapsed_time(b) / 1e3)
+            t_in.append(c.elapsed_time(d) / 1e3)
+    out_gbs = moved / (sum(t_out) / len(t_out)) / 1e9
+    in_gbs = moved / (sum(t_in) / len(t_in)) / 1e9
+    log(f"[bench] swap out {moved / 2**30:.2f} GiB in {1e3 * sum(t_out) / len(t_out):.2f} ms = {out_gbs:.1f} GB/s; "
+        f"in {1e3 * sum(t_in) / len(t_in):.2f} ms = {in_gbs:.1f} GB/s")
+    print(json.dumps({"metric": "KV block swap GB/s per direction (HBM <-> pinned host)", "value": round(
+        min(out_gbs, in_gbs), 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": True, "swap_out_GB_s": round(out_gbs, 2), "swap_in_GB_s": round(in_gbs, 2),
+        "bytes_per_direction": moved, "pcie_peak_GB_s": 64.0,
+        "config": {"workload": "swap", "sequences": S, "tokens": n, "layers": L, "num_kv_heads": Hkv,
+                   "block_size": B, "head_dim": D}}), flush=True)
 
 
 if __name__ == "__main__":

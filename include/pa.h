@@ -175,6 +175,38 @@ int pa_copy_blocks(void *const *k_caches, void *const *v_caches,
                    int32_t dtype, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Whole-block copies between the device cache and a host cache ("swap").
+ * Under memory pressure a sequence's KV blocks can be moved out to host
+ * memory and back later, at a large latency cost ([lpnh-1824136] 4.2).  The
+ * block manager's pa_bm_swap_out / pa_bm_swap_in produce the pairs.
+ *
+ *   dev_caches     HOST array of num_caches device pointers: cache tensors of
+ *                  dev_num_blocks blocks of block_elems fp16 each (list the K
+ *                  and the V tensor of every layer)
+ *   host_caches    HOST array of num_caches pointers to pinned, device-mapped
+ *                  host memory (hipHostMalloc, or a pinned torch tensor) of
+ *                  host_num_blocks blocks each; host_caches[i] mirrors
+ *                  dev_caches[i]
+ *   pairs          device, int64 [num_pairs, 2]: (source id, destination id);
+ *                  PA_SWAP_OUT copies device block pairs[i][0] to host block
+ *                  pairs[i][1], PA_SWAP_IN host block pairs[i][0] to device
+ *                  block pairs[i][1].  Destinations must be distinct.  A pair
+ *                  with an id outside its pool is skipped.
+ * The copy runs as one kernel per 128 caches that reads or writes the host
+ * side through its device mapping (PCIe).  PA_ERR_INVALID, before anything is
+ * enqueued, if a device pointer is not device memory or a host pointer is not
+ * pinned, mapped host memory.  The caller orders it on the stream before
+ * anything that reuses the source blocks (pa_bm_swap_out frees them at once).
+ * ------------------------------------------------------------------------ */
+enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 };
+
+int pa_swap_blocks(void *const *dev_caches, void *const *host_caches,
+                   int32_t num_caches, const int64_t *pairs, int32_t num_pairs,
+                   int32_t dev_num_blocks, int32_t host_num_blocks,
+                   int64_t block_elems, int32_t direction, int32_t dtype,
+                   void *stream);
+
+/* ------------------------------------------------------------------------
  * Host block manager: free list, reference counts, per-sequence tables.
  * Host memory only; every call takes an internal lock, so calls from
  * several threads are serialised ([lpnh-2758356] 4.3: count updates must be
@@ -197,8 +229,11 @@ int pa_copy_blocks(void *const *k_caches, void *const *v_caches,
  * ------------------------------------------------------------------------ */
 typedef struct pa_bm pa_bm;
 
-/* NULL on bad sizes or out of host memory. */
+/* NULL on bad sizes or out of host memory.  pa_bm_create has no host pool
+ * (num_host_blocks = 0). */
 pa_bm *pa_bm_create(int32_t num_blocks, int32_t block_size);
+pa_bm *pa_bm_create_with_host(int32_t num_blocks, int32_t block_size,
+                              int32_t num_host_blocks);
 void pa_bm_destroy(pa_bm *bm);
 
 /* New sequence with n_tokens tokens: ceil(n_tokens / B) blocks taken from
@@ -232,8 +267,33 @@ int pa_bm_append_tokens(pa_bm *bm, const int64_t *seqs, int32_t n,
                         int32_t *num_cow_out, int32_t *num_done_out);
 
 /* Release seq: counts - 1, ids reaching 0 pushed on the free list in
- * logical order. */
+ * logical order (the host pool's, for a swapped-out sequence). */
 int pa_bm_free_sequence(pa_bm *bm, int64_t seq);
+
+/* Swap a group of n distinct sequences out to the host pool, or back in.
+ * Every distinct block of the group, in order of first appearance
+ * (sequence order, then table order), gets one block of the other pool
+ * (allocated from the end of its free list) whose count is the number of
+ * group members holding it, so blocks shared by forks stay shared; the old
+ * block's count drops by that number and it is freed at 0.  pairs_out
+ * receives (old id, new id) rows -- (device, host) for swap_out, (host,
+ * device) for swap_in -- and *num_pairs_out their number.  A swapped-out
+ * sequence can only be swapped in or freed (other calls: PA_ERR_STATE).
+ * PA_ERR_OOM if the other pool has too few free blocks, PA_ERR_INVALID if
+ * cap is too small: both leave the state unchanged. */
+int pa_bm_swap_out(pa_bm *bm, const int64_t *seqs, int32_t n,
+                   int64_t *pairs_out, int32_t cap, int32_t *num_pairs_out);
+int pa_bm_swap_in(pa_bm *bm, const int64_t *seqs, int32_t n,
+                  int64_t *pairs_out, int32_t cap, int32_t *num_pairs_out);
+/* 1 if seq is swapped out, 0 if resident, -1 if unknown. */
+int32_t pa_bm_is_swapped(pa_bm *bm, int64_t seq);
+/* Holders of host block hblk (0 if free); -1 if outside the host pool. */
+int32_t pa_bm_host_refcount(pa_bm *bm, int32_t hblk);
+/* Like pa_bm_free_list, for the host pool. */
+int32_t pa_bm_host_free_list(pa_bm *bm, int32_t *out, int32_t cap);
+/* Copies min(len, cap) ids of seq's table (host ids while swapped out) into
+ * out; returns the table length, or -1 if seq is unknown. */
+int32_t pa_bm_seq_table(pa_bm *bm, int64_t seq, int32_t *out, int32_t cap);
 
 /* Pack tables of the given sequences into tables_out[n, max_blocks] (padding
  * -1) and their lengths into lens_out[n] (may be NULL).  PA_ERR_INVALID if a

@@ -170,3 +170,29 @@ def copy_blocks(k_caches: Sequence[np.ndarray], v_caches: Sequence[np.ndarray],
                                   block_elems, NB)
     if rc != 0:
         raise RuntimeError(f"oracle_copy_blocks failed: {rc}")
+
+
+def move_blocks(dst_pools: Sequence[np.ndarray], src_pools: Sequence[np.ndarray], pairs: np.ndarray) -> None:
+    """In place, for every pool i and pair row (s, d): dst_pools[i][d] :=
+    src_pools[i][s] -- whole blocks, bit for bit.  This is the data movement
+    of a swap between the device pool and the host pool ([lpnh-1824136] 4.2:
+    KV blocks can be moved out to host memory and back).  Destinations must
+    be distinct; the source and destination pools are different arrays, so
+    the order of the rows does not matter."""
+    if len(dst_pools) != len(src_pools):
+        raise ValueError("pool count mismatch")
+    _need(pairs, np.int64, "pairs")
+    if pairs.size == 0:
+        return
+    if pairs.ndim != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [N, 2]")
+    if len(set(pairs[:, 1].tolist())) != pairs.shape[0]:
+        raise ValueError("destinations must be distinct")
+    for dst, src in zip(dst_pools, src_pools):
+        if dst.dtype != src.dtype or dst.shape[1:] != src.shape[1:]:
+            raise ValueError("pools must share the block shape")
+        if np.any(pairs[:, 0] < 0) or np.any(pairs[:, 0] >= src.shape[0]) or \
+           np.any(pairs[:, 1] < 0) or np.any(pairs[:, 1] >= dst.shape[0]):
+            raise ValueError("block id outside its pool")
+        for sblk, dblk in pairs.tolist():
+            dst[dblk] = src[sblk]

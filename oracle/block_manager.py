@@ -32,6 +32,10 @@ Rules modelled:
   * Slot of logical position p: table[p // B] * B + p % B ([5688vip]
     分页机制 figure; [lpnh-2758356] 2.2).
 
+  * Under memory pressure a sequence's KV blocks can be moved to host memory
+    and back ("swap": [lpnh-1824136] 4.2 names it as a supported, slow
+    option for serving very long contexts when latency can be traded).
+
 Readings where the pages leave a step open (also listed in the design doc):
   * Fill level is tracked per sequence (its length) rather than per block;
     for an unshared block the two agree, and for a shared block the
@@ -41,6 +45,15 @@ Readings where the pages leave a step open (also listed in the design doc):
   * A batch of appends is processed in the order given; samples that share a
     block therefore copy one after another until the last holder finds a
     count of 1 and writes in place.
+  * Swap works on a group of sequences at once (so blocks shared by forks
+    stay shared): every distinct block of the group, in order of first
+    appearance (sequence order, then table order), gets one block of a host
+    pool -- a second pool with its own free list and counts, allocated like
+    the device pool -- whose count is the number of group members holding
+    it; the device count drops by that number and a block reaching 0 goes
+    back to the device free list in the same order.  Swapping in is the
+    mirror image.  A swapped-out sequence can only be swapped in or freed.
+    A group short of free blocks on the receiving side changes nothing.
 """
 from __future__ import annotations
 
@@ -60,17 +73,29 @@ class StateError(Exception):
 class _Seq:
     table: List[int] = field(default_factory=list)
     length: int = 0
+    swapped: bool = False            # table holds host-pool ids
 
 
 class BlockManagerModel:
-    def __init__(self, num_blocks: int, block_size: int):
-        if num_blocks < 0 or block_size <= 0:
-            raise ValueError("num_blocks >= 0 and block_size > 0 required")
+    def __init__(self, num_blocks: int, block_size: int, num_host_blocks: int = 0):
+        if num_blocks < 0 or block_size <= 0 or num_host_blocks < 0:
+            raise ValueError("num_blocks >= 0, num_host_blocks >= 0 and block_size > 0 required")
         self.num_blocks = num_blocks
         self.block_size = block_size
         self.free: List[int] = list(range(num_blocks))
         self.refcount: List[int] = [0] * num_blocks
         self.seqs: Dict[int, _Seq] = {}
+        self.num_host_blocks = num_host_blocks
+        self.host_free: List[int] = list(range(num_host_blocks))
+        self.host_refcount: List[int] = [0] * num_host_blocks
+
+    def _resident(self, seq: int) -> _Seq:
+        if seq not in self.seqs:
+            raise StateError(f"unknown sequence {seq}")
+        s = self.seqs[seq]
+        if s.swapped:
+            raise StateError(f"sequence {seq} is swapped out")
+        return s
 
     # -- allocation ---------------------------------------------------------
     def _alloc(self) -> Optional[int]:
@@ -120,11 +145,9 @@ class BlockManagerModel:
         self.seqs[seq] = _Seq(table=list(blocks), length=n_tokens)
 
     def fork(self, parent: int, child: int) -> None:
-        if parent not in self.seqs:
-            raise StateError(f"unknown sequence {parent}")
+        p = self._resident(parent)
         if child in self.seqs:
             raise StateError(f"sequence {child} exists")
-        p = self.seqs[parent]
         for b in p.table:
             self.refcount[b] += 1
         self.seqs[child] = _Seq(table=list(p.table), length=p.length)
@@ -134,9 +157,7 @@ class BlockManagerModel:
 
         Returns (slot, cow) where cow is (src, dst) when the shared last
         block had to be copied, else None.  Raises OOM with no change."""
-        if seq not in self.seqs:
-            raise StateError(f"unknown sequence {seq}")
-        s = self.seqs[seq]
+        s = self._resident(seq)
         B = self.block_size
         n = s.length
         cow = None
@@ -162,14 +183,62 @@ class BlockManagerModel:
         if seq not in self.seqs:
             raise StateError(f"unknown sequence {seq}")
         s = self.seqs.pop(seq)
+        count, free = (self.host_refcount, self.host_free) if s.swapped else (self.refcount, self.free)
         for b in s.table:
-            self.refcount[b] -= 1
-            if self.refcount[b] == 0:
-                self.free.append(b)
+            count[b] -= 1
+            if count[b] == 0:
+                free.append(b)
+
+    # -- swap to / from the host pool ---------------------------------------
+    def _move(self, seqs: Sequence[int], out: bool) -> List[Tuple[int, int]]:
+        seqs = [int(q) for q in seqs]
+        if len(set(seqs)) != len(seqs):
+            raise StateError("a sequence appears twice in the group")
+        for q in seqs:
+            if q not in self.seqs:
+                raise StateError(f"unknown sequence {q}")
+            if self.seqs[q].swapped == out:
+                raise StateError(f"sequence {q} is already {'swapped out' if out else 'resident'}")
+        src_count, src_free = (self.refcount, self.free) if out else (self.host_refcount, self.host_free)
+        dst_count, dst_free = (self.host_refcount, self.host_free) if out else (self.refcount, self.free)
+        order: List[int] = []
+        holders: Dict[int, int] = {}
+        for q in seqs:
+            for b in self.seqs[q].table:
+                if b not in holders:
+                    order.append(b)
+                    holders[b] = 0
+                holders[b] += 1
+        if len(order) > len(dst_free):
+            raise OOM()
+        new_id: Dict[int, int] = {}
+        pairs = []
+        for b in order:
+            d = dst_free.pop()
+            dst_count[d] = holders[b]
+            new_id[b] = d
+            pairs.append((b, d))
+            src_count[b] -= holders[b]
+            if src_count[b] == 0:
+                src_free.append(b)
+        for q in seqs:
+            s = self.seqs[q]
+            s.table = [new_id[b] for b in s.table]
+            s.swapped = out
+        return pairs
+
+    def swap_out(self, seqs: Sequence[int]) -> List[Tuple[int, int]]:
+        """Move a group's blocks to the host pool; returns (device id, host
+        id) pairs in order of first appearance.  Raises OOM with no change."""
+        return self._move(seqs, True)
+
+    def swap_in(self, seqs: Sequence[int]) -> List[Tuple[int, int]]:
+        """Move a swapped-out group back; returns (host id, device id) pairs."""
+        return self._move(seqs, False)
 
     # -- queries ------------------------------------------------------------
     def slot(self, seq: int, pos: int) -> int:
-        s = self.seqs[seq]
+        s = self._resident(seq)
         B = self.block_size
         if not 0 <= pos < len(s.table) * B:
             raise IndexError(pos)
@@ -184,7 +253,7 @@ class BlockManagerModel:
     def tables(self, seqs: Sequence[int], max_blocks: int) -> Tuple[List[List[int]], List[int]]:
         rows, lens = [], []
         for q in seqs:
-            t = self.seqs[q].table
+            t = self._resident(q).table
             if len(t) > max_blocks:
                 raise ValueError("max_blocks too small")
             rows.append(t + [-1] * (max_blocks - len(t)))
@@ -195,22 +264,27 @@ class BlockManagerModel:
         return len(self.free)
 
     def check_invariants(self) -> None:
-        """Counts equal the number of tables holding each block; free ids
-        have count 0; every id is either free or held."""
-        held: Dict[int, int] = {}
-        for s in self.seqs.values():
-            if len(set(s.table)) != len(s.table):
-                raise AssertionError("duplicate id within a table")
-            if len(s.table) != self.blocks_for(s.length):
-                raise AssertionError("table length != ceil(len / B)")
-            for b in s.table:
-                held[b] = held.get(b, 0) + 1
-        for b in range(self.num_blocks):
-            if self.refcount[b] != held.get(b, 0):
-                raise AssertionError(f"refcount[{b}]={self.refcount[b]} held={held.get(b, 0)}")
-        if len(set(self.free)) != len(self.free):
-            raise AssertionError("duplicate id on the free list")
-        if set(self.free) & set(held):
-            raise AssertionError("a held block is on the free list")
-        if len(self.free) + len(held) != self.num_blocks:
-            raise AssertionError("free + held != num_blocks")
+        """In each pool (device, host): counts equal the number of tables
+        holding each block; free ids have count 0; every id is either free
+        or held."""
+        for swapped, n, count, free in ((False, self.num_blocks, self.refcount, self.free),
+                                        (True, self.num_host_blocks, self.host_refcount, self.host_free)):
+            held: Dict[int, int] = {}
+            for s in self.seqs.values():
+                if len(set(s.table)) != len(s.table):
+                    raise AssertionError("duplicate id within a table")
+                if len(s.table) != self.blocks_for(s.length):
+                    raise AssertionError("table length != ceil(len / B)")
+                if s.swapped != swapped:
+                    continue
+                for b in s.table:
+                    held[b] = held.get(b, 0) + 1
+            for b in range(n):
+                if count[b] != held.get(b, 0):
+                    raise AssertionError(f"count[{b}]={count[b]} held={held.get(b, 0)} (host={swapped})")
+            if len(set(free)) != len(free):
+                raise AssertionError("duplicate id on a free list")
+            if set(free) & set(held):
+                raise AssertionError("a held block is on a free list")
+            if len(free) + len(held) != n:
+                raise AssertionError("free + held != pool size")

@@ -9,8 +9,8 @@ current HIP stream.  There is no fallback: if the library is not built, every
 call raises.
 
 Functions carry the C names: ``pa_reshape_and_cache``, ``pa_decode``,
-``pa_decode_workspace_size``, ``pa_copy_blocks``; ``BlockManager`` wraps the
-``pa_bm_*`` calls.
+``pa_decode_workspace_size``, ``pa_copy_blocks``, ``pa_swap_blocks``;
+``BlockManager`` wraps the ``pa_bm_*`` calls.
 """
 from __future__ import annotations
 
@@ -31,6 +31,8 @@ PA_ERR_HIP = -3
 PA_ERR_OOM = -4
 PA_ERR_STATE = -5
 PA_DTYPE_F16 = 0
+PA_SWAP_OUT = 0
+PA_SWAP_IN = 1
 
 _lib = None
 
@@ -66,7 +68,15 @@ def lib() -> ctypes.CDLL:
         "pa_decode_workspace_size": ([i32, i32, i32, i32, i32, i32, i32], sz),
         "pa_decode_default_partition": ([i32, i32, i32, i32, i32, i32], i32),
         "pa_copy_blocks": ([P, P, i32, P, i32, i32, i64, i32, P], ctypes.c_int),
+        "pa_swap_blocks": ([P, P, i32, P, i32, i32, i32, i64, i32, i32, P], ctypes.c_int),
         "pa_bm_create": ([i32, i32], P),
+        "pa_bm_create_with_host": ([i32, i32, i32], P),
+        "pa_bm_swap_out": ([P, P, i32, P, i32, P], ctypes.c_int),
+        "pa_bm_swap_in": ([P, P, i32, P, i32, P], ctypes.c_int),
+        "pa_bm_is_swapped": ([P, i64], i32),
+        "pa_bm_host_refcount": ([P, i32], i32),
+        "pa_bm_host_free_list": ([P, P, i32], i32),
+        "pa_bm_seq_table": ([P, i64, P, i32], i32),
         "pa_bm_destroy": ([P], None),
         "pa_bm_add_sequence": ([P, i64, i32, P], ctypes.c_int),
         "pa_bm_set_table": ([P, i64, P, i32, i32], ctypes.c_int),
@@ -245,6 +255,43 @@ def pa_copy_blocks(k_caches: Sequence, v_caches: Sequence, src_dst_pairs) -> Non
                                 _stream(src_dst_pairs.device)), "pa_copy_blocks")
 
 
+def pa_swap_blocks(dev_caches: Sequence, host_caches: Sequence, pairs, direction: int) -> None:
+    """Copy whole blocks between device caches and pinned host caches:
+    direction PA_SWAP_OUT copies device block pairs[i, 0] to host block
+    pairs[i, 1] in every cache, PA_SWAP_IN host pairs[i, 0] to device
+    pairs[i, 1].  dev_caches[i] / host_caches[i]: fp16 tensors of one block
+    shape (list K and V of every layer); pairs: int64 device tensor [N, 2]."""
+    torch = _torch()
+    if len(dev_caches) != len(host_caches):
+        raise ValueError("dev_caches and host_caches differ in length")
+    _dev_tensor(pairs, "pairs", torch.int64, 2)
+    if pairs.shape[1] != 2:
+        raise ValueError("pairs must be [N, 2]")
+    N = pairs.shape[0]
+    C = len(dev_caches)
+    if N == 0 or C == 0:
+        return
+    bshape = tuple(dev_caches[0].shape[1:])
+    for i, t in enumerate(dev_caches):
+        _dev_tensor(t, f"dev_caches[{i}]", torch.float16)
+        if tuple(t.shape[1:]) != bshape or t.shape[0] != dev_caches[0].shape[0]:
+            raise ValueError("all device caches must share one shape")
+    for i, t in enumerate(host_caches):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cpu" or not t.is_pinned():
+            raise ValueError(f"host_caches[{i}]: must be a pinned CPU tensor")
+        if t.dtype != torch.float16 or not t.is_contiguous():
+            raise TypeError(f"host_caches[{i}]: must be contiguous float16")
+        if tuple(t.shape[1:]) != bshape or t.shape[0] != host_caches[0].shape[0]:
+            raise ValueError("all host caches must share one shape, with the device block shape")
+    block_elems = int(np.prod(bshape))
+    dp = (ctypes.c_void_p * C)(*[t.data_ptr() for t in dev_caches])
+    hp = (ctypes.c_void_p * C)(*[t.data_ptr() for t in host_caches])
+    _check(lib().pa_swap_blocks(ctypes.cast(dp, ctypes.c_void_p), ctypes.cast(hp, ctypes.c_void_p), C,
+                                pairs.data_ptr(), N, dev_caches[0].shape[0], host_caches[0].shape[0],
+                                block_elems, int(direction), PA_DTYPE_F16, _stream(pairs.device)),
+           "pa_swap_blocks")
+
+
 # ---------------------------------------------------------------------------
 # host block manager
 # ---------------------------------------------------------------------------
@@ -259,14 +306,15 @@ def _i32(a) -> np.ndarray:
 class BlockManager:
     """Owner of a ``pa_bm`` handle (host memory only)."""
 
-    def __init__(self, num_blocks: int, block_size: int):
+    def __init__(self, num_blocks: int, block_size: int, num_host_blocks: int = 0):
         self._L = lib()
-        h = self._L.pa_bm_create(num_blocks, block_size)
+        h = self._L.pa_bm_create_with_host(num_blocks, block_size, num_host_blocks)
         if not h:
             raise PAError(PA_ERR_INVALID, last_error())
         self._h = ctypes.c_void_p(h)
         self.num_blocks = num_blocks
         self.block_size = block_size
+        self.num_host_blocks = num_host_blocks
 
     def close(self):
         if getattr(self, "_h", None):
@@ -343,6 +391,49 @@ class BlockManager:
         n = self._L.pa_bm_free_list(self._h, None, 0)
         out = np.empty(max(n, 1), dtype=np.int32)
         self._L.pa_bm_free_list(self._h, out.ctypes.data, n)
+        return out[:n].tolist()
+
+    def _move(self, fn, seqs) -> np.ndarray:
+        s = _i64(seqs)
+        cap = 0
+        for q in s.tolist():
+            cap += max(self._L.pa_bm_seq_table(self._h, q, None, 0), 0)
+        pairs = np.empty((max(cap, 1), 2), dtype=np.int64)
+        n = ctypes.c_int32()
+        _check(fn(self._h, s.ctypes.data if s.size else None, s.size, pairs.ctypes.data, cap, ctypes.byref(n)),
+               "swap")
+        return pairs[:n.value]
+
+    def swap_out(self, seqs) -> np.ndarray:
+        """Move a group to the host pool; returns (device id, host id) rows."""
+        return self._move(self._L.pa_bm_swap_out, seqs)
+
+    def swap_in(self, seqs) -> np.ndarray:
+        """Move a swapped-out group back; returns (host id, device id) rows."""
+        return self._move(self._L.pa_bm_swap_in, seqs)
+
+    def is_swapped(self, seq: int) -> bool:
+        r = self._L.pa_bm_is_swapped(self._h, seq)
+        if r < 0:
+            raise BadState(PA_ERR_STATE, f"unknown sequence {seq}")
+        return bool(r)
+
+    def host_refcount(self, hblk: int) -> int:
+        return self._L.pa_bm_host_refcount(self._h, hblk)
+
+    def host_free_list(self) -> List[int]:
+        n = self._L.pa_bm_host_free_list(self._h, None, 0)
+        out = np.empty(max(n, 1), dtype=np.int32)
+        self._L.pa_bm_host_free_list(self._h, out.ctypes.data, n)
+        return out[:n].tolist()
+
+    def raw_table(self, seq: int) -> List[int]:
+        """The table as stored: device ids, or host ids while swapped out."""
+        n = self._L.pa_bm_seq_table(self._h, seq, None, 0)
+        if n < 0:
+            raise BadState(PA_ERR_STATE, f"unknown sequence {seq}")
+        out = np.empty(max(n, 1), dtype=np.int32)
+        self._L.pa_bm_seq_table(self._h, seq, out.ctypes.data, n)
         return out[:n].tolist()
 
     def seq_len(self, seq: int) -> int:

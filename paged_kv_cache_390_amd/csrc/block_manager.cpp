@@ -13,11 +13,17 @@
 //                   4.2 (fork shares blocks; writing into a shared block that
 //                   is not full copies it; a full one is never copied), 4.3
 //                   (count updates must be atomic)
+//   [lpnh-1824136]  lpnh.cn/news/1824136, 4.2 (KV blocks can be swapped out
+//                   to host memory, at a large latency cost)
 //
 // Design: the state is a vector of counts, a vector used as the free stack
 // and a hash map from sequence id to (table, length).  Every public call
 // validates first, then mutates, so a failing call changes nothing.  One
-// mutex serialises calls.
+// mutex serialises calls.  A second pool (host blocks, its own counts and
+// free stack) receives the blocks of swapped-out sequences; a group of
+// sequences is swapped together so that blocks shared by forks stay shared:
+// each distinct block, in order of first appearance, gets one block on the
+// other side whose count is the number of group members holding it.
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
@@ -33,8 +39,20 @@
 namespace {
 
 struct Seq {
-    std::vector<int32_t> table;
+    std::vector<int32_t> table;   // device ids, or host ids while swapped
     int64_t len = 0;
+    bool swapped = false;
+};
+
+struct Pool {
+    std::vector<int32_t> free_stack;   // allocation pops from the back
+    std::vector<int32_t> count;        // holders per block
+
+    void init(int32_t n) {
+        free_stack.resize(n);
+        for (int32_t i = 0; i < n; ++i) free_stack[i] = i;
+        count.assign(n, 0);
+    }
 };
 
 }  // namespace
@@ -45,6 +63,7 @@ struct pa_bm {
     std::vector<int32_t> free_stack;   // allocation pops from the back
     std::vector<int32_t> count;        // holders per block
     std::unordered_map<int64_t, Seq> seqs;
+    Pool host;                         // swap target
     std::mutex mu;
 
     int64_t blocks_for(int64_t n) const { return (n + block_size - 1) / block_size; }
@@ -87,13 +106,66 @@ struct pa_bm {
         *slot = slot_of(s, n);
         return rc;
     }
+
+    // Swap a group between the device pool and the host pool (out: device
+    // -> host).  Validates everything first; changes nothing on failure.
+    int move(const int64_t* ids, int32_t n, bool out, int64_t* pairs, int32_t cap, int32_t* npairs,
+             const char* what) {
+        std::vector<Seq*> group;
+        group.reserve(n);
+        std::unordered_set<int64_t> seen;
+        for (int32_t i = 0; i < n; ++i) {
+            auto it = seqs.find(ids[i]);
+            if (it == seqs.end())
+                return pa::fail(PA_ERR_STATE, "%s: unknown sequence %lld", what, (long long)ids[i]);
+            if (!seen.insert(ids[i]).second)
+                return pa::fail(PA_ERR_STATE, "%s: sequence %lld appears twice", what, (long long)ids[i]);
+            if (it->second.swapped == out)
+                return pa::fail(PA_ERR_STATE, "%s: sequence %lld is already %s", what, (long long)ids[i],
+                                out ? "swapped out" : "resident");
+            group.push_back(&it->second);
+        }
+        std::vector<int32_t>& src_count = out ? count : host.count;
+        std::vector<int32_t>& src_free = out ? free_stack : host.free_stack;
+        std::vector<int32_t>& dst_count = out ? host.count : count;
+        std::vector<int32_t>& dst_free = out ? host.free_stack : free_stack;
+        std::vector<int32_t> order;
+        std::unordered_map<int32_t, int32_t> holders;
+        for (Seq* q : group)
+            for (int32_t b : q->table)
+                if (holders[b]++ == 0) order.push_back(b);
+        if (order.size() > dst_free.size())
+            return pa::fail(PA_ERR_OOM, "%s: %zu blocks needed, %zu free", what, order.size(), dst_free.size());
+        if ((int64_t)order.size() > cap)
+            return pa::fail(PA_ERR_INVALID, "%s: %zu pairs, room for %d", what, order.size(), cap);
+        std::unordered_map<int32_t, int32_t> moved;
+        for (size_t i = 0; i < order.size(); ++i) {
+            const int32_t b = order[i];
+            const int32_t d = dst_free.back();
+            dst_free.pop_back();
+            dst_count[d] = holders[b];
+            moved[b] = d;
+            pairs[2 * i] = b;
+            pairs[2 * i + 1] = d;
+            src_count[b] -= holders[b];
+            if (src_count[b] == 0) src_free.push_back(b);
+        }
+        for (Seq* q : group) {
+            for (int32_t& b : q->table) b = moved[b];
+            q->swapped = out;
+        }
+        *npairs = (int32_t)order.size();
+        return PA_OK;
+    }
 };
 
 extern "C" {
 
-pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size) {
-    if (num_blocks < 0 || block_size <= 0) {
-        pa::set_error("pa_bm_create: num_blocks >= 0 and block_size > 0 required");
+pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size) { return pa_bm_create_with_host(num_blocks, block_size, 0); }
+
+pa_bm* pa_bm_create_with_host(int32_t num_blocks, int32_t block_size, int32_t num_host_blocks) {
+    if (num_blocks < 0 || block_size <= 0 || num_host_blocks < 0) {
+        pa::set_error("pa_bm_create: num_blocks >= 0, num_host_blocks >= 0 and block_size > 0 required");
         return nullptr;
     }
     pa_bm* bm = new (std::nothrow) pa_bm();
@@ -107,6 +179,7 @@ pa_bm* pa_bm_create(int32_t num_blocks, int32_t block_size) {
         bm->free_stack.resize(num_blocks);
         for (int32_t i = 0; i < num_blocks; ++i) bm->free_stack[i] = i;
         bm->count.assign(num_blocks, 0);
+        bm->host.init(num_host_blocks);
     } catch (...) {
         delete bm;
         pa::set_error("pa_bm_create: out of host memory");
@@ -164,6 +237,7 @@ int pa_bm_fork(pa_bm* bm, int64_t parent, int64_t child) {
     std::lock_guard<std::mutex> g(bm->mu);
     auto it = bm->seqs.find(parent);
     if (it == bm->seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_fork: unknown parent %lld", (long long)parent);
+    if (it->second.swapped) return pa::fail(PA_ERR_STATE, "pa_bm_fork: parent %lld is swapped out", (long long)parent);
     if (bm->seqs.count(child)) return pa::fail(PA_ERR_STATE, "pa_bm_fork: sequence %lld exists", (long long)child);
     Seq c = it->second;
     for (int32_t b : c.table) bm->count[b] += 1;
@@ -176,6 +250,7 @@ int pa_bm_append_token(pa_bm* bm, int64_t seq, int64_t* slot_out, int64_t* cow_s
     std::lock_guard<std::mutex> g(bm->mu);
     auto it = bm->seqs.find(seq);
     if (it == bm->seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_append_token: unknown sequence %lld", (long long)seq);
+    if (it->second.swapped) return pa::fail(PA_ERR_STATE, "pa_bm_append_token: sequence %lld is swapped out", (long long)seq);
     int64_t slot, src, dst;
     const int rc = bm->append(it->second, &slot, &src, &dst);
     if (rc == PA_ERR_OOM) return pa::fail(PA_ERR_OOM, "pa_bm_append_token: no free block");
@@ -197,6 +272,8 @@ int pa_bm_append_tokens(pa_bm* bm, const int64_t* seqs, int32_t n, int64_t* slot
         auto it = bm->seqs.find(seqs[i]);
         if (it == bm->seqs.end())
             return pa::fail(PA_ERR_STATE, "pa_bm_append_tokens: unknown sequence %lld", (long long)seqs[i]);
+        if (it->second.swapped)
+            return pa::fail(PA_ERR_STATE, "pa_bm_append_tokens: sequence %lld is swapped out", (long long)seqs[i]);
         int64_t src, dst;
         const int rc = bm->append(it->second, &slots_out[i], &src, &dst);
         if (rc == PA_ERR_OOM) return pa::fail(PA_ERR_OOM, "pa_bm_append_tokens: no free block at entry %d", i);
@@ -216,12 +293,55 @@ int pa_bm_free_sequence(pa_bm* bm, int64_t seq) {
     std::lock_guard<std::mutex> g(bm->mu);
     auto it = bm->seqs.find(seq);
     if (it == bm->seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_free_sequence: unknown sequence %lld", (long long)seq);
+    std::vector<int32_t>& count = it->second.swapped ? bm->host.count : bm->count;
+    std::vector<int32_t>& free_stack = it->second.swapped ? bm->host.free_stack : bm->free_stack;
     for (int32_t b : it->second.table) {
-        bm->count[b] -= 1;
-        if (bm->count[b] == 0) bm->free_stack.push_back(b);
+        count[b] -= 1;
+        if (count[b] == 0) free_stack.push_back(b);
     }
     bm->seqs.erase(it);
     return PA_OK;
+}
+
+int pa_bm_swap_out(pa_bm* bm, const int64_t* seqs, int32_t n, int64_t* pairs_out, int32_t cap,
+                   int32_t* num_pairs_out) {
+    if (num_pairs_out) *num_pairs_out = 0;
+    if (!bm || n < 0 || cap < 0 || (n > 0 && !seqs) || (cap > 0 && !pairs_out) || !num_pairs_out)
+        return pa::fail(PA_ERR_INVALID, "pa_bm_swap_out: bad argument");
+    std::lock_guard<std::mutex> g(bm->mu);
+    return bm->move(seqs, n, true, pairs_out, cap, num_pairs_out, "pa_bm_swap_out");
+}
+
+int pa_bm_swap_in(pa_bm* bm, const int64_t* seqs, int32_t n, int64_t* pairs_out, int32_t cap,
+                  int32_t* num_pairs_out) {
+    if (num_pairs_out) *num_pairs_out = 0;
+    if (!bm || n < 0 || cap < 0 || (n > 0 && !seqs) || (cap > 0 && !pairs_out) || !num_pairs_out)
+        return pa::fail(PA_ERR_INVALID, "pa_bm_swap_in: bad argument");
+    std::lock_guard<std::mutex> g(bm->mu);
+    return bm->move(seqs, n, false, pairs_out, cap, num_pairs_out, "pa_bm_swap_in");
+}
+
+int32_t pa_bm_is_swapped(pa_bm* bm, int64_t seq) {
+    if (!bm) return -1;
+    std::lock_guard<std::mutex> g(bm->mu);
+    auto it = bm->seqs.find(seq);
+    return it == bm->seqs.end() ? -1 : (it->second.swapped ? 1 : 0);
+}
+
+int32_t pa_bm_host_refcount(pa_bm* bm, int32_t hblk) {
+    if (!bm) return -1;
+    std::lock_guard<std::mutex> g(bm->mu);
+    if (hblk < 0 || hblk >= (int32_t)bm->host.count.size()) return -1;
+    return bm->host.count[hblk];
+}
+
+int32_t pa_bm_host_free_list(pa_bm* bm, int32_t* out, int32_t cap) {
+    if (!bm) return -1;
+    std::lock_guard<std::mutex> g(bm->mu);
+    const int32_t n = (int32_t)bm->host.free_stack.size();
+    const int32_t k = std::min(n, std::max(cap, 0));
+    if (out && k) std::memcpy(out, bm->host.free_stack.data(), (size_t)k * sizeof(int32_t));
+    return n;
 }
 
 int pa_bm_get_tables(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* tables_out,
@@ -232,6 +352,8 @@ int pa_bm_get_tables(pa_bm* bm, const int64_t* seqs, int32_t n, int32_t* tables_
     for (int32_t i = 0; i < n; ++i) {
         auto it = bm->seqs.find(seqs[i]);
         if (it == bm->seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_get_tables: unknown sequence %lld", (long long)seqs[i]);
+        if (it->second.swapped)
+            return pa::fail(PA_ERR_STATE, "pa_bm_get_tables: sequence %lld is swapped out", (long long)seqs[i]);
         if ((int64_t)it->second.table.size() > max_blocks)
             return pa::fail(PA_ERR_INVALID, "pa_bm_get_tables: table of %lld has %zu blocks > %d",
                             (long long)seqs[i], it->second.table.size(), max_blocks);
@@ -253,6 +375,7 @@ int pa_bm_get_slots(pa_bm* bm, int64_t seq, int32_t pos_begin, int32_t count, in
     std::lock_guard<std::mutex> g(bm->mu);
     auto it = bm->seqs.find(seq);
     if (it == bm->seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_get_slots: unknown sequence %lld", (long long)seq);
+    if (it->second.swapped) return pa::fail(PA_ERR_STATE, "pa_bm_get_slots: sequence %lld is swapped out", (long long)seq);
     const Seq& s = it->second;
     if ((int64_t)pos_begin + count > (int64_t)s.table.size() * bm->block_size)
         return pa::fail(PA_ERR_INVALID, "pa_bm_get_slots: positions beyond the table");
@@ -287,6 +410,17 @@ int32_t pa_bm_seq_len(pa_bm* bm, int64_t seq) {
     std::lock_guard<std::mutex> g(bm->mu);
     auto it = bm->seqs.find(seq);
     return it == bm->seqs.end() ? -1 : (int32_t)it->second.len;
+}
+
+int32_t pa_bm_seq_table(pa_bm* bm, int64_t seq, int32_t* out, int32_t cap) {
+    if (!bm) return -1;
+    std::lock_guard<std::mutex> g(bm->mu);
+    auto it = bm->seqs.find(seq);
+    if (it == bm->seqs.end()) return -1;
+    const int32_t n = (int32_t)it->second.table.size();
+    const int32_t k = std::min(n, std::max(cap, 0));
+    if (out && k) std::memcpy(out, it->second.table.data(), (size_t)k * sizeof(int32_t));
+    return n;
 }
 
 int32_t pa_bm_seq_blocks(pa_bm* bm, int64_t seq) {

@@ -5,15 +5,23 @@
 // LDS or MFMA; they are bound by launch latency at decode batch sizes
 // (reshape) or by HBM bandwidth (block copy).
 //
+// A third operation moves whole blocks between a device cache and a pinned
+// host cache (swap out / in) with the same copy loop: the kernel reads or
+// writes the host side through its device mapping over PCIe, one launch for
+// every block and layer of a group.
+//
 // Sources (pages named by address, sections as they number them):
 //   [lpnh-1824136]  lpnh.cn/news/1824136, 3.1: results are scattered back
 //                   into the proper blocks
 //   [lpnh-2758356]  lpnh.cn/news/2758356, 2.2 (slot = block id * block size
 //                   + row), 4.2 third step (copy the whole shared block into
 //                   the new one), 4.3 (that copy costs bandwidth)
+//   [lpnh-1824136]  lpnh.cn/news/1824136, 4.2: KV blocks can be swapped out
+//                   to host memory, at a large latency cost
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <vector>
 
 #include "pa.h"
 #include "pa_internal.h"
@@ -53,25 +61,26 @@ scatter_kv_kernel(const uint16_t* __restrict__ key, const uint16_t* __restrict__
     }
 }
 
-constexpr int kMaxLayersPerLaunch = 64;
+constexpr int kMaxCachesPerLaunch = 128;   // cache tensors (K or V of one layer) per launch
 constexpr int kCopyUnroll = 4;
 
-struct LayerPtrs {
-    void* k[kMaxLayersPerLaunch];
-    void* v[kMaxLayersPerLaunch];
+// Source and destination tensor of each cache in one launch: the same
+// tensor for copy-on-write copies, a device and a host tensor for swaps.
+struct CachePtrs {
+    const void* src[kMaxCachesPerLaunch];
+    void* dst[kMaxCachesPerLaunch];
 };
 
-// grid: x = chunk of the block, y = pair, z = 2 * layer + (0: K, 1: V)
+// grid: x = chunk of the block, y = pair, z = cache; pairs[i] = (src id, dst id)
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
-copy_blocks_kernel(LayerPtrs layers, const int64_t* __restrict__ pairs, int64_t num_blocks,
-                   int64_t units_per_block) {
+block_copy_kernel(CachePtrs caches, const int64_t* __restrict__ pairs, int64_t src_blocks, int64_t dst_blocks,
+                  int64_t units_per_block) {
     const int64_t src = pairs[2 * (int64_t)blockIdx.y];
     const int64_t dst = pairs[2 * (int64_t)blockIdx.y + 1];
-    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-    T* base = static_cast<T*>((blockIdx.z & 1) ? layers.v[blockIdx.z >> 1] : layers.k[blockIdx.z >> 1]);
-    const T* s = base + src * units_per_block;
-    T* d = base + dst * units_per_block;
+    if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+    const T* s = static_cast<const T*>(caches.src[blockIdx.z]) + src * units_per_block;
+    T* d = static_cast<T*>(caches.dst[blockIdx.z]) + dst * units_per_block;
     const int64_t first = (int64_t)blockIdx.x * (kThreads * kCopyUnroll) + threadIdx.x;
     T tmp[kCopyUnroll];
 #pragma unroll
@@ -86,9 +95,58 @@ copy_blocks_kernel(LayerPtrs layers, const int64_t* __restrict__ pairs, int64_t 
     }
 }
 
+// Enqueue block copies for caches [0, n): src[i] -> dst[i] per pair.
+int launch_block_copies(const std::vector<const void*>& src, const std::vector<void*>& dst,
+                        const int64_t* pairs, int32_t num_pairs, int64_t src_blocks, int64_t dst_blocks,
+                        int64_t block_elems, bool vec, hipStream_t st, const char* what) {
+    const int64_t units = vec ? block_elems / 8 : block_elems;
+    const int64_t chunks = (units + kThreads * kCopyUnroll - 1) / (kThreads * kCopyUnroll);
+    if (chunks > 0x7fffffff) return pa::fail(PA_ERR_INVALID, "%s: block too large", what);
+    const int32_t n = (int32_t)src.size();
+    for (int32_t c0 = 0; c0 < n; c0 += kMaxCachesPerLaunch) {
+        const int32_t nc = n - c0 < kMaxCachesPerLaunch ? n - c0 : kMaxCachesPerLaunch;
+        CachePtrs cp{};
+        for (int32_t i = 0; i < nc; ++i) {
+            cp.src[i] = src[c0 + i];
+            cp.dst[i] = dst[c0 + i];
+        }
+        const dim3 grid((unsigned)chunks, (unsigned)num_pairs, (unsigned)nc);
+        if (vec)
+            hipLaunchKernelGGL(block_copy_kernel<uint4>, grid, dim3(kThreads), 0, st, cp, pairs, src_blocks,
+                               dst_blocks, units);
+        else
+            hipLaunchKernelGGL(block_copy_kernel<uint16_t>, grid, dim3(kThreads), 0, st, cp, pairs, src_blocks,
+                               dst_blocks, units);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    }
+    return PA_OK;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool supported_head_dim(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128 || d == 256; }
+
+// Device address of pinned host memory (hipHostMalloc / torch pin_memory),
+// or null if `p` is not pinned, mapped host memory.
+void* host_device_address(void* p) {
+    hipPointerAttribute_t a{};
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (a.type != hipMemoryTypeHost || !a.devicePointer || !a.hostPointer) return nullptr;
+    return static_cast<char*>(a.devicePointer) + (static_cast<char*>(p) - static_cast<char*>(a.hostPointer));
+}
+
+bool is_device_memory(const void* p) {
+    hipPointerAttribute_t a{};
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return a.type == hipMemoryTypeDevice;
+}
 
 }  // namespace
 
@@ -142,30 +200,50 @@ extern "C" int pa_copy_blocks(void* const* k_caches, void* const* v_caches, int3
     if (!k_caches || !v_caches || !src_dst_pairs) return pa::fail(PA_ERR_INVALID, "pa_copy_blocks: null pointer");
     if (num_pairs > 65535) return pa::fail(PA_ERR_INVALID, "pa_copy_blocks: more than 65535 pairs in one call");
     bool vec = block_elems % 8 == 0;
+    std::vector<const void*> src;
+    std::vector<void*> dst;
     for (int32_t l = 0; l < num_layers; ++l) {
         if (!k_caches[l] || !v_caches[l]) return pa::fail(PA_ERR_INVALID, "pa_copy_blocks: null cache of layer %d", l);
         vec = vec && aligned16(k_caches[l]) && aligned16(v_caches[l]);
+        src.push_back(k_caches[l]);
+        dst.push_back(k_caches[l]);
+        src.push_back(v_caches[l]);
+        dst.push_back(v_caches[l]);
     }
-    auto st = static_cast<hipStream_t>(stream);
-    const int64_t units = vec ? block_elems / 8 : block_elems;
-    const int64_t chunks = (units + kThreads * kCopyUnroll - 1) / (kThreads * kCopyUnroll);
-    if (chunks > 0x7fffffff) return pa::fail(PA_ERR_INVALID, "pa_copy_blocks: block too large");
-    for (int32_t l0 = 0; l0 < num_layers; l0 += kMaxLayersPerLaunch) {
-        const int32_t nl = num_layers - l0 < kMaxLayersPerLaunch ? num_layers - l0 : kMaxLayersPerLaunch;
-        LayerPtrs lp{};
-        for (int32_t i = 0; i < nl; ++i) {
-            lp.k[i] = k_caches[l0 + i];
-            lp.v[i] = v_caches[l0 + i];
-        }
-        const dim3 grid((unsigned)chunks, (unsigned)num_pairs, (unsigned)(2 * nl));
-        if (vec)
-            hipLaunchKernelGGL(copy_blocks_kernel<uint4>, grid, dim3(kThreads), 0, st, lp, src_dst_pairs,
-                               (int64_t)num_blocks, units);
-        else
-            hipLaunchKernelGGL(copy_blocks_kernel<uint16_t>, grid, dim3(kThreads), 0, st, lp, src_dst_pairs,
-                               (int64_t)num_blocks, units);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "pa_copy_blocks: %s", hipGetErrorString(e));
+    return launch_block_copies(src, dst, src_dst_pairs, num_pairs, num_blocks, num_blocks, block_elems, vec,
+                               static_cast<hipStream_t>(stream), "pa_copy_blocks");
+}
+
+extern "C" int pa_swap_blocks(void* const* dev_caches, void* const* host_caches, int32_t num_caches,
+                              const int64_t* pairs, int32_t num_pairs, int32_t dev_num_blocks,
+                              int32_t host_num_blocks, int64_t block_elems, int32_t direction, int32_t dtype,
+                              void* stream) {
+    if (dtype != PA_DTYPE_F16) return pa::fail(PA_ERR_UNSUPPORTED, "pa_swap_blocks: dtype %d", dtype);
+    if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN)
+        return pa::fail(PA_ERR_INVALID, "pa_swap_blocks: direction %d", direction);
+    if (num_caches < 0 || num_pairs < 0 || dev_num_blocks < 0 || host_num_blocks < 0 || block_elems <= 0)
+        return pa::fail(PA_ERR_INVALID, "pa_swap_blocks: bad sizes");
+    if (num_pairs == 0 || num_caches == 0) return PA_OK;
+    if (!dev_caches || !host_caches || !pairs) return pa::fail(PA_ERR_INVALID, "pa_swap_blocks: null pointer");
+    if (num_pairs > 65535) return pa::fail(PA_ERR_INVALID, "pa_swap_blocks: more than 65535 pairs in one call");
+    if (!is_device_memory(pairs)) return pa::fail(PA_ERR_INVALID, "pa_swap_blocks: pairs must be device memory");
+    // resolve every pointer before anything is enqueued
+    bool vec = block_elems % 8 == 0;
+    std::vector<const void*> src;
+    std::vector<void*> dst;
+    for (int32_t i = 0; i < num_caches; ++i) {
+        if (!dev_caches[i] || !host_caches[i])
+            return pa::fail(PA_ERR_INVALID, "pa_swap_blocks: null cache pointer %d", i);
+        if (!is_device_memory(dev_caches[i]))
+            return pa::fail(PA_ERR_INVALID, "pa_swap_blocks: cache %d on the device side is not device memory", i);
+        void* h = host_device_address(host_caches[i]);
+        if (!h) return pa::fail(PA_ERR_INVALID, "pa_swap_blocks: host cache %d is not pinned, mapped host memory", i);
+        vec = vec && aligned16(dev_caches[i]) && aligned16(h);
+        src.push_back(direction == PA_SWAP_OUT ? dev_caches[i] : h);
+        dst.push_back(direction == PA_SWAP_OUT ? h : dev_caches[i]);
     }
-    return PA_OK;
+    const int64_t src_nb = direction == PA_SWAP_OUT ? dev_num_blocks : host_num_blocks;
+    const int64_t dst_nb = direction == PA_SWAP_OUT ? host_num_blocks : dev_num_blocks;
+    return launch_block_copies(src, dst, pairs, num_pairs, src_nb, dst_nb, block_elems, vec,
+                               static_cast<hipStream_t>(stream), "pa_swap_blocks");
 }

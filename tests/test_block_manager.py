@@ -14,8 +14,12 @@ def _same_state(bm, m):
     assert bm.free_list() == m.free
     for b in range(m.num_blocks):
         assert bm.refcount(b) == m.refcount[b]
+    assert bm.host_free_list() == m.host_free
+    for b in range(m.num_host_blocks):
+        assert bm.host_refcount(b) == m.host_refcount[b]
     for seq, st in m.seqs.items():
-        assert bm.table(seq) == st.table
+        assert bm.raw_table(seq) == st.table
+        assert bm.is_swapped(seq) == st.swapped
         assert bm.seq_len(seq) == st.length
 
 
@@ -30,6 +34,10 @@ def _apply(bm, m, op):
             want = m.fork(op[1], op[2])
         elif kind == "append":
             want = m.append_token(op[1])
+        elif kind == "swap_out":
+            want = m.swap_out(op[1])
+        elif kind == "swap_in":
+            want = m.swap_in(op[1])
         else:
             want = m.free_sequence(op[1])
     except (OOM, StateError) as e:
@@ -41,6 +49,10 @@ def _apply(bm, m, op):
             got = bm.fork(op[1], op[2])
         elif kind == "append":
             got = bm.append_token(op[1])
+        elif kind == "swap_out":
+            got = [tuple(p) for p in bm.swap_out(op[1]).tolist()]
+        elif kind == "swap_in":
+            got = [tuple(p) for p in bm.swap_in(op[1]).tolist()]
         else:
             got = bm.free_sequence(op[1])
     except pa.OutOfBlocks:
@@ -61,6 +73,19 @@ def test_random_streams_match_the_model(seed, nb, B):
     for op in workloads.block_manager_ops(seed * 31 + nb, 300, max_prompt=3 * B):
         _apply(bm, m, op)
         _same_state(bm, m)
+
+
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("nb,nh,B", [(12, 6, 4), (7, 20, 1), (20, 9, 16)])
+def test_random_streams_with_swaps_match_the_model(seed, nb, nh, B):
+    """Group swaps to and from a host pool interleaved with everything else;
+    both pools compared after every step."""
+    bm = pa.BlockManager(nb, B, nh)
+    m = BlockManagerModel(nb, B, nh)
+    for op in workloads.block_manager_ops(seed * 17 + nb, 300, max_prompt=3 * B, swap=True):
+        _apply(bm, m, op)
+        _same_state(bm, m)
+        m.check_invariants()
 
 
 def test_page_figure_through_the_product(load_golden):

@@ -96,3 +96,29 @@ def test_copy_then_write_matches_cow_semantics():
     assert np.array_equal(kc[cow[0]].view(np.uint16), parent_tail.view(np.uint16))
     assert np.array_equal(kc[cow[1], :, :2].view(np.uint16), parent_tail[:, :2].view(np.uint16))
     assert np.array_equal(kc[cow[1], :, 2].view(np.uint16), new[0].view(np.uint16))
+
+
+def test_move_blocks_matches_elementwise_copy_and_round_trips():
+    """The swap data movement: every element of a destination block equals
+    the source block's element (checked one element at a time), untouched
+    blocks keep their bytes, and out-then-in restores the blocks."""
+    rng = np.random.default_rng(5)
+    dev = [rng.standard_normal((6, 2, 4, 8)).astype(np.float16) for _ in range(3)]
+    host = [np.full((5, 2, 4, 8), np.nan, dtype=np.float16) for _ in range(3)]
+    pairs = np.array([[4, 0], [1, 3], [5, 2]], dtype=np.int64)
+    before_host = [h.copy() for h in host]
+    oracle.move_blocks(host, dev, pairs)
+    for i in range(3):
+        for s, d in pairs.tolist():
+            for idx in np.ndindex(dev[i].shape[1:]):
+                assert host[i][(d,) + idx].view(np.uint16) == dev[i][(s,) + idx].view(np.uint16)
+        untouched = [b for b in range(5) if b not in pairs[:, 1]]
+        assert np.array_equal(host[i][untouched].view(np.uint16), before_host[i][untouched].view(np.uint16))
+    back = [np.zeros_like(d) for d in dev]
+    oracle.move_blocks(back, host, pairs[:, ::-1].copy())
+    for i in range(3):
+        assert np.array_equal(back[i][pairs[:, 0]].view(np.uint16), dev[i][pairs[:, 0]].view(np.uint16))
+    with pytest.raises(ValueError):
+        oracle.move_blocks(host, dev, np.array([[0, 1], [2, 1]], dtype=np.int64))
+    with pytest.raises(ValueError):
+        oracle.move_blocks(host, dev, np.array([[6, 1]], dtype=np.int64))

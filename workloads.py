@@ -257,14 +257,26 @@ def parallel_sampling(seed: int = 0, num_blocks: int = 1024, block_size: int = 1
 # Random operation streams for the block manager (differential testing)
 # ---------------------------------------------------------------------------
 def block_manager_ops(seed: int, n_ops: int, max_seqs: int = 6,
-                      max_prompt: int = 40) -> List[tuple]:
+                      max_prompt: int = 40, swap: bool = False) -> List[tuple]:
     """A stream of ('add', seq, n) / ('fork', parent, child) / ('append', seq)
-    / ('free', seq) operations.  Ids may be stale or unknown on purpose, so
-    error paths are exercised too."""
+    / ('free', seq) operations, plus ('swap_out', [seqs]) / ('swap_in',
+    [seqs]) groups when swap is set.  Ids may be stale or unknown on purpose,
+    so error paths are exercised too."""
     rng = _rng(seed, 6)
     ops = []
     next_id = 0
+    swapped_groups: List[List[int]] = []      # groups sent out, to bring back later
     for _ in range(n_ops):
+        if swap and rng.random() < 0.15:
+            if swapped_groups and rng.random() < 0.5:
+                group = swapped_groups.pop(int(rng.integers(0, len(swapped_groups))))
+                ops.append(("swap_in", group))
+            else:
+                k = int(rng.integers(1, 4))
+                group = sorted({int(x) for x in rng.integers(max(next_id - 6, 0), max(next_id, 1), size=k)})
+                ops.append(("swap_out", group))
+                swapped_groups.append(group)
+            continue
         r = rng.random()
         if r < 0.15:
             ops.append(("add", next_id, int(rng.integers(0, max_prompt + 1))))
