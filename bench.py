@@ -47,10 +47,11 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="llama7b", choices=["llama7b", "gqa", "long", "copy", "swap"],
+    p.add_argument("--workload", default="llama7b", choices=["llama7b", "gqa", "long", "copy", "swap", "prefix"],
                    help="llama7b: the Llama-2-7B decode batch (default); gqa: 64 query heads over 8 KV "
                         "heads (matrix-core kernel); long: 16 x 4096 tokens; copy: block-copy calibration; "
-                        "swap: block swaps between HBM and pinned host memory")
+                        "swap: block swaps between HBM and pinned host memory; prefix: 100 requests "
+                        "sharing a 1000-token system prompt")
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--batch", type=int, default=0, help="sequences (0: 64 for llama7b, 256 for gqa)")
     p.add_argument("--block-size", type=int, default=16)
@@ -113,6 +114,8 @@ def main():
         return copy_bench(args, dev)
     if args.workload == "swap":
         return swap_bench(args, dev)
+    if args.workload == "prefix":
+        return prefix_bench(args, dev)
 
     L = args.layers
     B = args.block_size
@@ -363,6 +366,78 @@ def swap_bench(args, dev):
         "bytes_per_direction": moved, "pcie_peak_GB_s": 64.0,
         "config": {"workload": "swap", "sequences": S, "tokens": n, "layers": L, "num_kv_heads": Hkv,
                    "block_size": B, "head_dim": D}}), flush=True)
+
+
+def prefix_bench(args, dev):
+    """100 requests whose prompts start with one 1000-token system prompt
+    (the n1n.ai page's example), each followed by its own 1..200 tokens,
+    Llama-2-7B heads, B = 16, --layers layers resident.  The product block
+    manager shares the prompt's 62 full blocks (one copy, count 100); one
+    decode step per layer is timed with HIP events.  Reported: logical KV
+    GB/s (what the kernel attends over, the shared blocks counted once per
+    request) next to the unique bytes in HBM per step, and the host time of
+    the cached prompt admissions."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_390_amd as pa
+
+    L = args.layers
+    R, P, Hkv, H, B, D = 100, 1000, 32, 32, 16, 128
+    rng = np.random.default_rng(args.seed)
+    system = rng.integers(0, 32000, size=P).tolist()
+    suffix = rng.integers(1, 201, size=R).tolist()
+    toks = [system + rng.integers(0, 32000, size=s).tolist() for s in suffix]
+    NB = P // B + sum(-(-(P + s) // B) - P // B for s in suffix) + 64
+    bm = pa.BlockManager(NB, B)
+    t0 = time.perf_counter()
+    cached = [bm.add_sequence_cached(r, toks[r])[1] for r in range(R)]
+    admit_us = (time.perf_counter() - t0) / R * 1e6
+    used = NB - bm.num_free()
+    width = -(-max(len(t) for t in toks) // B)
+    tables, lens = bm.get_tables(range(R), width)
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    kcs = [torch.randn((NB, Hkv, B, D), generator=g, device=dev, dtype=torch.float16) for _ in range(L)]
+    vcs = [torch.randn((NB, Hkv, B, D), generator=g, device=dev, dtype=torch.float16) for _ in range(L)]
+    q = torch.randn((R, H, D), generator=g, device=dev, dtype=torch.float16)
+    d_tables, d_lens = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
+    out = torch.empty_like(q)
+    ws = torch.zeros(max(1, pa.pa_decode_workspace_size(R, H, Hkv, D, B, width * B, 0)), dtype=torch.uint8,
+                     device=dev)
+
+    def call(l):
+        pa.pa_decode(out, q, kcs[l], vcs[l], d_tables, d_lens, 1 / np.sqrt(D), B, max_context_len=width * B,
+                     workspace=ws)
+
+    for _ in range(args.warmup):
+        for l in range(L):
+            call(l)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps * L)]
+    for i in range(args.steps):
+        for l in range(L):
+            a, b = ev[i * L + l]
+            a.record()
+            call(l)
+            b.record()
+    torch.cuda.synchronize()
+    us = np.mean([a.elapsed_time(b) for a, b in ev]) * 1e3
+    kv_tok = 2 * Hkv * D * 2
+    logical = int(lens.astype(np.int64).sum()) * kv_tok
+    unique = used * B * kv_tok
+    log(f"[bench] prefix: {R} requests, {used} blocks in use ({sum(-(-len(t) // B) for t in toks)} unshared), "
+        f"admission {admit_us:.1f} us/request on the host; decode {us:.1f} us/layer = {logical / us / 1e3:.0f} GB/s "
+        f"logical, {unique / us / 1e3:.0f} GB/s of unique blocks")
+    print(json.dumps({"metric": "prefix-shared decode: logical KV GB/s", "value": round(logical / us / 1e3, 2),
+                      "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "higher_is_better": True, "us_per_layer": round(us, 2),
+                      "unique_GB_s": round(unique / us / 1e3, 2), "blocks_in_use": used,
+                      "blocks_unshared": sum(-(-len(t) // B) for t in toks),
+                      "cached_tokens": int(sum(cached)), "admission_us_per_request": round(admit_us, 2),
+                      "config": {"workload": "prefix", "requests": R, "system_prompt": P,
+                                 "own_tokens": "U[1,200]", "num_heads": H, "num_kv_heads": Hkv,
+                                 "head_dim": D, "block_size": B, "layers_resident": L}}), flush=True)
 
 
 if __name__ == "__main__":

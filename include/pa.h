@@ -243,6 +243,25 @@ void pa_bm_destroy(pa_bm *bm);
 int pa_bm_add_sequence(pa_bm *bm, int64_t seq, int32_t n_tokens,
                        int64_t *slots_out);
 
+/* New sequence given its prompt's token ids (host int32 [n_tokens]),
+ * sharing the blocks of a common prefix with sequences already there
+ * ([n1n] 前缀缓存: requests with one long system prompt share its physical
+ * blocks; [lpnh-1824136] 3.2, second step).  Every full block of a prompt
+ * added this way is indexed by (the id of the block before it, or -1; its
+ * B token ids); a new prompt takes each leading full block whose key it
+ * finds (count + 1) and allocates the rest.  A partial last block is never
+ * shared this way.  An indexed block leaves the index when its count
+ * reaches 0.  slots_out (may be NULL) receives all n_tokens slots;
+ * *num_cached_out the number of leading positions whose K/V are already in
+ * shared blocks -- the caller computes and writes only the rest.
+ * PA_ERR_STATE if seq exists, PA_ERR_OOM (state unchanged) if short of
+ * blocks. */
+int pa_bm_add_sequence_cached(pa_bm *bm, int64_t seq, const int32_t *token_ids,
+                              int32_t n_tokens, int64_t *slots_out,
+                              int32_t *num_cached_out);
+/* Number of full blocks currently in the prefix index. */
+int32_t pa_bm_num_cached_blocks(pa_bm *bm);
+
 /* New sequence with an explicit table: nblk == ceil(n_tokens / B) distinct
  * ids, each currently free; they leave the free list (the rest keep their
  * order) with a count of 1. */

@@ -32,6 +32,11 @@ Rules modelled:
   * Slot of logical position p: table[p // B] * B + p % B ([5688vip]
     分页机制 figure; [lpnh-2758356] 2.2).
 
+  * Requests whose prompts start with the same tokens (the page's example:
+    100 requests with one long system prompt) share the physical blocks of
+    that common prefix; copying happens only where their tokens diverge
+    ([n1n] 前缀缓存; [lpnh-1824136] 3.2, second step: a prompt equal to a
+    running sequence's may share its blocks).
   * Under memory pressure a sequence's KV blocks can be moved to host memory
     and back ("swap": [lpnh-1824136] 4.2 names it as a supported, slow
     option for serving very long contexts when latency can be traded).
@@ -54,6 +59,14 @@ Readings where the pages leave a step open (also listed in the design doc):
     back to the device free list in the same order.  Swapping in is the
     mirror image.  A swapped-out sequence can only be swapped in or freed.
     A group short of free blocks on the receiving side changes nothing.
+  * Prefix sharing is decided per FULL block and exactly: a full block is
+    found again by (the id of the block before it in the sequence, or -1 for
+    the first block; the block's own token ids).  Since a block's KV depends
+    on every earlier token, chaining through the previous block's id makes
+    the key stand for the whole prefix without storing it.  Only full prompt
+    blocks of sequences added with their token ids are indexed; a partial
+    last block is never shared this way (its next token would have to copy
+    it), and a block leaves the index when its count drops to 0.
 """
 from __future__ import annotations
 
@@ -88,6 +101,16 @@ class BlockManagerModel:
         self.num_host_blocks = num_host_blocks
         self.host_free: List[int] = list(range(num_host_blocks))
         self.host_refcount: List[int] = [0] * num_host_blocks
+        self.prefix_index: Dict[tuple, int] = {}     # (previous block or -1, token ids) -> block
+        self.block_key: Dict[int, tuple] = {}
+
+    def _release(self, b: int) -> None:
+        """A device block whose count reached 0 goes back on the free list
+        and out of the prefix index."""
+        self.free.append(b)
+        key = self.block_key.pop(b, None)
+        if key is not None:
+            del self.prefix_index[key]
 
     def _resident(self, seq: int) -> _Seq:
         if seq not in self.seqs:
@@ -124,6 +147,39 @@ class BlockManagerModel:
         s.length = n_tokens
         self.seqs[seq] = s
         return [self.slot(seq, p) for p in range(n_tokens)]
+
+    def add_sequence_cached(self, seq: int, tokens: Sequence[int]) -> Tuple[List[int], int]:
+        """Add a sequence given its prompt's token ids, sharing every leading
+        full block whose prefix is already cached.  Returns (slots of all
+        positions, number of leading positions whose KV is already there)."""
+        if seq in self.seqs:
+            raise StateError(f"sequence {seq} exists")
+        tokens = [int(t) for t in tokens]
+        B = self.block_size
+        n = len(tokens)
+        hits: List[int] = []
+        parent = -1
+        for i in range(n // B):
+            b = self.prefix_index.get((parent, tuple(tokens[i * B:(i + 1) * B])))
+            if b is None:
+                break
+            hits.append(b)
+            parent = b
+        need = self.blocks_for(n) - len(hits)
+        if need > len(self.free):
+            raise OOM()
+        for b in hits:
+            self.refcount[b] += 1
+        s = _Seq(table=list(hits), length=n)
+        for i in range(len(hits), self.blocks_for(n)):
+            b = self._alloc()
+            s.table.append(b)
+            if (i + 1) * B <= n:                       # a full prompt block: index it
+                key = (s.table[i - 1] if i > 0 else -1, tuple(tokens[i * B:(i + 1) * B]))
+                self.prefix_index[key] = b
+                self.block_key[b] = key
+        self.seqs[seq] = s
+        return [self.slot(seq, p) for p in range(n)], len(hits) * B
 
     def set_table(self, seq: int, blocks: Sequence[int], n_tokens: int) -> None:
         """Give a new sequence an explicit table (ids must be free)."""
@@ -183,11 +239,15 @@ class BlockManagerModel:
         if seq not in self.seqs:
             raise StateError(f"unknown sequence {seq}")
         s = self.seqs.pop(seq)
-        count, free = (self.host_refcount, self.host_free) if s.swapped else (self.refcount, self.free)
         for b in s.table:
-            count[b] -= 1
-            if count[b] == 0:
-                free.append(b)
+            if s.swapped:
+                self.host_refcount[b] -= 1
+                if self.host_refcount[b] == 0:
+                    self.host_free.append(b)
+            else:
+                self.refcount[b] -= 1
+                if self.refcount[b] == 0:
+                    self._release(b)
 
     # -- swap to / from the host pool ---------------------------------------
     def _move(self, seqs: Sequence[int], out: bool) -> List[Tuple[int, int]]:
@@ -220,7 +280,10 @@ class BlockManagerModel:
             pairs.append((b, d))
             src_count[b] -= holders[b]
             if src_count[b] == 0:
-                src_free.append(b)
+                if out:
+                    self._release(b)
+                else:
+                    src_free.append(b)
         for q in seqs:
             s = self.seqs[q]
             s.table = [new_id[b] for b in s.table]
@@ -288,3 +351,8 @@ class BlockManagerModel:
                 raise AssertionError("a held block is on a free list")
             if len(free) + len(held) != n:
                 raise AssertionError("free + held != pool size")
+        for key, b in self.prefix_index.items():
+            if self.block_key.get(b) != key or self.refcount[b] == 0:
+                raise AssertionError(f"prefix index entry for block {b} is stale")
+        if len(self.block_key) != len(self.prefix_index):
+            raise AssertionError("prefix index and its reverse map differ")

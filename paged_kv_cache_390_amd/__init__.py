@@ -77,6 +77,8 @@ def lib() -> ctypes.CDLL:
         "pa_bm_host_refcount": ([P, i32], i32),
         "pa_bm_host_free_list": ([P, P, i32], i32),
         "pa_bm_seq_table": ([P, i64, P, i32], i32),
+        "pa_bm_add_sequence_cached": ([P, i64, P, i32, P, P], ctypes.c_int),
+        "pa_bm_num_cached_blocks": ([P], i32),
         "pa_bm_destroy": ([P], None),
         "pa_bm_add_sequence": ([P, i64, i32, P], ctypes.c_int),
         "pa_bm_set_table": ([P, i64, P, i32, i32], ctypes.c_int),
@@ -332,6 +334,21 @@ class BlockManager:
         _check(self._L.pa_bm_add_sequence(self._h, seq, n_tokens, slots.ctypes.data if n_tokens else None),
                "add_sequence")
         return slots
+
+    def add_sequence_cached(self, seq: int, token_ids) -> Tuple[np.ndarray, int]:
+        """New sequence from its prompt's token ids, sharing the blocks of a
+        cached common prefix; returns (slots of every position, number of
+        leading positions whose K/V are already cached)."""
+        t = _i32(token_ids)
+        slots = np.empty(max(t.size, 0), dtype=np.int64)
+        nc = ctypes.c_int32()
+        _check(self._L.pa_bm_add_sequence_cached(self._h, seq, t.ctypes.data if t.size else None, t.size,
+                                                 slots.ctypes.data if t.size else None, ctypes.byref(nc)),
+               "add_sequence_cached")
+        return slots, nc.value
+
+    def num_cached_blocks(self) -> int:
+        return self._L.pa_bm_num_cached_blocks(self._h)
 
     def set_table(self, seq: int, blocks, n_tokens: int) -> None:
         b = _i32(blocks)

@@ -24,6 +24,10 @@
 // sequences is swapped together so that blocks shared by forks stay shared:
 // each distinct block, in order of first appearance, gets one block on the
 // other side whose count is the number of group members holding it.
+// Prefix sharing across requests ([n1n] 前缀缓存; [lpnh-1824136] 3.2 second
+// step): full prompt blocks are indexed by (previous block id or -1, their
+// token ids) -- the previous block's id stands for the whole prefix before
+// it -- and a new prompt takes every leading full block it finds there.
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
@@ -42,6 +46,25 @@ struct Seq {
     std::vector<int32_t> table;   // device ids, or host ids while swapped
     int64_t len = 0;
     bool swapped = false;
+};
+
+// Index key of a full block: the block before it (-1 for the first) and
+// its token ids.  Exact: equality compares every token.
+struct PrefixKey {
+    int32_t prev;
+    std::vector<int32_t> toks;
+    bool operator==(const PrefixKey& o) const { return prev == o.prev && toks == o.toks; }
+};
+
+struct PrefixKeyHash {
+    size_t operator()(const PrefixKey& k) const {
+        uint64_t h = 1469598103934665603ull ^ (uint32_t)k.prev;   // FNV-1a over the ids
+        for (int32_t t : k.toks) {
+            h ^= (uint32_t)t;
+            h *= 1099511628211ull;
+        }
+        return (size_t)h;
+    }
 };
 
 struct Pool {
@@ -64,7 +87,20 @@ struct pa_bm {
     std::vector<int32_t> count;        // holders per block
     std::unordered_map<int64_t, Seq> seqs;
     Pool host;                         // swap target
+    std::unordered_map<PrefixKey, int32_t, PrefixKeyHash> prefix_index;
+    std::unordered_map<int32_t, PrefixKey> block_key;
     std::mutex mu;
+
+    // A device block whose count reached 0: back on the free stack and out
+    // of the prefix index.
+    void release(int32_t b) {
+        free_stack.push_back(b);
+        auto it = block_key.find(b);
+        if (it != block_key.end()) {
+            prefix_index.erase(it->second);
+            block_key.erase(it);
+        }
+    }
 
     int64_t blocks_for(int64_t n) const { return (n + block_size - 1) / block_size; }
 
@@ -148,7 +184,12 @@ struct pa_bm {
             pairs[2 * i] = b;
             pairs[2 * i + 1] = d;
             src_count[b] -= holders[b];
-            if (src_count[b] == 0) src_free.push_back(b);
+            if (src_count[b] == 0) {
+                if (out)
+                    release(b);
+                else
+                    src_free.push_back(b);
+            }
         }
         for (Seq* q : group) {
             for (int32_t& b : q->table) b = moved[b];
@@ -293,14 +334,68 @@ int pa_bm_free_sequence(pa_bm* bm, int64_t seq) {
     std::lock_guard<std::mutex> g(bm->mu);
     auto it = bm->seqs.find(seq);
     if (it == bm->seqs.end()) return pa::fail(PA_ERR_STATE, "pa_bm_free_sequence: unknown sequence %lld", (long long)seq);
-    std::vector<int32_t>& count = it->second.swapped ? bm->host.count : bm->count;
-    std::vector<int32_t>& free_stack = it->second.swapped ? bm->host.free_stack : bm->free_stack;
     for (int32_t b : it->second.table) {
-        count[b] -= 1;
-        if (count[b] == 0) free_stack.push_back(b);
+        if (it->second.swapped) {
+            if (--bm->host.count[b] == 0) bm->host.free_stack.push_back(b);
+        } else {
+            if (--bm->count[b] == 0) bm->release(b);
+        }
     }
     bm->seqs.erase(it);
     return PA_OK;
+}
+
+int pa_bm_add_sequence_cached(pa_bm* bm, int64_t seq, const int32_t* token_ids, int32_t n_tokens,
+                              int64_t* slots_out, int32_t* num_cached_out) {
+    if (num_cached_out) *num_cached_out = 0;
+    if (!bm || n_tokens < 0 || (n_tokens > 0 && !token_ids))
+        return pa::fail(PA_ERR_INVALID, "pa_bm_add_sequence_cached: bad argument");
+    std::lock_guard<std::mutex> g(bm->mu);
+    if (bm->seqs.count(seq))
+        return pa::fail(PA_ERR_STATE, "pa_bm_add_sequence_cached: sequence %lld exists", (long long)seq);
+    const int32_t B = bm->block_size;
+    const int64_t nfull = n_tokens / B;
+    std::vector<int32_t> hits;
+    PrefixKey key{-1, {}};
+    for (int64_t i = 0; i < nfull; ++i) {
+        key.toks.assign(token_ids + i * B, token_ids + (i + 1) * B);
+        auto f = bm->prefix_index.find(key);
+        if (f == bm->prefix_index.end()) break;
+        hits.push_back(f->second);
+        key.prev = f->second;
+    }
+    const int64_t total = bm->blocks_for(n_tokens);
+    const int64_t need = total - (int64_t)hits.size();
+    if (need > (int64_t)bm->free_stack.size())
+        return pa::fail(PA_ERR_OOM, "pa_bm_add_sequence_cached: need %lld blocks, %zu free", (long long)need,
+                        bm->free_stack.size());
+    Seq s;
+    s.table.reserve(total);
+    for (int32_t b : hits) {
+        bm->count[b] += 1;
+        s.table.push_back(b);
+    }
+    for (int64_t i = (int64_t)hits.size(); i < total; ++i) {
+        const int32_t b = bm->pop_free();
+        s.table.push_back(b);
+        if (i < nfull) {                       // a full prompt block: index it
+            PrefixKey k{i > 0 ? s.table[i - 1] : -1, std::vector<int32_t>(token_ids + i * B, token_ids + (i + 1) * B)};
+            bm->block_key[b] = k;
+            bm->prefix_index.emplace(std::move(k), b);
+        }
+    }
+    s.len = n_tokens;
+    if (slots_out)
+        for (int64_t p = 0; p < n_tokens; ++p) slots_out[p] = bm->slot_of(s, p);
+    if (num_cached_out) *num_cached_out = (int32_t)hits.size() * B;
+    bm->seqs.emplace(seq, std::move(s));
+    return PA_OK;
+}
+
+int32_t pa_bm_num_cached_blocks(pa_bm* bm) {
+    if (!bm) return -1;
+    std::lock_guard<std::mutex> g(bm->mu);
+    return (int32_t)bm->prefix_index.size();
 }
 
 int pa_bm_swap_out(pa_bm* bm, const int64_t* seqs, int32_t n, int64_t* pairs_out, int32_t cap,

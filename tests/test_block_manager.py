@@ -15,6 +15,7 @@ def _same_state(bm, m):
     for b in range(m.num_blocks):
         assert bm.refcount(b) == m.refcount[b]
     assert bm.host_free_list() == m.host_free
+    assert bm.num_cached_blocks() == len(m.prefix_index)
     for b in range(m.num_host_blocks):
         assert bm.host_refcount(b) == m.host_refcount[b]
     for seq, st in m.seqs.items():
@@ -34,6 +35,8 @@ def _apply(bm, m, op):
             want = m.fork(op[1], op[2])
         elif kind == "append":
             want = m.append_token(op[1])
+        elif kind == "add_cached":
+            want = m.add_sequence_cached(op[1], op[2])
         elif kind == "swap_out":
             want = m.swap_out(op[1])
         elif kind == "swap_in":
@@ -49,6 +52,9 @@ def _apply(bm, m, op):
             got = bm.fork(op[1], op[2])
         elif kind == "append":
             got = bm.append_token(op[1])
+        elif kind == "add_cached":
+            sl, nc = bm.add_sequence_cached(op[1], op[2])
+            got = (sl.tolist(), nc)
         elif kind == "swap_out":
             got = [tuple(p) for p in bm.swap_out(op[1]).tolist()]
         elif kind == "swap_in":
@@ -83,6 +89,19 @@ def test_random_streams_with_swaps_match_the_model(seed, nb, nh, B):
     bm = pa.BlockManager(nb, B, nh)
     m = BlockManagerModel(nb, B, nh)
     for op in workloads.block_manager_ops(seed * 17 + nb, 300, max_prompt=3 * B, swap=True):
+        _apply(bm, m, op)
+        _same_state(bm, m)
+        m.check_invariants()
+
+
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("nb,nh,B", [(16, 8, 4), (30, 10, 2), (24, 9, 8)])
+def test_random_streams_with_prefix_sharing_match_the_model(seed, nb, nh, B):
+    """Prompts built from a few shared prefixes, mixed with every other
+    operation (swaps included): index contents, tables and counts agree."""
+    bm = pa.BlockManager(nb, B, nh)
+    m = BlockManagerModel(nb, B, nh)
+    for op in workloads.block_manager_ops(seed * 7 + nb, 300, max_prompt=4 * B, swap=True, cached=True):
         _apply(bm, m, op)
         _same_state(bm, m)
         m.check_invariants()

@@ -335,3 +335,80 @@ def test_swap_round_trip_preserves_structure(seed):
         assert m.refcount[b] == holders[a]            # the group's share of the old count
         assert holders[a] <= counts[a]
     m.check_invariants()
+
+
+# ---------------------------------------------------------------------------
+# prefix sharing across requests ([n1n] 前缀缓存: 100 requests with one long
+# system prompt share its physical blocks; [lpnh-1824136] 3.2 second step)
+# ---------------------------------------------------------------------------
+def test_hundred_requests_share_one_system_prompt():
+    """The page's example, counted: a 1000-token system prompt (62 full
+    blocks of 16 + an 8-token tail) followed by each request's own text.
+    The 62 full blocks exist once with count 100; every request owns only
+    the blocks holding its tail and its own tokens."""
+    import numpy as np
+    rng = np.random.default_rng(0)
+    B, P, R = 16, 1000, 100
+    system = rng.integers(0, 32000, size=P).tolist()
+    suffix_lens = rng.integers(1, 200, size=R).tolist()
+    m = BlockManagerModel(20000, B)
+    cached = []
+    for r in range(R):
+        toks = system + rng.integers(0, 32000, size=suffix_lens[r]).tolist()
+        _, nc = m.add_sequence_cached(r, toks)
+        cached.append(nc)
+    full = P // B
+    assert cached == [0] + [full * B] * (R - 1)
+    shared = m.table(0)[:full]
+    assert all(m.table(r)[:full] == shared for r in range(R))
+    assert all(m.refcount[b] == R for b in shared)
+    used = 20000 - m.num_free()
+    want = full + sum(-(-(P + s) // B) - full for s in suffix_lens)
+    assert used == want
+    unshared = sum(-(-(P + s) // B) for s in suffix_lens)
+    assert unshared - used == (R - 1) * full        # the prefix is stored once, not 100 times
+    m.check_invariants()
+
+
+def test_divergence_inside_a_block_shares_the_blocks_before_it():
+    m = BlockManagerModel(32, 4)
+    a = list(range(100, 114))                      # 3 full blocks + 2 tokens
+    m.add_sequence_cached(0, a)
+    b = a[:9] + [7, 7, 7, 7, 7]                    # differs at position 9, inside block 2
+    _, nc = m.add_sequence_cached(1, b)
+    assert nc == 8 and m.table(1)[:2] == m.table(0)[:2] and m.table(1)[2] != m.table(0)[2]
+    _, nc = m.add_sequence_cached(2, a[:3])         # shorter than one block: nothing shared
+    assert nc == 0 and not set(m.table(2)) & set(m.table(0))
+    c = [9] * 4 + a[4:8]                           # same tokens as block 1 of `a`, another block 0
+    _, nc = m.add_sequence_cached(3, c)
+    assert nc == 0 and m.table(3)[1] != m.table(0)[1]   # the key chains through the block before
+    m.check_invariants()
+
+
+def test_fully_shared_prompt_appends_without_copy_and_index_forgets_freed_blocks():
+    m = BlockManagerModel(16, 4)
+    p = [1, 2, 3, 4, 5, 6, 7, 8]
+    m.add_sequence_cached(0, p)
+    _, nc = m.add_sequence_cached(1, p)
+    assert nc == 8 and m.table(1) == m.table(0)
+    slot, cow = m.append_token(1)                  # the shared last block is full: fresh block
+    assert cow is None and m.table(1)[:2] == m.table(0)[:2] and len(m.table(1)) == 3
+    assert len(m.prefix_index) == 2
+    m.free_sequence(0)
+    assert len(m.prefix_index) == 2                # sequence 1 still holds both blocks
+    m.free_sequence(1)
+    assert m.prefix_index == {} and m.num_free() == 16
+    _, nc = m.add_sequence_cached(2, p)
+    assert nc == 0
+    m.check_invariants()
+
+
+def test_cached_add_oom_changes_nothing():
+    m = BlockManagerModel(3, 4)
+    m.add_sequence_cached(0, list(range(8)))       # 2 blocks, both indexed
+    snap = (list(m.free), list(m.refcount), dict(m.prefix_index))
+    import pytest as _pytest
+    with _pytest.raises(OOM):
+        m.add_sequence_cached(1, list(range(8)) + list(range(50, 59)))   # 2 shared + 3 new > 1 free
+    assert snap == (list(m.free), list(m.refcount), dict(m.prefix_index))
+    m.check_invariants()

@@ -257,16 +257,25 @@ def parallel_sampling(seed: int = 0, num_blocks: int = 1024, block_size: int = 1
 # Random operation streams for the block manager (differential testing)
 # ---------------------------------------------------------------------------
 def block_manager_ops(seed: int, n_ops: int, max_seqs: int = 6,
-                      max_prompt: int = 40, swap: bool = False) -> List[tuple]:
+                      max_prompt: int = 40, swap: bool = False, cached: bool = False) -> List[tuple]:
     """A stream of ('add', seq, n) / ('fork', parent, child) / ('append', seq)
     / ('free', seq) operations, plus ('swap_out', [seqs]) / ('swap_in',
-    [seqs]) groups when swap is set.  Ids may be stale or unknown on purpose,
-    so error paths are exercised too."""
+    [seqs]) groups when swap is set and ('add_cached', seq, [token ids])
+    prompts drawn from a few shared prefixes when cached is set.  Ids may be
+    stale or unknown on purpose, so error paths are exercised too."""
     rng = _rng(seed, 6)
     ops = []
     next_id = 0
     swapped_groups: List[List[int]] = []      # groups sent out, to bring back later
+    prefixes = [rng.integers(0, 50, size=max_prompt).tolist() for _ in range(3)] if cached else []
     for _ in range(n_ops):
+        if cached and rng.random() < 0.2:
+            base = prefixes[int(rng.integers(0, 3))]
+            keep = int(rng.integers(0, max_prompt + 1))
+            tail = rng.integers(0, 50, size=int(rng.integers(0, max_prompt // 2 + 1))).tolist()
+            ops.append(("add_cached", next_id, [int(t) for t in base[:keep] + tail][:max_prompt]))
+            next_id += 1
+            continue
         if swap and rng.random() < 0.15:
             if swapped_groups and rng.random() < 0.5:
                 group = swapped_groups.pop(int(rng.integers(0, len(swapped_groups))))
