@@ -44,6 +44,8 @@ def lib() -> ctypes.CDLL:
     L.oracle_half_to_double.restype = f64
     L.oracle_decode.argtypes = [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i64, f64, i32]
     L.oracle_decode.restype = ctypes.c_int
+    L.oracle_prefill.argtypes = [P, P, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i64, f64, i32]
+    L.oracle_prefill.restype = ctypes.c_int
     L.oracle_attention_contig.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, f64, i32]
     L.oracle_attention_contig.restype = ctypes.c_int
     L.oracle_reshape_and_cache.argtypes = [P, P, i64, P, i32, P, P, i64, i32, i32, i32]
@@ -97,6 +99,34 @@ def decode(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
                              float(scale), nthreads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle_decode failed: {rc}")
+    return out
+
+
+def prefill(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+            block_tables: np.ndarray, context_lens: np.ndarray, query_start: np.ndarray,
+            scale: float, nthreads: int | None = None) -> np.ndarray:
+    """fp64 causal attention of the packed new tokens q[T, H, D] over the
+    paged caches: sequence s's rows query_start[s] .. query_start[s+1]-1 are
+    its last m tokens, row i at position context_lens[s] - m + i, attending
+    to positions 0 .. that position."""
+    _need(q, np.float16, "q")
+    _need(k_cache, np.float16, "k_cache")
+    _need(v_cache, np.float16, "v_cache")
+    _need(block_tables, np.int32, "block_tables")
+    _need(context_lens, np.int32, "context_lens")
+    _need(query_start, np.int32, "query_start")
+    T, H, D = q.shape
+    NB, Hkv, B, D2 = k_cache.shape
+    S = context_lens.shape[0]
+    if D2 != D or v_cache.shape != k_cache.shape or block_tables.shape[0] != S or \
+       query_start.shape != (S + 1,) or query_start[-1] != T or query_start[0] != 0:
+        raise ValueError("shape mismatch")
+    out = np.zeros((T, H, D), dtype=np.float64)
+    rc = lib().oracle_prefill(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                              block_tables.shape[1], _ptr(context_lens), _ptr(query_start), S, H, Hkv, D,
+                              B, NB, float(scale), nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle_prefill failed: {rc}")
     return out
 
 

@@ -231,6 +231,83 @@ int oracle_decode(double *out, const uint16_t *q, const uint16_t *k_cache,
 }
 
 /* ---------------------------------------------------------------------- */
+/* Paged prefill / chunked prefill: several new tokens of a sequence,     */
+/* each attending causally to the cached positions up to its own.         */
+/*                                                                        */
+/* Sequence s has n = context_lens[s] cached tokens, the last m of which  */
+/* are its new ones (m = query_start[s+1] - query_start[s]); query row    */
+/* query_start[s] + i is the token at position n - m + i and attends to   */
+/* positions 0 .. n - m + i.  This is the prompt path of a request (the   */
+/* pages: [lpnh-1824136] 3.2 second step; the attention kernels must read */
+/* the paged cache since a contiguous-memory kernel cannot, [n1n] on the  */
+/* limits of FlashAttention), with the same textbook softmax attention as */
+/* decode; m = 1 is decode.                                               */
+/* ---------------------------------------------------------------------- */
+struct prefill_ctx {
+    double *out;
+    const uint16_t *q, *k_cache, *v_cache;
+    const int32_t *block_tables, *context_lens, *query_start;
+    int32_t max_blocks, H, Hkv, D, B;
+    int64_t num_blocks;
+    double scale;
+};
+
+static int prefill_item(void *vctx, int64_t item)
+{
+    const struct prefill_ctx *c = (const struct prefill_ctx *)vctx;
+    int64_t s = item / c->H;
+    int h = (int)(item % c->H);
+    int kvh = h / (c->H / c->Hkv);
+    int D = c->D, B = c->B;
+    int64_t n = c->context_lens[s];
+    int64_t q0 = c->query_start[s], m = c->query_start[s + 1] - q0;
+    if (n < 0 || m < 0 || m > n || n > (int64_t)c->max_blocks * B) return ORACLE_ERANGE;
+    if (m == 0) return ORACLE_OK;
+
+    double *q = (double *)malloc((size_t)D * sizeof(double));
+    double *K = (double *)malloc((size_t)n * D * sizeof(double));
+    double *V = (double *)malloc((size_t)n * D * sizeof(double));
+    if (!q || !K || !V) { free(q); free(K); free(V); return ORACLE_ENOMEM; }
+    for (int64_t p = 0; p < n; ++p) {
+        int64_t phys = c->block_tables[s * c->max_blocks + p / B];
+        if (phys < 0 || phys >= c->num_blocks) { free(q); free(K); free(V); return ORACLE_ERANGE; }
+        int64_t base = ((phys * c->Hkv + kvh) * B + p % B) * (int64_t)D;
+        for (int d = 0; d < D; ++d) {
+            K[p * D + d] = oracle_half_to_double(c->k_cache[base + d]);
+            V[p * D + d] = oracle_half_to_double(c->v_cache[base + d]);
+        }
+    }
+    int rc = ORACLE_OK;
+    for (int64_t i = 0; i < m && rc == ORACLE_OK; ++i) {
+        int64_t row = (q0 + i) * c->H + h;
+        for (int d = 0; d < D; ++d) q[d] = oracle_half_to_double(c->q[row * D + d]);
+        /* causal: the token at position n - m + i sees positions 0 .. n - m + i */
+        rc = attend(c->out + row * D, q, K, V, n - m + i + 1, D, c->scale);
+    }
+    free(q); free(K); free(V);
+    return rc;
+}
+
+int oracle_prefill(double *out, const uint16_t *q, const uint16_t *k_cache,
+                   const uint16_t *v_cache, const int32_t *block_tables,
+                   int32_t max_blocks, const int32_t *context_lens,
+                   const int32_t *query_start, int32_t num_seqs, int32_t num_heads,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                   int64_t num_blocks, double scale, int32_t nthreads)
+{
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+        return ORACLE_EINVAL;
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 ||
+        num_heads % num_kv_heads || head_dim <= 0 || block_size <= 0 ||
+        max_blocks < 0 || num_blocks < 0)
+        return ORACLE_EINVAL;
+    struct prefill_ctx c = {out, q, k_cache, v_cache, block_tables, context_lens, query_start,
+                            max_blocks, num_heads, num_kv_heads, head_dim, block_size,
+                            num_blocks, scale};
+    return run_items(&c, prefill_item, (int64_t)num_seqs * num_heads, nthreads);
+}
+
+/* ---------------------------------------------------------------------- */
 /* Attention over logically contiguous K/V (no paging).                   */
 /* ---------------------------------------------------------------------- */
 struct contig_ctx {
