@@ -47,11 +47,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="llama7b", choices=["llama7b", "gqa", "long", "copy", "swap", "prefix"],
+    p.add_argument("--workload", default="llama7b", choices=["llama7b", "gqa", "long", "copy", "swap", "prefix", "prefill"],
                    help="llama7b: the Llama-2-7B decode batch (default); gqa: 64 query heads over 8 KV "
                         "heads (matrix-core kernel); long: 16 x 4096 tokens; copy: block-copy calibration; "
                         "swap: block swaps between HBM and pinned host memory; prefix: 100 requests "
-                        "sharing a 1000-token system prompt")
+                        "sharing a 1000-token system prompt; prefill: causal attention of 32 prompts "
+                        "(mean 500 tokens) over the paged cache")
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--batch", type=int, default=0, help="sequences (0: 64 for llama7b, 256 for gqa)")
     p.add_argument("--block-size", type=int, default=16)
@@ -116,6 +117,8 @@ def main():
         return swap_bench(args, dev)
     if args.workload == "prefix":
         return prefix_bench(args, dev)
+    if args.workload == "prefill":
+        return prefill_bench(args, dev)
 
     L = args.layers
     B = args.block_size
@@ -438,6 +441,83 @@ def prefix_bench(args, dev):
                       "config": {"workload": "prefix", "requests": R, "system_prompt": P,
                                  "own_tokens": "U[1,200]", "num_heads": H, "num_kv_heads": Hkv,
                                  "head_dim": D, "block_size": B, "layers_resident": L}}), flush=True)
+
+
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense fp16 matrix cores, published
+
+
+def prefill_bench(args, dev):
+    """Prompt prefill over the paged cache: 32 prompts with lengths
+    clip(N(500, 150), 16, 2048) (the prompt mix of the block-size
+    experiment on the 5688vip.com page), Llama-2-7B heads (32 x 128), B = 16,
+    --layers layers resident (default here 4).  Each timed call is one
+    layer's pa_prefill over every prompt (the K/V already scattered).
+    Algorithmic flops = sum over heads and new tokens of 4 * D * (causal
+    positions seen); against the dense fp16 matrix-core peak."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_390_amd as pa
+    import workloads
+
+    L = args.layers if args.layers != 32 else 4
+    S, H, Hkv, D, B = 32, 32, 32, 128, args.block_size
+    sw = workloads.block_size_sweep(seed=args.seed, num_seqs=S, gen_max=1)
+    lens_l = [int(n) - 1 for n in sw.lens]                 # the prompt part only
+    T = int(sum(lens_l))
+    NB = sum(-(-n // B) for n in lens_l) + 8
+    bm = pa.BlockManager(NB, B)
+    slots = np.concatenate([bm.add_sequence(s, n) for s, n in enumerate(lens_l)])
+    width = -(-max(lens_l) // B)
+    tables, lens = bm.get_tables(range(S), width)
+    qs = np.concatenate([[0], np.cumsum(lens_l)]).astype(np.int32)
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    kcs, vcs = [], []
+    for _ in range(L):
+        kc = torch.empty((NB, Hkv, B, D), dtype=torch.float16, device=dev)
+        vc = torch.empty_like(kc)
+        key = torch.randn((T, Hkv, D), generator=g, device=dev, dtype=torch.float16)
+        val = torch.randn((T, Hkv, D), generator=g, device=dev, dtype=torch.float16)
+        pa.pa_reshape_and_cache(key, val, torch.from_numpy(slots).to(dev), kc, vc)
+        kcs.append(kc)
+        vcs.append(vc)
+    q = torch.randn((T, H, D), generator=g, device=dev, dtype=torch.float16)
+    out = torch.empty_like(q)
+    d_t, d_l, d_q = (torch.from_numpy(x).to(dev) for x in (tables, lens, qs))
+    mq = max(lens_l)
+    flops = sum(4.0 * D * H * n * (n + 1) / 2 for n in lens_l)
+
+    def call(l):
+        pa.pa_prefill(out, q, kcs[l], vcs[l], d_t, d_l, d_q, 1 / np.sqrt(D), max_query_len=mq)
+
+    for _ in range(max(args.warmup, 3)):
+        for l in range(L):
+            call(l)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps * L)]
+    for i in range(args.steps):
+        for l in range(L):
+            a, b = ev[i * L + l]
+            a.record()
+            call(l)
+            b.record()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    tflops = flops / us / 1e6
+    log(f"[bench] prefill: {S} prompts, {T} tokens (max {mq}), {L} layers; {us:.1f} us per layer = "
+        f"{tflops:.1f} TFLOP/s ({100 * tflops / MFMA_F16_PEAK_TFLOPS:.1f}% of dense fp16 MFMA peak), "
+        f"{T / us * 1e6:.0f} prompt tokens/s per layer")
+    print(json.dumps({"metric": "paged prefill TFLOP/s", "value": round(tflops, 2), "unit": "TFLOP/s",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+                      "us_per_layer": round(us, 2), "tokens_per_s_per_layer": round(T / us * 1e6, 1),
+                      "dtype": "f16",
+                      "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
+                                   "traffic": None},
+                      "config": {"workload": "prefill", "prompts": S, "tokens": T, "max_prompt": mq,
+                                 "num_heads": H, "num_kv_heads": Hkv, "head_dim": D, "block_size": B,
+                                 "layers_resident": L}}), flush=True)
 
 
 if __name__ == "__main__":

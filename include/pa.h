@@ -136,6 +136,42 @@ int pa_decode(void *out, const void *q, const void *k_cache,
               void *workspace, size_t workspace_bytes, int32_t dtype,
               void *stream);
 
+/* ------------------------------------------------------------------------
+ * Paged prefill / chunked prefill: several new tokens per sequence, each
+ * attending causally to the cached positions up to its own.  This is the
+ * prompt path of a request ([lpnh-1824136] 3.2, second step) over the paged
+ * cache, which a contiguous-memory attention kernel cannot read ([n1n]
+ * 权衡与局限性); the result is textbook softmax attention, and one new token
+ * per sequence is exactly pa_decode.
+ *
+ *   out, q         device, fp16 [num_tokens, num_heads, head_dim]: the new
+ *                  tokens of all sequences packed in sequence order
+ *   query_start    device, int32 [num_seqs + 1]: sequence s owns rows
+ *                  query_start[s] .. query_start[s+1] - 1 (m_s of them); a
+ *                  sequence whose range is not inside [0, num_tokens) is
+ *                  skipped (its rows are left untouched)
+ *   context_lens   device, int32 [num_seqs]: n_s cached tokens INCLUDING the
+ *                  m_s new ones, whose K/V must already be in the cache
+ *                  (pa_reshape_and_cache); row query_start[s] + i is the
+ *                  token at position n_s - m_s + i
+ *   block_tables, k_cache, v_cache, num_blocks, block_size, scale: as for
+ *                  pa_decode
+ *   max_query_len  host-known bound on every m_s; it sizes the grid.  A
+ *                  sequence with m_s > max_query_len, m_s > n_s or n_s beyond
+ *                  its table gets its first max_query_len rows as NaN.
+ * head_dim 128 only (PA_ERR_UNSUPPORTED otherwise); any num_heads multiple of
+ * num_kv_heads.  Runs on the matrix cores (v_mfma_f32_16x16x16_f16, fp32
+ * accumulation); no workspace.
+ * ------------------------------------------------------------------------ */
+int pa_prefill(void *out, const void *q, int32_t num_tokens,
+               const void *k_cache, const void *v_cache,
+               const int32_t *block_tables, int32_t max_blocks_per_seq,
+               const int32_t *context_lens, const int32_t *query_start,
+               int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+               int32_t head_dim, int32_t block_size, int32_t num_blocks,
+               float scale, int32_t max_query_len, int32_t dtype,
+               void *stream);
+
 /* Bytes of workspace pa_decode needs for these sizes (0 when every sequence
  * fits one partition).  partition_size as for pa_decode (0 = default).
  * Returns (size_t)-1 for invalid arguments. */

@@ -9,7 +9,7 @@ current HIP stream.  There is no fallback: if the library is not built, every
 call raises.
 
 Functions carry the C names: ``pa_reshape_and_cache``, ``pa_decode``,
-``pa_decode_workspace_size``, ``pa_copy_blocks``, ``pa_swap_blocks``;
+``pa_decode_workspace_size``, ``pa_prefill``, ``pa_copy_blocks``, ``pa_swap_blocks``;
 ``BlockManager`` wraps the ``pa_bm_*`` calls.
 """
 from __future__ import annotations
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         "pa_reshape_and_cache": ([P, P, i64, P, i32, P, P, i32, i32, i32, i32, i32, P], ctypes.c_int),
         "pa_decode": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P, sz, i32, P],
                       ctypes.c_int),
+        "pa_prefill": ([P, P, i32, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P],
+                       ctypes.c_int),
         "pa_decode_workspace_size": ([i32, i32, i32, i32, i32, i32, i32], sz),
         "pa_decode_default_partition": ([i32, i32, i32, i32, i32, i32], i32),
         "pa_copy_blocks": ([P, P, i32, P, i32, i32, i64, i32, P], ctypes.c_int),
@@ -228,6 +230,37 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float
                            block_tables.data_ptr(), W, context_lens.data_ptr(), S, H, Hkv, D, B, NB,
                            float(scale), int(max_context_len), int(partition_size), ws_ptr, ws_bytes,
                            PA_DTYPE_F16, _stream(q.device)), "pa_decode")
+
+
+def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float,
+               max_query_len: Optional[int] = None) -> None:
+    """Causal attention of the packed new tokens q[T, H, D] over the paged
+    cache: sequence s's rows query_start[s] .. query_start[s+1]-1 are its
+    last m tokens (K/V already cached), row i at position context_lens[s] -
+    m + i.  max_query_len defaults to T."""
+    torch = _torch()
+    _dev_tensor(k_cache, "k_cache", torch.float16, 4)
+    _dev_tensor(v_cache, "v_cache", torch.float16, 4)
+    NB, Hkv, B, D = k_cache.shape
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    _dev_tensor(q, "q", torch.float16, 3)
+    _dev_tensor(out, "out", torch.float16, 3)
+    T, H, Dq = q.shape
+    if Dq != D or tuple(out.shape) != (T, H, D):
+        raise ValueError("q/out must be [T, H, head_dim]")
+    _dev_tensor(block_tables, "block_tables", torch.int32, 2)
+    _dev_tensor(context_lens, "context_lens", torch.int32, 1)
+    _dev_tensor(query_start, "query_start", torch.int32, 1)
+    S = context_lens.shape[0]
+    if block_tables.shape[0] != S or query_start.shape[0] != S + 1:
+        raise ValueError("block_tables / context_lens / query_start disagree on the number of sequences")
+    if max_query_len is None:
+        max_query_len = T
+    _check(lib().pa_prefill(out.data_ptr(), q.data_ptr(), T, k_cache.data_ptr(), v_cache.data_ptr(),
+                            block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
+                            query_start.data_ptr(), S, H, Hkv, D, B, NB, float(scale), int(max_query_len),
+                            PA_DTYPE_F16, _stream(q.device)), "pa_prefill")
 
 
 def pa_copy_blocks(k_caches: Sequence, v_caches: Sequence, src_dst_pairs) -> None:

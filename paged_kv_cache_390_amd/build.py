@@ -17,7 +17,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpa.so")
 
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
-HIP_SOURCES = ["decode.hip", "decode_gqa.hip", "cache_ops.hip"]
+HIP_SOURCES = ["decode.hip", "decode_gqa.hip", "prefill.hip", "cache_ops.hip"]
 CXX_SOURCES = ["block_manager.cpp", "status.cpp"]
 
 HIPCC_FLAGS = [
@@ -27,10 +27,11 @@ HIPCC_FLAGS = [
     "-Wall", "-Wno-unused-function",
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
-# per-source extra hipcc flags: the grouped-query kernel keeps its matrix-core
+# per-source extra hipcc flags: the matrix-core attention kernels keep their
 # accumulators in VGPRs (the online softmax reads and rescales them every tile;
 # in AGPRs each access would add a copy)
-HIP_EXTRA = {"decode_gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+HIP_EXTRA = {"decode_gqa.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+             "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:

@@ -1,0 +1,143 @@
+"""GPU parity of pa_prefill (several new tokens per sequence, causal over the
+paged cache, matrix-core kernel) against the oracle, through the C ABI.
+
+Caches are built on the host by the oracle (model slots + oracle scatter, NaN
+in every unused slot) and uploaded, so these tests isolate the kernel; the
+full-size case writes the prompt with the product's scatter first."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_390_amd as pa
+import workloads
+from gpu_common import assert_attention_close, bits, device, say
+from test_gpu_decode import _oracle_cache
+
+pytestmark = pytest.mark.gpu
+
+
+def _queries(seed, ms, H, D):
+    rng = np.random.default_rng([seed, 77])
+    q = rng.standard_normal((int(sum(ms)), H, D), dtype=np.float32).astype(np.float16)
+    return q, np.concatenate([[0], np.cumsum(ms)]).astype(np.int32)
+
+
+def _gpu_prefill(dev, q, kc, vc, tables, lens, qs, scale, max_query_len=None):
+    out = torch.full(q.shape, float("nan"), dtype=torch.float16, device=dev)
+    pa.pa_prefill(out, torch.from_numpy(q).to(dev), torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev),
+                  torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), torch.from_numpy(qs).to(dev),
+                  scale, max_query_len=max_query_len)
+    torch.cuda.synchronize()
+    return out
+
+
+LENS = [1, 2, 15, 16, 17, 33, 64, 100, 129, 300]
+
+
+@pytest.mark.parametrize("B", [1, 4, 8, 16, 32, 128])
+@pytest.mark.parametrize("H,Hkv", [(2, 2), (8, 2), (6, 3)])
+@pytest.mark.parametrize("chunk", ["full", "chunked", "decode"])
+def test_prefill_matches_oracle(B, H, Hkv, chunk):
+    dev = device()
+    case = workloads.random_case(900 + B + 10 * H + Hkv, LENS, H, Hkv, 128, B)
+    kc, vc, tables, lens = _oracle_cache(case)
+    if chunk == "full":
+        ms = list(LENS)
+    elif chunk == "chunked":
+        ms = [max(1, n // 3) for n in LENS]
+    else:
+        ms = [1] * len(LENS)
+    q, qs = _queries(B + H, ms, H, 128)
+    say(f"prefill B={B} H={H}/{Hkv} {chunk}: rows {int(qs[-1])}")
+    out = _gpu_prefill(dev, q, kc, vc, tables, lens, qs, case.scale)
+    ref = oracle.prefill(q, kc, vc, tables, lens, qs, case.scale)
+    assert_attention_close(out, ref, f"prefill B={B} H={H}/{Hkv} {chunk}")
+    if chunk == "decode":                                     # one new token per sequence is decode
+        dec = torch.empty_like(out)
+        pa.pa_decode(dec, torch.from_numpy(q).to(dev), torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev),
+                     torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), case.scale)
+        torch.cuda.synchronize()
+        assert_attention_close(dec, ref, "decode of the same rows")
+
+
+def test_prefill_edge_rows_and_bad_sequences():
+    """Empty sequences, a sequence whose new tokens exceed its context (NaN
+    rows), one beyond max_query_len (NaN for the covered rows), and one whose
+    query range leaves [0, T) (skipped: rows untouched)."""
+    dev = device()
+    case = workloads.random_case(31, [40, 10, 20, 30], 4, 2, 128, 16)
+    kc, vc, tables, lens = _oracle_cache(case)
+    ms = [40, 0, 25, 5]                                        # seq 2: 25 new > 20 cached
+    q, qs = _queries(31, ms, 4, 128)
+    out = _gpu_prefill(dev, q, kc, vc, tables, lens, qs, case.scale)
+    # rows 0..39: sequence 0; 40..64: sequence 2 (NaN); 65..69: sequence 3
+    ref = np.full(q.shape, np.nan)
+    sel = np.r_[0:40, 65:70]
+    ref[sel] = oracle.prefill(np.ascontiguousarray(q[sel]), kc, vc, np.ascontiguousarray(tables[[0, 3]]),
+                              np.ascontiguousarray(lens[[0, 3]]), np.array([0, 40, 45], np.int32), case.scale)
+    assert_attention_close(out, ref, "edge rows")
+    # max_query_len 30: sequence 0 (40 new tokens) is out of bounds -> its first 30 rows NaN, the rest untouched
+    out2 = _gpu_prefill(dev, q, kc, vc, tables, lens, qs, case.scale, max_query_len=30)
+    o2 = out2.float().cpu().numpy()
+    assert np.all(np.isnan(o2[0:30])) and np.all(np.isnan(o2[30:40]))   # (untouched rows stay NaN too)
+    assert_attention_close(out2[65:70], ref[65:70], "other sequences unaffected")
+    # a query range outside [0, T): sequence skipped, nothing written for it
+    bad_qs = qs.copy()
+    bad_qs[4] = int(qs[-1]) + 3
+    out3 = torch.zeros(q.shape, dtype=torch.float16, device=dev)
+    pa.pa_prefill(out3, torch.from_numpy(q).to(dev), torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev),
+                  torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), torch.from_numpy(bad_qs).to(dev),
+                  case.scale)
+    torch.cuda.synchronize()
+    assert np.all(bits(out3)[65:70] == 0)
+
+
+def test_prefill_is_deterministic_and_blind_to_placement():
+    dev = device()
+    case = workloads.random_case(41, [300, 64, 129], 8, 2, 128, 16, spare_blocks=30)
+    kc, vc, tables, lens = _oracle_cache(case)
+    q, qs = _queries(41, [300, 20, 100], 8, 128)
+    a = _gpu_prefill(dev, q, kc, vc, tables, lens, qs, case.scale)
+    b = _gpu_prefill(dev, q, kc, vc, tables, lens, qs, case.scale)
+    assert np.array_equal(bits(a), bits(b))
+    sigma = np.random.default_rng(2).permutation(case.num_blocks)
+    kc2, vc2 = np.empty_like(kc), np.empty_like(vc)
+    kc2[sigma], vc2[sigma] = kc, vc
+    t2 = np.where(tables >= 0, sigma[np.maximum(tables, 0)], -1).astype(np.int32)
+    c = _gpu_prefill(dev, q, kc2, vc2, t2, lens, qs, case.scale)
+    assert np.array_equal(bits(a), bits(c))
+
+
+def test_prompt_prefill_at_the_llama_shape():
+    """8 prompts of the block-size-sweep length mix (normal around 500
+    tokens) at 32 x 128 heads, B = 16: the product block manager admits
+    them, the product scatter writes their K/V, pa_prefill attends; every
+    row against the oracle."""
+    dev = device()
+    rng = np.random.default_rng(12)
+    lens_l = [int(x) for x in np.clip(np.rint(rng.normal(500, 150, size=8)), 16, 2048)]
+    H = Hkv = 32
+    D, B = 128, 16
+    NB = sum(-(-n // B) for n in lens_l) + 8
+    bm = pa.BlockManager(NB, B)
+    slots = np.concatenate([bm.add_sequence(s, n) for s, n in enumerate(lens_l)])
+    T = int(sum(lens_l))
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    key = torch.randn((T, Hkv, D), generator=g, device=dev, dtype=torch.float16)
+    val = torch.randn((T, Hkv, D), generator=g, device=dev, dtype=torch.float16)
+    q = torch.randn((T, H, D), generator=g, device=dev, dtype=torch.float16)
+    kc = torch.full((NB, Hkv, B, D), float("nan"), dtype=torch.float16, device=dev)
+    vc = torch.full_like(kc, float("nan"))
+    pa.pa_reshape_and_cache(key, val, torch.from_numpy(slots).to(dev), kc, vc)
+    width = -(-max(lens_l) // B)
+    tables, lens = bm.get_tables(range(8), width)
+    qs = np.concatenate([[0], np.cumsum(lens_l)]).astype(np.int32)
+    out = torch.empty_like(q)
+    pa.pa_prefill(out, q, kc, vc, torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev),
+                  torch.from_numpy(qs).to(dev), 1 / np.sqrt(D), max_query_len=max(lens_l))
+    torch.cuda.synchronize()
+    say(f"llama prompts: {lens_l}, T={T}")
+    ref = oracle.prefill(q.cpu().numpy(), kc.cpu().numpy(), vc.cpu().numpy(), tables, lens, qs, 1 / np.sqrt(D))
+    assert_attention_close(out, ref, "llama prompts")
