@@ -47,12 +47,13 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="llama7b", choices=["llama7b", "gqa", "long", "copy", "swap", "prefix", "prefill"],
+    p.add_argument("--workload", default="llama7b", choices=["llama7b", "gqa", "long", "copy", "swap", "prefix", "prefill", "sweep", "sampling"],
                    help="llama7b: the Llama-2-7B decode batch (default); gqa: 64 query heads over 8 KV "
                         "heads (matrix-core kernel); long: 16 x 4096 tokens; copy: block-copy calibration; "
                         "swap: block swaps between HBM and pinned host memory; prefix: 100 requests "
                         "sharing a 1000-token system prompt; prefill: causal attention of 32 prompts "
-                        "(mean 500 tokens) over the paged cache")
+                        "(mean 500 tokens) over the paged cache; sweep: decode of 256 sequences at "
+                        "block_size 8/16/32/64; sampling: 32 samples of one prompt with copy-on-write")
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--batch", type=int, default=0, help="sequences (0: 64 for llama7b, 256 for gqa)")
     p.add_argument("--block-size", type=int, default=16)
@@ -119,6 +120,10 @@ def main():
         return prefix_bench(args, dev)
     if args.workload == "prefill":
         return prefill_bench(args, dev)
+    if args.workload == "sweep":
+        return sweep_bench(args, dev)
+    if args.workload == "sampling":
+        return sampling_bench(args, dev)
 
     L = args.layers
     B = args.block_size
@@ -132,7 +137,8 @@ def main():
         wl_name = "gqa-64q-8kv-decode"
         ctx_desc = "U[1,2048]"
     else:
-        w = workloads.long_context(seed=args.seed, num_seqs=16, block_size=B)
+        w = workloads.long_context(seed=args.seed, num_seqs=16, block_size=B,
+                                   spare_blocks=16 * workloads.ceil_div(W + K + 1, B))
         wl_name = "long-context-decode"
         ctx_desc = "4096"
     S, H, Hkv, D, NB = len(w.lens), w.num_heads, w.num_kv_heads, w.head_dim, w.num_blocks
@@ -518,6 +524,136 @@ def prefill_bench(args, dev):
                       "config": {"workload": "prefill", "prompts": S, "tokens": T, "max_prompt": mq,
                                  "num_heads": H, "num_kv_heads": Hkv, "head_dim": D, "block_size": B,
                                  "layers_resident": L}}), flush=True)
+
+
+def sweep_bench(args, dev):
+    """Block-size sweep: 256 sequences with context = prompt (N(500, 150),
+    clipped to [16, 2048]) + generated (U[1, 1024]) -- the length mix of the
+    5688vip.com page's block-size experiment -- at the Llama-2-7B head shape,
+    one set of token values laid out at B = 8, 16, 32, 64 (pool = the blocks
+    the sequences need, tables a random permutation).  For each B: pa_decode
+    timed with HIP events (K/V ~4.2 GB, far beyond the 256 MB MALL), KV GB/s,
+    and the bytes the partly filled last blocks leave unused."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_390_amd as pa
+    import workloads
+
+    w = workloads.block_size_sweep(seed=args.seed)
+    S = len(w.lens)
+    k, v = w.tokens(dev)
+    q = w.query(dev)
+    kv_tok = 2 * w.num_kv_heads * w.head_dim * 2
+    logical = int(w.lens.astype(np.int64).sum()) * kv_tok
+    res = {}
+    for B in (8, 16, 32, 64):
+        tables = w.perm_tables(B)
+        NB = sum(len(t) for t in tables)
+        bm = pa.BlockManager(NB, B)
+        for s in range(S):
+            bm.set_table(s, tables[s], int(w.lens[s]))
+        slots = np.concatenate([bm.get_slots(s, 0, int(w.lens[s])) for s in range(S)])
+        width = max(len(t) for t in tables)
+        tab, lens = bm.get_tables(range(S), width)
+        kc = torch.empty((NB, w.num_kv_heads, B, w.head_dim), dtype=torch.float16, device=dev)
+        vc = torch.empty_like(kc)
+        pa.pa_reshape_and_cache(k, v, torch.from_numpy(slots).to(dev), kc, vc)
+        d_t, d_l = torch.from_numpy(tab).to(dev), torch.from_numpy(lens).to(dev)
+        ws = torch.zeros(max(1, pa.pa_decode_workspace_size(S, w.num_heads, w.num_kv_heads, w.head_dim, B,
+                                                            width * B, 0)), dtype=torch.uint8, device=dev)
+        out = torch.empty_like(q)
+
+        def call():
+            pa.pa_decode(out, q, kc, vc, d_t, d_l, w.scale, B, max_context_len=width * B, workspace=ws)
+
+        for _ in range(max(args.warmup, 5)):
+            call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in ev:
+            a.record()
+            call()
+            b.record()
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+        waste = sum(len(t) * B - int(n) for t, n in zip(tables, w.lens)) * kv_tok
+        res[B] = {"us": round(us, 2), "GB_s": round(logical / us / 1e3, 1),
+                  "pct_hbm_peak": round(100 * logical / us / 1e3 / HBM_PEAK_GBS, 2),
+                  "tail_waste_MB": round(waste / 1e6, 1), "table_entries": int(NB),
+                  "partition": pa.pa_decode_default_partition(S, w.num_heads, w.num_kv_heads, w.head_dim, B,
+                                                              width * B)}
+        log(f"[bench] sweep B={B}: {us:.1f} us = {logical / us / 1e3:.0f} GB/s, tail waste {waste / 1e6:.1f} MB, "
+            f"{NB} blocks")
+        del kc, vc
+        torch.cuda.empty_cache()
+    print(json.dumps({"metric": "paged-decode KV GB/s by block size", "value": res[16]["GB_s"], "unit": "GB/s",
+                      "n_gpus": 1, "steps": args.steps, "higher_is_better": True, "by_block_size": res,
+                      "kv_bytes_per_call": logical,
+                      "config": {"workload": "block-size-sweep", "batch": S, "context": "N(500,150)+U[1,1024]",
+                                 "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads,
+                                 "head_dim": w.head_dim}}), flush=True)
+
+
+def sampling_bench(args, dev):
+    """Parallel sampling with copy-on-write: one 1000-token prompt (63
+    blocks, the last holding 8 tokens) forked into 32 samples; every step
+    appends one token per sample through the block manager (step 0: 31
+    copy-on-write pairs -> pa_copy_blocks), writes the 32 new K/V rows and
+    decodes all 32 samples -- the lpnh.cn/news/2758356 section 4 scenario,
+    Llama-2-7B heads, B = 16, one layer.  Reported: time per step, and the
+    logical KV bytes the decodes attend over per second (shared prompt
+    blocks counted once per sample; they are re-read from the caches)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_390_amd as pa
+    import workloads
+
+    w = workloads.parallel_sampling(seed=args.seed)
+    NB, B, N = w.num_blocks, w.block_size, w.num_samples
+    bm = pa.BlockManager(NB, B)
+    kp, vp = w.prompt_tokens(dev)
+    kc = torch.empty((NB, w.num_kv_heads, B, w.head_dim), dtype=torch.float16, device=dev)
+    vc = torch.empty_like(kc)
+    pa.pa_reshape_and_cache(kp, vp, torch.from_numpy(bm.add_sequence(0, w.prompt_len)).to(dev), kc, vc)
+    for c in range(1, N):
+        bm.fork(0, c)
+    seqs = list(range(N))
+    width = workloads.ceil_div(w.prompt_len + w.steps, B)
+    toks = [w.step_tokens(i, dev) for i in range(w.steps)]
+    out = torch.empty_like(toks[0][0])
+    ws = torch.zeros(max(1, pa.pa_decode_workspace_size(N, w.num_heads, w.num_kv_heads, w.head_dim, B, width * B,
+                                                        0)), dtype=torch.uint8, device=dev)
+    kv_tok = 2 * w.num_kv_heads * w.head_dim * 2
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    logical = 0
+    ncow = 0
+    for i in range(w.steps):
+        q, key, val = toks[i]
+        slots, pairs = bm.append_tokens(seqs)
+        ncow += len(pairs)
+        if len(pairs):
+            pa.pa_copy_blocks([kc], [vc], torch.from_numpy(pairs).to(dev))
+        pa.pa_reshape_and_cache(key, val, torch.from_numpy(slots).to(dev), kc, vc)
+        tables, lens = bm.get_tables(seqs, width)
+        pa.pa_decode(out, q, kc, vc, torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), w.scale, B,
+                     max_context_len=width * B, workspace=ws)
+        logical += int(lens.astype(np.int64).sum()) * kv_tok
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    used = NB - bm.num_free()
+    log(f"[bench] sampling: {w.steps} steps of {N} samples in {wall * 1e3:.1f} ms ({wall / w.steps * 1e6:.1f} us "
+        f"per step incl. host work), {ncow} copy-on-write pairs, {used} blocks at the end "
+        f"({N * workloads.ceil_div(w.prompt_len + w.steps, B)} unshared); {logical / wall / 1e9:.0f} GB/s logical KV")
+    print(json.dumps({"metric": "parallel-sampling decode step (COW), logical KV GB/s",
+                      "value": round(logical / wall / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": w.steps,
+                      "higher_is_better": True, "us_per_step": round(wall / w.steps * 1e6, 2),
+                      "cow_pairs": ncow, "blocks_at_end": used,
+                      "blocks_unshared": N * workloads.ceil_div(w.prompt_len + w.steps, B),
+                      "config": {"workload": "parallel-sampling", "samples": N, "prompt": w.prompt_len,
+                                 "block_size": B, "num_heads": w.num_heads, "head_dim": w.head_dim}}), flush=True)
 
 
 if __name__ == "__main__":

@@ -153,14 +153,16 @@ def gqa_decode(seed: int = 0, num_seqs: int = 256, max_len: int = 2048, block_si
 
 def long_context(seed: int = 0, num_seqs: int = 16, ctx: int = 4096,
                  block_size: int = 16, num_heads: int = 32, num_kv_heads: int = 32,
-                 head_dim: int = 128, layers: int = 32) -> PoolDecode:
-    """Every sequence at the same length; one permutation table for all layers."""
+                 head_dim: int = 128, layers: int = 32, spare_blocks: int = 0) -> PoolDecode:
+    """Every sequence at the same length; one permutation table for all
+    layers.  spare_blocks extra ids (the highest) stay out of the tables, for
+    tokens appended later."""
     rng = _rng(seed, 4)
     lens = np.full(num_seqs, ctx, dtype=np.int32)
     width = ceil_div(ctx, block_size)
     nb = num_seqs * width
     perm = rng.permutation(nb).astype(np.int32)
-    return PoolDecode(block_size, nb, num_heads, num_kv_heads, head_dim, lens,
+    return PoolDecode(block_size, nb + spare_blocks, num_heads, num_kv_heads, head_dim, lens,
                       perm.reshape(num_seqs, width), 1.0 / math.sqrt(head_dim), seed, layers)
 
 
