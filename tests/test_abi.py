@@ -116,3 +116,69 @@ def test_copy_blocks_rejects_bad_arguments():
     assert L.pa_copy_blocks(None, None, 1, 16, 1, 8, 64, 0, None) == pa.PA_ERR_INVALID
     assert L.pa_copy_blocks(None, None, 0, None, 0, 8, 64, 0, None) == pa.PA_OK
     assert L.pa_copy_blocks(None, None, 1, 16, 1, 8, 64, 3, None) == pa.PA_ERR_UNSUPPORTED
+
+
+def _prefill_args(**kw):
+    a = dict(out=16, q=16, T=4, k=16, v=16, tables=16, W=4, lens=16, qs=16, S=1, H=2, Hkv=2, D=128, B=16, NB=8,
+             scale=0.1, maxq=4, dtype=0, stream=None)
+    a.update(kw)
+    return (a["out"], a["q"], a["T"], a["k"], a["v"], a["tables"], a["W"], a["lens"], a["qs"], a["S"], a["H"],
+            a["Hkv"], a["D"], a["B"], a["NB"], a["scale"], a["maxq"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=1), pa.PA_ERR_UNSUPPORTED),
+    (dict(D=64), pa.PA_ERR_UNSUPPORTED),            # the matrix-core prefill serves head_dim 128
+    (dict(B=12), pa.PA_ERR_UNSUPPORTED),
+    (dict(H=3, Hkv=2), pa.PA_ERR_INVALID),
+    (dict(NB=0), pa.PA_ERR_INVALID),
+    (dict(T=-1), pa.PA_ERR_INVALID),
+    (dict(maxq=-1), pa.PA_ERR_INVALID),
+    (dict(scale=float("inf")), pa.PA_ERR_INVALID),
+    (dict(qs=None), pa.PA_ERR_INVALID),
+    (dict(out=8), pa.PA_ERR_INVALID),               # misaligned
+    (dict(maxq=1 << 30), pa.PA_ERR_INVALID),        # more row tiles than a grid holds
+])
+def test_prefill_rejects_bad_arguments_before_launch(kw, code):
+    assert pa.lib().pa_prefill(*_prefill_args(**kw)) == code
+    assert pa.last_error()
+
+
+def test_prefill_with_nothing_to_do_is_a_no_op():
+    L = pa.lib()
+    assert L.pa_prefill(*_prefill_args(S=0, out=None)) == pa.PA_OK
+    assert L.pa_prefill(*_prefill_args(T=0, out=None)) == pa.PA_OK
+
+
+def test_swap_blocks_rejects_bad_arguments_before_launch():
+    """Bad sizes, directions and dtypes are refused before any pointer is
+    looked at; zero pairs or caches enqueue nothing."""
+    L = pa.lib()
+    call = L.pa_swap_blocks
+    assert call(None, None, 1, 16, 1, 8, 8, 64, pa.PA_SWAP_OUT, 1, None) == pa.PA_ERR_UNSUPPORTED
+    assert call(None, None, 1, 16, 1, 8, 8, 64, 5, 0, None) == pa.PA_ERR_INVALID
+    assert call(None, None, 1, 16, 1, 8, 8, 0, pa.PA_SWAP_IN, 0, None) == pa.PA_ERR_INVALID
+    assert call(None, None, -1, 16, 1, 8, 8, 64, pa.PA_SWAP_IN, 0, None) == pa.PA_ERR_INVALID
+    assert call(None, None, 1, 16, 1, 8, 8, 64, pa.PA_SWAP_OUT, 0, None) == pa.PA_ERR_INVALID   # null arrays
+    assert call(None, None, 0, None, 0, 8, 8, 64, pa.PA_SWAP_OUT, 0, None) == pa.PA_OK
+    assert call(None, None, 2, None, 0, 8, 8, 64, pa.PA_SWAP_IN, 0, None) == pa.PA_OK
+
+
+def test_block_manager_swap_and_prefix_calls_check_arguments():
+    L = pa.lib()
+    bm = pa.BlockManager(8, 4, 4)
+    n = ctypes.c_int32()
+    assert L.pa_bm_swap_out(bm._h, None, -1, None, 0, ctypes.byref(n)) == pa.PA_ERR_INVALID
+    assert L.pa_bm_swap_in(bm._h, None, 0, None, 0, None) == pa.PA_ERR_INVALID       # no count output
+    assert L.pa_bm_add_sequence_cached(bm._h, 0, None, 3, None, None) == pa.PA_ERR_INVALID
+    assert L.pa_bm_is_swapped(bm._h, 42) == -1
+    assert L.pa_bm_host_refcount(bm._h, 4) == -1 and L.pa_bm_host_refcount(bm._h, 0) == 0
+    assert L.pa_bm_num_cached_blocks(bm._h) == 0
+    bm.add_sequence(0, 9)
+    with pytest.raises(pa.PAError):                                                   # cap too small
+        L_pairs = (ctypes.c_int64 * 2)()
+        seqs = (ctypes.c_int64 * 1)(0)
+        rc = L.pa_bm_swap_out(bm._h, ctypes.cast(seqs, ctypes.c_void_p), 1, ctypes.cast(L_pairs, ctypes.c_void_p), 1,
+                              ctypes.byref(n))
+        pa._check(rc, "swap_out")
+    assert not bm.is_swapped(0) and bm.num_free() == 5 and bm.host_free_list() == [0, 1, 2, 3]
