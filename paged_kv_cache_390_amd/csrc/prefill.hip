@@ -13,24 +13,33 @@
 // K/V tile meets every later query of its sequence, so the products run on
 // the matrix cores (v_mfma_f32_16x16x32_f16, fp32 accumulation).
 //  * Query rows: the m new tokens x g query heads of one KV head, token
-//    major (row r = token r / g, head r % g).  A wave owns 16 rows -- the N
-//    side of the MFMA tiles.  A 512-thread workgroup is 8 such waves (128
-//    rows) of one (KV head, sequence); grid x = KV head (fastest, for XCD
-//    balance), y = sequence, z = row tile, issued last row tile first so the
-//    longest causal ranges start earliest.
+//    major (row r = token r / g, head r % g).  A wave owns 32 rows as two
+//    groups of 16 -- the N side of its MFMA tiles -- so that every K or V
+//    operand read from LDS feeds two products.  A 256-thread workgroup is 4
+//    such waves (128 rows) of one (KV head, sequence); 2 workgroups share a
+//    CU.  Grid x = KV head (fastest, for XCD balance), y = sequence, z = row
+//    tile, issued last row tile first so the longest causal ranges start
+//    earliest.
 //  * K/V tiles of 32 tokens are staged through LDS once per workgroup and
-//    read by all 8 waves: each thread fetches 16 bytes of one token row of K
-//    and of V (table lookup per row, nontemporal loads) two tiles ahead into
-//    registers, and stores them one tile ahead into the other of two LDS
-//    buffers; one barrier per tile.  Rows are padded to 272 bytes so that
-//    the 16 rows one operand read touches fall in different banks.
+//    read by all 4 waves: each thread fetches 16 bytes of two token rows of
+//    K and of V (nontemporal loads) two tiles ahead into registers, and
+//    stores them one tile ahead into the other of two LDS buffers; one
+//    barrier per tile.  A wave's 4 rows of one fetch share a table entry
+//    (blocks of 4 or more tokens), read a tile ahead with a scalar load.
+//    Every step issues the same loads, so the waits before a store count
+//    only the older tile.  Rows are padded to 272 bytes so that the 16 rows
+//    one operand read touches fall in different banks.
 //  * QK as S^T = K Q^T: MFMA c takes head_dim 32c + 8*(l/16) + 0..7 in lane
-//    l, one 16-byte LDS read of K per MFMA; Q^T operands stay in registers.
-//    S^T lands with each lane holding 8 scores of one row (tokens 4j..4j+3
-//    and 16+4j..16+4j+3 of the tile) -- exactly that lane's A operand of P
-//    for the 32-token PV product, so the online softmax (base 2, causal and
-//    validity masks by select) runs in place and P goes to the matrix core
-//    as fp16; the row sum adds the same rounded weights.
+//    l, one 16-byte LDS read of K per two MFMAs; Q^T operands stay in
+//    registers.  S^T lands with each lane holding 8 scores of one row
+//    (tokens 4j..4j+3 and 16+4j..16+4j+3 of the tile) -- exactly that lane's
+//    A operand of P for the 32-token PV product, so the online softmax (base
+//    2) runs in place and P goes to the matrix core as fp16; the row sum
+//    adds the same rounded weights.  Row max and sum cross the 4 lanes of a
+//    row with v_permlane32_swap / v_permlane16_swap.  Tiles wholly before a
+//    wave's first row and wholly valid skip the masks; the running maximum
+//    moves lazily (only when a tile's exceeds it by a factor above 2^8), so
+//    O is rarely rescaled.
 //  * PV: output column n of d-tile c is d = 8n + c; the lane reads its 8
 //    token rows' columns 8n..8n+7 and builds each B operand with 4
 //    v_perm_b32 (an 8 x 8 transpose of halves).
@@ -48,9 +57,10 @@
 
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowsPerWave = 16;
+constexpr int kNT = 2;                     // 16-row groups per wave (the N side of its MFMA tiles)
+constexpr int kRowsPerWave = 16 * kNT;
 constexpr int kRowsPerGroup = kWaves * kRowsPerWave;
 constexpr double kLog2e = 1.4426950408889634073599246810019;
 
@@ -65,8 +75,10 @@ constexpr int kTileBytes = kKvTile * kPitch;
 typedef _Float16 half8_t_ __attribute__((ext_vector_type(8)));
 
 // One thread's share of a K/V tile in flight: 16 bytes (columns 8*col ..
-// 8*col+7) of kStageRows token rows -- tok, tok + kThreads/16, ... with tok
-// = thread / 16 -- of K and of V.
+// 8*col+7) of kStageRows token rows of K and of V.  Thread (wave w, lane l)
+// stages rows 4w + l/16 + (kThreads/16)*i, i < kStageRows: a wave's rows for
+// one i are 4 consecutive tokens starting at a multiple of 4, so with blocks
+// of 4 or more tokens they share one table entry, read with a scalar load.
 constexpr int kStageRows = kKvTile * 16 / kThreads;
 static_assert(kStageRows >= 1 && kKvTile * 16 == kStageRows * kThreads, "tile rows must split evenly");
 
@@ -75,111 +87,212 @@ struct Staged {
     bool ok[kStageRows];
 };
 
-// Fetch tile k (tokens 32k .. 32k+31) from HBM into registers.
+// First token of the wave's stage row i of tile k.
+__device__ __forceinline__ int stage_token0(int k, int wave, int i) {
+    return k * kKvTile + 4 * wave + (kThreads / 16) * i;
+}
+
+// Table entries of the wave's stage rows of tile k (B >= 4: one per row,
+// uniform over the wave); tokens past the context read the last token's
+// entry and are masked.
 template <int B>
-__device__ __forceinline__ void fetch_tile(Staged& st, int k, int n, const int32_t* __restrict__ trow,
-                                           const _Float16* __restrict__ kbase, const _Float16* __restrict__ vbase,
-                                           int64_t blk_stride, int32_t num_blocks) {
-    const int tok = (int)threadIdx.x / 16;
-    const int col = (int)threadIdx.x % 16;
+__device__ __forceinline__ void table_entries(int32_t (&e)[kStageRows], int k, int wave, int n,
+                                              const int32_t* __restrict__ trow) {
 #pragma unroll
     for (int i = 0; i < kStageRows; ++i) {
-        const int t = k * kKvTile + tok + (kThreads / 16) * i;
-        const int tc = t < n ? t : n - 1;
-        const int32_t phys = trow[tc / B];
-        const bool ok = t < n && (uint32_t)phys < (uint32_t)num_blocks;
-        const int64_t off = (int64_t)(ok ? phys : 0) * blk_stride + (int64_t)(tc % B) * kD + col * 8;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        st.k[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off)) : z;
-        st.v[i] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + off)) : z;
+        const int t = stage_token0(k, wave, i);
+        e[i] = trow[(t < n ? t : n - 1) / B];
+    }
+}
+
+// Fetch tile k (tokens 32k .. 32k+31) from HBM into registers; `e` holds
+// its table entries when B >= 4 (read a step earlier), else every thread
+// looks up its own row.
+template <int B>
+__device__ __forceinline__ void fetch_tile(Staged& st, int k, const int32_t (&e)[kStageRows], int wave, int lane,
+                                           int n, const int32_t* __restrict__ trow,
+                                           const _Float16* __restrict__ kbase, const _Float16* __restrict__ vbase,
+                                           int64_t blk_stride, int32_t num_blocks) {
+    const int col = lane & 15;
+#pragma unroll
+    for (int i = 0; i < kStageRows; ++i) {
+        const int t0 = stage_token0(k, wave, i);           // uniform, a multiple of 4
+        const int t = t0 + (lane >> 4);
+        int32_t phys;
+        int row;                                           // row inside the block
+        if constexpr (B >= 4) {
+            // the wave's 4 rows share entry e[i] (of token min(t0, n-1)) and
+            // lie at t0 % B + 0..3 of a block -- inside it also past the context
+            phys = e[i];
+            row = t0 % B + (lane >> 4);
+        } else {
+            const int tc = t < n ? t : n - 1;
+            phys = trow[tc / B];
+            row = tc % B;
+        }
+        const bool in_pool = (uint32_t)phys < (uint32_t)num_blocks;
+        const bool ok = t < n && in_pool;
+        const int64_t off = (int64_t)(in_pool ? phys : 0) * blk_stride + row * kD + col * 8;
+        // unconditional loads (a row past the context or with an id outside
+        // the pool reads a row of some valid block and is zeroed when
+        // stored): a fixed number of loads per tile lets the waits count
+        // only the older tile's
+        st.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off));
+        st.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + off));
         st.ok[i] = ok;
     }
 }
 
-__device__ __forceinline__ void store_tile(const Staged& st, unsigned char* buf, unsigned char* flags) {
-    const int tok = (int)threadIdx.x / 16;
-    const int col = (int)threadIdx.x % 16;
+__device__ __forceinline__ void store_tile(const Staged& st, unsigned char* buf, unsigned char* flags, int wave,
+                                           int lane) {
+    const int col = lane & 15;
+    bool all_ok = true;
 #pragma unroll
-    for (int i = 0; i < kStageRows; ++i) {
-        const int row = tok + (kThreads / 16) * i;
-        *reinterpret_cast<u32x4*>(buf + row * kPitch + col * 16) = st.k[i];
-        *reinterpret_cast<u32x4*>(buf + kTileBytes + row * kPitch + col * 16) = st.v[i];
-        if (col == 0) flags[row] = st.ok[i];
+    for (int i = 0; i < kStageRows; ++i) all_ok = all_ok && st.ok[i];
+    if (__all(all_ok)) {                                   // no row to zero (uniform)
+#pragma unroll
+        for (int i = 0; i < kStageRows; ++i) {
+            const int row = stage_token0(0, wave, i) + (lane >> 4);
+            *reinterpret_cast<u32x4*>(buf + row * kPitch + col * 16) = st.k[i];
+            *reinterpret_cast<u32x4*>(buf + kTileBytes + row * kPitch + col * 16) = st.v[i];
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kStageRows; ++i) {
+            const int row = stage_token0(0, wave, i) + (lane >> 4);
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(buf + row * kPitch + col * 16) = st.ok[i] ? st.k[i] : z;
+            *reinterpret_cast<u32x4*>(buf + kTileBytes + row * kPitch + col * 16) = st.ok[i] ? st.v[i] : z;
+        }
     }
+#pragma unroll
+    for (int i = 0; i < kStageRows; ++i)
+        if (col == 0) flags[stage_token0(0, wave, i) + (lane >> 4)] = st.ok[i];
 }
 
-// Runtime flags of one wave's rows.
+// Runtime flags of one of the wave's 16-row groups, for this lane's row.
 struct Rows {
-    bool live;       // this lane's row (l % 16) exists
+    bool live;       // the row (l % 16 of its group) exists
     int pos;         // its position
 };
 
-// Consume one LDS tile for the wave's 16 rows on v_mfma_f32_16x16x32_f16.
+typedef _Float16 half2_t_ __attribute__((ext_vector_type(2)));
+
+constexpr float kLazyMax = 8.f;           // log2 slack of the running maximum
+
+// Cross-lane reductions over the four lanes l % 16 + 16 j (j = 0..3) that
+// hold one row's scores: v_permlane32_swap pairs lanes l and l ^ 32,
+// v_permlane16_swap lanes l and l ^ 16; each returns the two values of the
+// pair in its two results, so max / sum of them is the pair's.
+
+__device__ __forceinline__ float row_max4(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float row_sum4(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Consume one LDS tile for the wave's kNT groups of 16 rows on
+// v_mfma_f32_16x16x32_f16.  Every operand read from LDS feeds kNT products.
 //   QK, per 16-token half h: S^T[token][row] = sum_d K[token][d] Q[row][d];
 //     MFMA c takes d = 32c + 8*(l/16) + 0..7 in lane l (one 16-byte LDS read).
 //   PV: k = 32 tokens; lane (n, j) supplies P[row n][tokens 4j..4j+3 and
 //     16+4j..16+4j+3] -- exactly the scores it holds -- and V rows of the
 //     same tokens at columns 8n..8n+7; output column n of d-tile c is d = 8n+c.
-__device__ __forceinline__ void consume_lds_tile(Softmax& st, const unsigned char* buf, const unsigned char* flags,
-                                                 int t0, const half8_t_ (&qb)[4], float scale_log2, int lane,
-                                                 const Rows& rw) {
+// `interior` (uniform): every token of the tile is valid and at or before
+// the first row's position, so no score is masked.  The exponent of a
+// weight is one FMA of the raw score: c = scale * log2(e) > 0, so the raw
+// maximum times c is the maximum of the scaled scores, and -inf stays -inf.
+__device__ __forceinline__ void consume_lds_tile(Softmax (&st)[kNT], const unsigned char* buf,
+                                                 const unsigned char* flags, int t0, bool interior,
+                                                 const half8_t_ (&qb)[kNT][4], float c_log2, int lane,
+                                                 const Rows (&rw)[kNT]) {
     constexpr int NS = kKvTile / 32;            // 32-token sub-tiles (one PV MFMA k-slab each)
     const int n = lane & 15;
     const int j = lane >> 4;
     const unsigned char* kb = buf;
     const unsigned char* vb = buf + kTileBytes;
-    float4_t s2[2 * NS];
+    float4_t s2[kNT][2 * NS];
 #pragma unroll
     for (int h = 0; h < 2 * NS; ++h) {
-        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+        float4_t acc[kNT];
+#pragma unroll
+        for (int t = 0; t < kNT; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const half8_t_ a = __builtin_bit_cast(half8_t_, *reinterpret_cast<const u32x4*>(
                                                                kb + (16 * h + n) * kPitch + 64 * c + 16 * j));
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[c], acc, 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < kNT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[t][c], acc[t], 0, 0, 0);
         }
-        s2[h] = acc;
+#pragma unroll
+        for (int t = 0; t < kNT; ++t) s2[t][h] = acc[t];
     }
-    // flags of this lane's tokens 16h + 4j .. 16h + 4j + 3: one dword per half
-    float sc[8 * NS];
-    float mt = -INFINITY;
+    half8_t_ p[kNT][NS];
 #pragma unroll
-    for (int h = 0; h < 2 * NS; ++h) {
-        const uint32_t fl = *reinterpret_cast<const uint32_t*>(flags + 16 * h + 4 * j);
+    for (int t = 0; t < kNT; ++t) {
+        // raw scores, -inf where masked
+        float sc[8 * NS];
+        if (interior) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int tok = 16 * h + 4 * j + e;
-            const bool keep = rw.live && ((fl >> (8 * e)) & 0xffu) && t0 + tok <= rw.pos;
-            sc[4 * h + e] = keep ? s2[h][e] * scale_log2 : -INFINITY;
-            mt = fmaxf(mt, sc[4 * h + e]);
+            for (int h = 0; h < 2 * NS; ++h)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sc[4 * h + e] = s2[t][h][e];
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2 * NS; ++h) {
+                // flags of tokens 16h + 4j .. +3, one byte each
+                const uint32_t fl = *reinterpret_cast<const uint32_t*>(flags + 16 * h + 4 * j);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tok = 16 * h + 4 * j + e;
+                    const bool keep = rw[t].live && ((fl >> (8 * e)) & 0xffu) && t0 + tok <= rw[t].pos;
+                    sc[4 * h + e] = keep ? s2[t][h][e] : -INFINITY;
+                }
+            }
         }
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(st.m, mt);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(st.m - m_use);
-    half8_t_ p[NS];
-    float lt = 0.f;
+        float mt = sc[0];
 #pragma unroll
-    for (int i = 0; i < 8 * NS; ++i) {
-        // sub-tile u = i / 8 takes halves 2u (k 0..3 of each lane group) and 2u+1 (k 4..7)
-        const _Float16 w = (_Float16)fast_exp2(sc[i] - m_use);
-        p[i / 8][i % 8] = w;
-        lt += (float)w;
-    }
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
-    st.l = st.l * alpha + lt;
-    st.m = m_new;
-    if (__any(alpha != 1.f)) {
-        float ar[4];
+        for (int i = 1; i < 8 * NS; ++i) mt = fmaxf(mt, sc[i]);
+        mt = row_max4(mt) * c_log2;             // c > 0: the maximum of the scaled scores
+        // The running maximum moves only when the tile's exceeds it by more
+        // than kLazyMax: the weights stay below 2^kLazyMax (fine in fp16,
+        // summed in fp32) and the rescale of O is rare after the first tiles.
+        const float m_new = fmaxf(st[t].m, mt);
+        const bool bump = m_new > st[t].m + kLazyMax;   // also the first finite maximum
+        const float m_run = bump ? m_new : st[t].m;
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        const float alpha = bump ? fast_exp2(st[t].m - m_use) : 1.f;
+        float lt = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ar[e] = __shfl(alpha, 4 * j + e);
+        for (int i = 0; i < 8 * NS; i += 2) {
+            // sub-tile u = i / 8 takes halves 2u (k 0..3 of each lane group) and 2u+1 (k 4..7)
+            const float w0 = fast_exp2(__builtin_fmaf(sc[i], c_log2, -m_use));
+            const float w1 = fast_exp2(__builtin_fmaf(sc[i + 1], c_log2, -m_use));
+            const half2_t_ w = {(_Float16)w0, (_Float16)w1};
+            p[t][i / 8][i % 8] = w[0];
+            p[t][i / 8][i % 8 + 1] = w[1];
+            lt = __builtin_amdgcn_fdot2(w, half2_t_{(_Float16)1.f, (_Float16)1.f}, lt, false);  // the rounded weights
+        }
+        lt = row_sum4(lt);
+        st[t].l = st[t].l * alpha + lt;
+        st[t].m = m_run;
+        if (__any(bump)) {
+            float ar[4];
 #pragma unroll
-        for (int c = 0; c < kDTiles; ++c)
+            for (int e = 0; e < 4; ++e) ar[e] = __shfl(alpha, 4 * j + e);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) st.o[c][e] *= ar[e];
+            for (int c = 0; c < kDTiles; ++c)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) st[t].o[c][e] *= ar[e];
+        }
     }
     // V rows of the lane's 8 tokens of each sub-tile, columns 8n..8n+7; the
     // B operand of d-tile c is element c of each -- an 8 x 8 transpose of
@@ -201,7 +314,10 @@ __device__ __forceinline__ void consume_lds_tile(Softmax& st, const unsigned cha
                              __builtin_amdgcn_perm(vv[3][dw], vv[2][dw], sel),
                              __builtin_amdgcn_perm(vv[5][dw], vv[4][dw], sel),
                              __builtin_amdgcn_perm(vv[7][dw], vv[6][dw], sel)};
-            st.o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p[u], __builtin_bit_cast(half8_t_, b), st.o[c], 0, 0, 0);
+#pragma unroll
+            for (int t = 0; t < kNT; ++t)
+                st[t].o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p[t][u], __builtin_bit_cast(half8_t_, b),
+                                                                    st[t].o[c], 0, 0, 0);
         }
     }
 }
@@ -238,34 +354,48 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
     const int nrow = lane & 15;
     const int jg = lane >> 4;
     if (bad) {                                             // the sequence's rows come out as NaN
-        if (jg == 0 && nrow < rows) {
-            const int r = row0 + nrow;
-            const int64_t orow = ((int64_t)q0 + r / g) * num_heads + (int64_t)kvh * g + r % g;
-            for (int d = 0; d < kD; ++d) out[orow * kD + d] = (_Float16)NAN;
-        }
+        if (jg == 0)
+            for (int t = 0; t < kNT; ++t) {
+                if (16 * t + nrow >= rows) continue;
+                const int r = row0 + 16 * t + nrow;
+                const int64_t orow = ((int64_t)q0 + r / g) * num_heads + (int64_t)kvh * g + r % g;
+                for (int d = 0; d < kD; ++d) out[orow * kD + d] = (_Float16)NAN;
+            }
         return;                                            // uniform: bad depends on the sequence only
     }
     const int n = n_raw, m = m_raw;
     const int base_pos = n - m;
 
-    Rows rw;
-    rw.live = nrow < rows;
-    const int r = row0 + (rw.live ? nrow : 0);
-    rw.pos = base_pos + r / g;
-    half8_t_ qb[4];
-    {
+    // A negative scale is carried by Q's sign (exact in fp16), so that the
+    // scale applied to the scores is positive; scale 0 becomes the least
+    // normal float, whose products with fp16 dot products (below 2^40) leave
+    // every weight exactly 1, as at 0.
+    const bool neg = scale_log2 < 0.f;
+    const float c_log2 = fmaxf(neg ? -scale_log2 : scale_log2, 1.17549435e-38f);
+    Rows rw[kNT];
+    half8_t_ qb[kNT][4];
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+        rw[t].live = 16 * t + nrow < rows;
+        const int r = row0 + 16 * t + (rw[t].live ? nrow : 0);
+        rw[t].pos = base_pos + r / g;
         const _Float16* qrow = q + (((int64_t)q0 + r / g) * num_heads + (int64_t)kvh * g + r % g) * kD;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const u32x4 z = {0u, 0u, 0u, 0u};
-            qb[c] = __builtin_bit_cast(half8_t_, rw.live ? *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * jg) : z);
+            const uint32_t flip = neg ? 0x80008000u : 0u;
+            u32x4 v = rw[t].live ? *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * jg) : z;
+            v ^= u32x4{flip, flip, flip, flip};
+            qb[t][c] = __builtin_bit_cast(half8_t_, v);
         }
     }
     // the workgroup walks the tiles up to its last row's position; a wave
-    // computes only up to its own last row's
+    // computes only up to its own last row's; tiles wholly at or before its
+    // first row's position need no causal mask
     const int wg_rows = min(rows_all - grow0, kRowsPerGroup);
     const int ntiles = (base_pos + (grow0 + wg_rows - 1) / g) / kKvTile + 1;
     const int my_tiles = rows > 0 ? (base_pos + (row0 + rows - 1) / g) / kKvTile + 1 : 0;
+    const int first_pos = base_pos + row0 / g;
 
     const int32_t* trow = tables + (int64_t)s * max_blocks;
     const int64_t slab = (int64_t)B * kD;
@@ -273,47 +403,69 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
     const _Float16* vbase = v_cache + (int64_t)kvh * slab;
     const int64_t blk_stride = (int64_t)num_kv_heads * slab;
 
-    Softmax st;
-    st.m = -INFINITY;
-    st.l = 0.f;
+    Softmax st[kNT];
 #pragma unroll
-    for (int c = 0; c < kDTiles; ++c) st.o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < kNT; ++t) {
+        st[t].m = -INFINITY;
+        st[t].l = 0.f;
+#pragma unroll
+        for (int c = 0; c < kDTiles; ++c) st[t].o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+    }
 
     // Pipeline: tile k is consumed from LDS while tile k+1 waits in
     // registers and tile k+2 is being fetched -- each fetch has two tile
-    // periods to land.  Registers sets R0/R1 alternate; LDS buffers too.
+    // periods to land; the table entries of tile k+3 are read meanwhile.
+    // Register sets R0/R1 alternate; LDS buffers too.  Every step issues
+    // the same loads (tiles past the last one read clamped rows that are
+    // never used), so the waits before a store count only the older tile.
     Staged R0, R1;
-    fetch_tile<B>(R0, 0, n, trow, kbase, vbase, blk_stride, num_blocks);
-    if (ntiles > 1) fetch_tile<B>(R1, 1, n, trow, kbase, vbase, blk_stride, num_blocks);
-    store_tile(R0, lds[0], lds_flags[0]);
+    int32_t e[kStageRows] = {};
+    if constexpr (B >= 4) table_entries<B>(e, 0, wave, n, trow);
+    fetch_tile<B>(R0, 0, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
+    if constexpr (B >= 4) table_entries<B>(e, 1, wave, n, trow);
+    fetch_tile<B>(R1, 1, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
+    if constexpr (B >= 4) table_entries<B>(e, 2, wave, n, trow);
+    store_tile(R0, lds[0], lds_flags[0], wave, lane);
     __syncthreads();
     auto step = [&](int k, Staged& fetch_into, const Staged& next) {
         const int cur = k & 1;
-        if (k + 2 < ntiles) fetch_tile<B>(fetch_into, k + 2, n, trow, kbase, vbase, blk_stride, num_blocks);
-        if (k < my_tiles) consume_lds_tile(st, lds[cur], lds_flags[cur], k * kKvTile, qb, scale_log2, lane, rw);
-        if (k + 1 < ntiles) store_tile(next, lds[cur ^ 1], lds_flags[cur ^ 1]);
+        fetch_tile<B>(fetch_into, k + 2, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
+        if constexpr (B >= 4) table_entries<B>(e, k + 3, wave, n, trow);
+        if (k < my_tiles) {
+            // uniform: tile below the wave's first row and wholly valid
+            bool interior = k * kKvTile + kKvTile - 1 <= first_pos;
+            if (interior) {
+                const uint32_t f0 = *reinterpret_cast<const uint32_t*>(lds_flags[cur] + 4 * jg);
+                const uint32_t f1 = *reinterpret_cast<const uint32_t*>(lds_flags[cur] + 16 + 4 * jg);
+                interior = __all(f0 == 0x01010101u && f1 == 0x01010101u);
+            }
+            consume_lds_tile(st, lds[cur], lds_flags[cur], k * kKvTile, interior, qb, c_log2, lane, rw);
+        }
+        store_tile(next, lds[cur ^ 1], lds_flags[cur ^ 1], wave, lane);
         __syncthreads();
     };
-    for (int k = 0; k < ntiles; k += 2) {
+    for (int k = 0; k < ntiles; k += 2) {   // an odd count runs one idle step at the end
         step(k, R0, R1);                    // R0 (tile k, now in LDS) refills with k+2; R1 holds k+1
-        if (k + 1 < ntiles) step(k + 1, R1, R0);
+        step(k + 1, R1, R0);
     }
 
-    // Rows 4*jg + e of the wave live in this lane's o[c][e] at column 8*nrow
-    // + c; their sums sit in lanes 4*jg + e.
+    // Rows 16t + 4*jg + e of the wave live in this lane's st[t].o[c][e] at
+    // column 8*nrow + c; their sums sit in lanes 4*jg + e.
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int rr = 4 * jg + e;
-        const float L = __shfl(st.l, rr);
-        if (rr >= rows) continue;
-        const int rwi = row0 + rr;
-        const int64_t orow = ((int64_t)q0 + rwi / g) * num_heads + (int64_t)kvh * g + rwi % g;
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        half8_t h;
+    for (int t = 0; t < kNT; ++t)
 #pragma unroll
-        for (int c = 0; c < kDTiles; ++c) h[c] = (_Float16)(st.o[c][e] * inv);
-        *reinterpret_cast<half8_t*>(out + orow * kD + 8 * nrow) = h;
-    }
+        for (int e = 0; e < 4; ++e) {
+            const int rr = 4 * jg + e;
+            const float L = __shfl(st[t].l, rr);
+            if (16 * t + rr >= rows) continue;
+            const int rwi = row0 + 16 * t + rr;
+            const int64_t orow = ((int64_t)q0 + rwi / g) * num_heads + (int64_t)kvh * g + rwi % g;
+            const float inv = L > 0.f ? 1.f / L : 0.f;
+            half8_t h;
+#pragma unroll
+            for (int c = 0; c < kDTiles; ++c) h[c] = (_Float16)(st[t].o[c][e] * inv);
+            *reinterpret_cast<half8_t*>(out + orow * kD + 8 * nrow) = h;
+        }
 }
 
 using PrefillFn = void (*)(_Float16*, const _Float16*, int32_t, const _Float16*, const _Float16*, const int32_t*,

@@ -93,6 +93,55 @@ def test_prefill_edge_rows_and_bad_sequences():
     assert np.all(bits(out3)[65:70] == 0)
 
 
+@pytest.mark.parametrize("sign", [-1.0, 0.0])
+def test_prefill_negative_and_zero_scale(sign):
+    """A negative scale flips every score (the kernel carries the sign on
+    Q); scale 0 gives the plain mean of the visible values."""
+    dev = device()
+    case = workloads.random_case(51, [300, 64, 129], 4, 2, 128, 16)
+    kc, vc, tables, lens = _oracle_cache(case)
+    q, qs = _queries(51, [300, 20, 129], 4, 128)
+    scale = sign * case.scale
+    out = _gpu_prefill(dev, q, kc, vc, tables, lens, qs, scale)
+    ref = oracle.prefill(q, kc, vc, tables, lens, qs, scale)
+    assert_attention_close(out, ref, f"scale {scale}")
+
+
+def test_prefill_skips_table_entries_outside_the_pool():
+    """A block id outside the pool drops its tokens from every row that
+    would see them, also inside tiles that lie wholly before a row."""
+    dev = device()
+    n = 200
+    case = workloads.random_case(61, [n], 2, 2, 128, 16)
+    kc, vc, tables, lens = _oracle_cache(case)
+    bad = tables.copy()
+    bad[0, 2] = case.num_blocks + 3                  # tokens 32..47 drop out
+    q, qs = _queries(61, [n], 2, 128)
+    out = _gpu_prefill(dev, q, kc, vc, bad, lens, qs, case.scale)
+    kept = np.array([p for p in range(n) if not 32 <= p < 48])
+    k = np.ascontiguousarray(case.k_tokens[kept])
+    v = np.ascontiguousarray(case.v_tokens[kept])
+    seen = np.array([int(np.sum(kept <= i)) for i in range(n)], np.int32)   # row i sits at position i
+    ref = oracle.attention_contig(q, k, v, np.zeros(n, np.int64), seen, case.scale)
+    assert_attention_close(out, ref, "skipped ids")
+
+
+def test_prefill_rising_scores_move_the_running_maximum():
+    """K rows grow along the context (x0.2 .. x20), so each row's maximum
+    climbs by many octaves over its tiles: the lazily moved running
+    maximum and the rescale of O are exercised over and over."""
+    dev = device()
+    n = 700
+    case = workloads.random_case(71, [n], 4, 2, 128, 16)
+    grow = (0.2 + 19.8 * np.arange(n) / n).astype(np.float32)
+    case.k_tokens[:] = (case.k_tokens.astype(np.float32) * grow[:, None, None]).astype(np.float16)
+    kc, vc, tables, lens = _oracle_cache(case)
+    q, qs = _queries(71, [n], 4, 128)
+    out = _gpu_prefill(dev, q, kc, vc, tables, lens, qs, case.scale)
+    ref = oracle.prefill(q, kc, vc, tables, lens, qs, case.scale)
+    assert_attention_close(out, ref, "rising scores")
+
+
 def test_prefill_is_deterministic_and_blind_to_placement():
     dev = device()
     case = workloads.random_case(41, [300, 64, 129], 8, 2, 128, 16, spare_blocks=30)
