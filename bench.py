@@ -17,9 +17,13 @@ One step = one decode iteration over the whole path:
 
 Printed: one JSON line.  `value` is KV GB/s over the whole step (bytes of
 cached K/V that decode must read, summed over layers, divided by wall time per
-step); `roofline` is the decode call alone, timed with HIP events on the
-launch stream; `cpu_baseline` times the fp64 oracle on one layer of the same
-workload on the host cores.
+step; no events inside the steps -- on this stack each recorded event costs
+several microseconds between kernels); `roofline` is the decode call alone:
+after the timed steps, --steps sweeps of pa_decode over the layers of the last
+step's batch run back to back, bracketed by HIP events on the launch stream,
+and the average call duration divides the call's algorithmic KV bytes;
+`cpu_baseline` times the fp64 oracle on one layer of the same workload on the
+host cores.
 """
 from __future__ import annotations
 
@@ -182,7 +186,7 @@ def main():
 
     kv_per_token = 2 * Hkv * D * 2           # K and V, fp16, one layer
 
-    def step(i, ev=None):
+    def step(i):
         b = i % nbuf
         if copied[b] is not None:
             copied[b].synchronize()          # the pinned buffer's previous upload has been consumed
@@ -199,25 +203,21 @@ def main():
         copied[b] = e
         for l in range(L):
             pa.pa_reshape_and_cache(key, val, d_slots, kcs[l], vcs[l])
-            if ev is not None:
-                ev[l][0].record(stream)
             pa.pa_decode(out, q, kcs[l], vcs[l], d_tables, d_lens, w.scale, B, max_context_len=width * B,
                          partition_size=part, workspace=workspace)
-            if ev is not None:
-                ev[l][1].record(stream)
         return ctx
 
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
 
-    events = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(L)]
-              for _ in range(K)]
     ctx_sum = 0
+    ctx_last = 0
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        ctx_sum += step(W + i, events[i])
+        ctx_last = step(W + i)
+        ctx_sum += ctx_last
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
@@ -225,14 +225,26 @@ def main():
     ms_per_step = wall / K * 1e3
     kv_bytes_total = ctx_sum * kv_per_token * L          # over the K timed steps
     value = kv_bytes_total / wall / 1e9
-    dec_ms = [events[i][l][0].elapsed_time(events[i][l][1]) for i in range(K) for l in range(L)]
-    dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
-    kv_per_launch = ctx_sum / K * kv_per_token
-    achieved = kv_per_launch / dec_avg_s / 1e9
     tokens_per_s_layer = S * L / (wall / K)
-    log(f"[bench] step {ms_per_step:.3f} ms ({L} layers); decode call avg {dec_avg_s * 1e6:.1f} us "
-        f"= {achieved:.0f} GB/s ({100 * achieved / HBM_PEAK_GBS:.1f}% of peak); "
-        f"min {min(dec_ms) * 1e3:.1f} us max {max(dec_ms) * 1e3:.1f} us")
+
+    # ---- the decode call alone: K sweeps over the layers of the last step's
+    # batch, back to back, events only between sweeps
+    sweep_ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    sweep_ev[0].record(stream)
+    for i in range(K):
+        for l in range(L):
+            pa.pa_decode(out, q, kcs[l], vcs[l], d_tables, d_lens, w.scale, B, max_context_len=width * B,
+                         partition_size=part, workspace=workspace)
+        sweep_ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    dec_ms = [sweep_ev[i].elapsed_time(sweep_ev[i + 1]) / L for i in range(K)]
+    dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
+    kv_per_launch = ctx_last * kv_per_token
+    achieved = kv_per_launch / dec_avg_s / 1e9
+    log(f"[bench] step {ms_per_step:.3f} ms ({L} layers) = {value:.0f} GB/s ({100 * value / HBM_PEAK_GBS:.1f}% of "
+        f"peak); decode call avg {dec_avg_s * 1e6:.1f} us = {achieved:.0f} GB/s "
+        f"({100 * achieved / HBM_PEAK_GBS:.1f}% of peak); per-sweep call avg min {min(dec_ms) * 1e3:.1f} us "
+        f"max {max(dec_ms) * 1e3:.1f} us")
 
     # ---- oracle on the host cores, same workload (layer 0, one decode)
     cpu = None
