@@ -122,8 +122,13 @@ int pa_reshape_and_cache(const void *key, const void *value,
  *                  a default).  Sequences longer than one partition are split
  *                  across workgroups and merged by a second kernel.
  *   workspace      device scratch of at least pa_decode_workspace_size()
- *                  bytes, or NULL when that size is 0.  Contents on entry are
- *                  ignored; calls sharing a workspace must be stream-ordered.
+ *                  bytes, 16-byte aligned.  It holds the longest-first order
+ *                  in which the sequences are dispatched (written by a small
+ *                  kernel launched first) and, when a sequence is split, the
+ *                  partial results.  With one partition it may be NULL (or
+ *                  smaller): the sequences then run in index order, with the
+ *                  same results.  Contents on entry are ignored; calls
+ *                  sharing a workspace must be stream-ordered.
  * Table entries outside [0, num_blocks) are skipped: their tokens take no
  * part in the softmax.
  * ------------------------------------------------------------------------ */
@@ -160,7 +165,7 @@ int pa_decode(void *out, const void *q, const void *k_cache,
  *                  sequence with m_s > max_query_len, m_s > n_s or n_s beyond
  *                  its table gets its first max_query_len rows as NaN.
  * head_dim 128 only (PA_ERR_UNSUPPORTED otherwise); any num_heads multiple of
- * num_kv_heads.  Runs on the matrix cores (v_mfma_f32_16x16x16_f16, fp32
+ * num_kv_heads.  Runs on the matrix cores (v_mfma_f32_16x16x32_f16, fp32
  * accumulation); no workspace.
  * ------------------------------------------------------------------------ */
 int pa_prefill(void *out, const void *q, int32_t num_tokens,
@@ -172,18 +177,23 @@ int pa_prefill(void *out, const void *q, int32_t num_tokens,
                float scale, int32_t max_query_len, int32_t dtype,
                void *stream);
 
-/* Bytes of workspace pa_decode needs for these sizes (0 when every sequence
- * fits one partition).  partition_size as for pa_decode (0 = default).
- * Returns (size_t)-1 for invalid arguments. */
+/* Bytes of workspace pa_decode uses for these sizes: the dispatch order
+ * (4 bytes per sequence, rounded up to 256; none for a single sequence) plus,
+ * when a sequence can span several partitions, the partial results.
+ * partition_size as for pa_decode (0 = default).  Returns (size_t)-1 for
+ * invalid arguments. */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
                                 int32_t num_kv_heads, int32_t head_dim,
                                 int32_t block_size, int32_t max_context_len,
                                 int32_t partition_size);
 
-/* The partition size pa_decode uses when given 0: the longest of 2048,
- * 1024, 512 and 256 tokens that still gives the launch at least four
- * workgroups per resident workgroup slot of the kernel that serves these
- * shapes.  -1 for invalid arguments. */
+/* The partition size pa_decode uses when given 0.  With rows =
+ * num_seqs x num_heads (x num_kv_heads on the matrix-core path) and slots =
+ * the resident workgroups of the kernel that serves these shapes (1024, or
+ * 512 on the matrix-core path): 2048 when rows >= 2 x slots; otherwise the
+ * longest of 2048, 1024, 512 and 256 tokens that gives at least four
+ * workgroups per slot counting full partitions of a max_context_len
+ * sequence; 256 when none does.  -1 for invalid arguments. */
 int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_heads,
                                     int32_t num_kv_heads, int32_t head_dim,
                                     int32_t block_size,

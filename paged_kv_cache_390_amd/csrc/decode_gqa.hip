@@ -58,13 +58,13 @@ constexpr int kThreads = kWaves * 64;
 template <int B>
 __global__ void __launch_bounds__(kThreads)
 decode_gqa_mfma_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
-                       const _Float16* __restrict__ q, const _Float16* __restrict__ k_cache,
+                       const int32_t* __restrict__ order, const _Float16* __restrict__ q, const _Float16* __restrict__ k_cache,
                        const _Float16* __restrict__ v_cache, const int32_t* __restrict__ tables,
                        int32_t max_blocks, const int32_t* __restrict__ lens, int32_t num_heads,
                        int32_t num_kv_heads, int32_t num_blocks, float scale_log2, int32_t part_size,
                        int32_t num_parts, int64_t len_cap) {
     const int kvh = blockIdx.x;
-    const int s = blockIdx.y;
+    const int s = order ? order[blockIdx.y] : (int)blockIdx.y;   // longest sequences first
     const int part = blockIdx.z;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -104,27 +104,33 @@ decode_gqa_mfma_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, fl
         Tile A, Bt;
         if constexpr (B >= kTile) {
             // One table entry per tile, read with scalar loads a tile ahead of
-            // its use; three tiles in flight per wave (A, Bt, C rotate).
-            Tile C;
-            auto entry = [&](int stp) { return trow[(start + stp * kTile) / B]; };
+            // its issue; three tiles in flight per wave beside the one being
+            // consumed (A, Bt, C, D rotate).  Every step issues a tile -- past
+            // the last step one that is never consumed, every lane reading the
+            // same 16 bytes of the last tile's block (one cache line per load)
+            // -- so the count of loads is the same on every path and the wait
+            // before a consume leaves the three newer tiles in flight.
+            Tile C, D;
+            auto clamp = [&](int stp) { return stp < nsteps ? stp : nsteps - 1; };
+            auto entry = [&](int stp) { return trow[(start + clamp(stp) * kTile) / B]; };
             auto issue = [&](Tile& t, int stp, int32_t phys) {
-                load_tile_block<B>(t, start + stp * kTile, end, phys, kbase, vbase, blk_stride, num_blocks, lane);
+                load_tile_block<B>(t, start + clamp(stp) * kTile, end, phys, kbase, vbase, blk_stride, num_blocks,
+                                   stp < nsteps ? lane : 0);
             };
             int stp = wave;
             issue(A, stp, entry(stp));
-            if (stp + kWaves < nsteps) issue(Bt, stp + kWaves, entry(stp + kWaves));
-            int32_t tnext = stp + 2 * kWaves < nsteps ? entry(stp + 2 * kWaves) : 0;
-            // before each consume: the tile 2 steps ahead is issued, the entry 3 steps ahead read
+            issue(Bt, stp + kWaves, entry(stp + kWaves));
+            issue(C, stp + 2 * kWaves, entry(stp + 2 * kWaves));
+            int32_t tnext = entry(stp + 3 * kWaves);
+            // before each consume: the tile 3 steps ahead is issued, the entry 4 steps ahead read
             auto advance = [&](Tile& t, int st) {
-                const int ahead = st + 2 * kWaves;
-                if (ahead < nsteps) {
-                    const int32_t cur = tnext;
-                    tnext = ahead + kWaves < nsteps ? entry(ahead + kWaves) : 0;
-                    issue(t, ahead, cur);
-                }
+                const int ahead = st + 3 * kWaves;
+                const int32_t cur = tnext;
+                tnext = entry(ahead + kWaves);
+                issue(t, ahead, cur);
             };
             for (;;) {
-                advance(C, stp);
+                advance(D, stp);
                 consume_tile(st, A, qb, scale_log2, lane, A.valid);
                 stp += kWaves;
                 if (stp >= nsteps) break;
@@ -134,6 +140,10 @@ decode_gqa_mfma_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, fl
                 if (stp >= nsteps) break;
                 advance(Bt, stp);
                 consume_tile(st, C, qb, scale_log2, lane, C.valid);
+                stp += kWaves;
+                if (stp >= nsteps) break;
+                advance(C, stp);
+                consume_tile(st, D, qb, scale_log2, lane, D.valid);
                 stp += kWaves;
                 if (stp >= nsteps) break;
             }
@@ -203,7 +213,7 @@ decode_gqa_mfma_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, fl
     }
 }
 
-using GqaFn = void (*)(_Float16*, float*, float*, const _Float16*, const _Float16*, const _Float16*,
+using GqaFn = void (*)(_Float16*, float*, float*, const int32_t*, const _Float16*, const _Float16*, const _Float16*,
                        const int32_t*, int32_t, const int32_t*, int32_t, int32_t, int32_t, float, int32_t,
                        int32_t, int64_t);
 
@@ -232,7 +242,7 @@ bool gqa_mfma_supported(int32_t head_dim, int32_t block_size, int32_t group) {
 hipError_t launch_gqa_mfma(const DecodeLaunch& a) {
     GqaFn fn = pick(a.block_size);
     hipLaunchKernelGGL(fn, dim3((unsigned)a.num_kv_heads, (unsigned)a.num_seqs, (unsigned)a.num_parts),
-                       dim3(kThreads), 0, a.stream, a.out, a.ws_ml, a.ws_acc, a.q, a.k_cache, a.v_cache,
+                       dim3(kThreads), 0, a.stream, a.out, a.ws_ml, a.ws_acc, a.order, a.q, a.k_cache, a.v_cache,
                        a.tables, a.max_blocks, a.lens, a.num_heads, a.num_kv_heads, a.num_blocks, a.scale_log2,
                        a.part_size, a.num_parts, a.len_cap);
     return hipGetLastError();

@@ -10,10 +10,13 @@ namespace pa {
 
 // Everything one pa_decode partition-kernel launch needs; pointers are
 // device pointers, the workspace pointers null when no sequence is split.
+// `order` (null: grid order) lists the sequences longest first: grid row y
+// works on sequence order[y].
 struct DecodeLaunch {
     _Float16* out;
     float* ws_ml;
     float* ws_acc;
+    const int32_t* order;
     const _Float16* q;
     const _Float16* k_cache;
     const _Float16* v_cache;

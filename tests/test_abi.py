@@ -74,10 +74,12 @@ def test_decode_with_no_sequences_is_a_no_op():
 
 def test_workspace_size():
     L = pa.lib()
-    assert L.pa_decode_workspace_size(64, 32, 32, 128, 16, 512, 512) == 0        # one partition
+    assert L.pa_decode_workspace_size(64, 32, 32, 128, 16, 512, 512) == 256      # one partition: the order only
+    assert L.pa_decode_workspace_size(65, 32, 32, 128, 16, 512, 512) == 512
+    assert L.pa_decode_workspace_size(1, 32, 32, 128, 16, 512, 512) == 0         # one sequence: nothing to order
     n = L.pa_decode_workspace_size(64, 32, 32, 128, 16, 2048, 512)
     rows = 64 * 32 * 4
-    assert n >= rows * (128 + 2) * 4 and n % 256 == 0
+    assert n >= 256 + rows * (128 + 2) * 4 and n % 256 == 0
     assert L.pa_decode_workspace_size(64, 32, 32, 100, 16, 2048, 512) == ctypes.c_size_t(-1).value
     assert L.pa_decode_workspace_size(64, 32, 32, 128, 16, 2048, 100) == ctypes.c_size_t(-1).value
     assert L.pa_decode_workspace_size(64, 32, 5, 128, 16, 2048, 512) == ctypes.c_size_t(-1).value
@@ -85,18 +87,21 @@ def test_workspace_size():
 
 
 def test_default_partition_keeps_the_gpu_busy():
-    """The longest of 2048/1024/512/256 tokens with >= 4 workgroups per
-    resident slot (1024 slots for one query per KV head, 512 for groups of
-    2..16 at head_dim 128), counting full partitions of the longest
-    sequence; 256 when even that is not reached."""
+    """2048 when one workgroup per row (sequence x query head, or x KV head
+    on the grouped path) fills the resident slots twice (1024 slots for one
+    query per KV head, 512 for groups of 2..16 at head_dim 128); otherwise
+    the longest of 2048/1024/512/256 tokens with >= 4 workgroups per slot,
+    counting full partitions of the longest sequence; 256 when even that is
+    not reached."""
     L = pa.lib()
-    assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2048) == 1024      # 2048 rows x 2
-    assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2112) == 1024
-    assert L.pa_decode_default_partition(256, 64, 8, 128, 16, 2048) == 2048     # grouped: 2048 rows x 1
+    assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2048) == 2048     # 2048 rows = 2 x 1024
+    assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 8192) == 2048
+    assert L.pa_decode_default_partition(63, 32, 32, 128, 16, 2048) == 512      # 2016 rows x 4 partitions
+    assert L.pa_decode_default_partition(256, 64, 8, 128, 16, 2048) == 2048     # grouped: 2048 rows, 512 slots
     assert L.pa_decode_default_partition(64, 64, 8, 128, 16, 2048) == 512       # 512 rows x 4
     assert L.pa_decode_default_partition(16, 32, 32, 128, 16, 4096) == 512      # 512 rows x 8
     assert L.pa_decode_default_partition(1, 8, 8, 128, 16, 1000) == 256
-    assert L.pa_decode_default_partition(64, 32, 32, 64, 16, 2048) == 1024      # head_dim 64: vector kernel
+    assert L.pa_decode_default_partition(64, 32, 32, 64, 16, 2048) == 2048      # head_dim 64: vector kernel
     assert L.pa_decode_default_partition(64, 32, 7, 128, 16, 2048) == -1
     for args in [(64, 32, 32, 128, 16, 2048), (256, 64, 8, 128, 16, 2048), (1, 8, 8, 128, 16, 1000)]:
         assert L.pa_decode_default_partition(*args) % 128 == 0

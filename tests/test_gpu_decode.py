@@ -135,6 +135,31 @@ def test_deterministic_and_blind_to_physical_placement():
     assert np.array_equal(bits(a), bits(c))
 
 
+@pytest.mark.parametrize("H,Hkv", [(8, 8), (8, 1)])
+def test_longest_first_order_changes_no_bit(H, Hkv):
+    """With one partition the workspace only carries the longest-first
+    dispatch order; without it (NULL) the sequences run in index order.
+    Both give the same bits, and both match the oracle."""
+    dev = device()
+    rng = np.random.default_rng(17)
+    lens_l = [int(x) for x in rng.integers(0, 2049, size=40)]
+    case = workloads.random_case(77 + Hkv, lens_l, H, Hkv, 128, 16)
+    kc, vc, tables, lens = _oracle_cache(case)
+    ordered = _gpu_decode(dev, case.q, kc, vc, tables, lens, case.scale, partition_size=2048, max_context_len=2048)
+    S, D = len(lens_l), 128
+    d_q, d_k, d_v = (torch.from_numpy(x).to(dev) for x in (case.q, kc, vc))
+    d_t, d_l = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
+    plain = torch.full((S, H, D), float("nan"), dtype=torch.float16, device=dev)
+    rc = pa.lib().pa_decode(plain.data_ptr(), d_q.data_ptr(), d_k.data_ptr(), d_v.data_ptr(), d_t.data_ptr(),
+                            tables.shape[1], d_l.data_ptr(), S, H, Hkv, D, 16, case.num_blocks, case.scale, 2048,
+                            2048, None, 0, pa.PA_DTYPE_F16, None)
+    assert rc == pa.PA_OK
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(ordered), bits(plain))
+    ref = oracle.decode(case.q, kc, vc, tables, lens, case.scale)
+    assert_attention_close(ordered, ref, f"ordered H={H}/{Hkv}")
+
+
 def test_workspace_reused_across_calls_of_different_sizes():
     """One workspace serves calls of different sizes and partition counts
     (its contents on entry are ignored).  Outputs start as NaN, so a row
