@@ -11,6 +11,8 @@ One step = one decode iteration over the whole path:
   host   the C++ block manager appends one token to every sequence (a new
          block when the last one is full) and packs tables / lengths / slots;
   H2D    the packed arrays go to the device (pinned, asynchronous);
+  order  pa_decode_order sorts the sequences longest first (one small
+         kernel, shared by every layer of the step);
   per layer (x32)
          pa_reshape_and_cache writes the new token's K/V,
          pa_decode runs attention for all 64 sequences.
@@ -69,7 +71,7 @@ def parse():
     return p.parse_args()
 
 
-KERNEL_SOURCES = {"llama7b": ("decode.hip",), "gqa": ("decode.hip", "decode_gqa.hip")}
+KERNEL_SOURCES = {"llama7b": ("decode.hip",), "gqa": ("decode.hip", "decode_gqa.hip", "mfma_tile.h")}
 
 
 def kernel_source_hash(workload: str) -> str:
@@ -182,6 +184,7 @@ def main():
     d_slots = torch.empty(S, dtype=torch.int64, device=dev)
     copied = [None] * nbuf
     out = torch.empty((S, H, D), dtype=torch.float16, device=dev)
+    d_order = torch.empty(S, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     kv_per_token = 2 * Hkv * D * 2           # K and V, fp16, one layer
@@ -201,10 +204,11 @@ def main():
         e = torch.cuda.Event()
         e.record(stream)
         copied[b] = e
+        pa.pa_decode_order(d_lens, width * B, out=d_order)     # one dispatch order for every layer
         for l in range(L):
             pa.pa_reshape_and_cache(key, val, d_slots, kcs[l], vcs[l])
             pa.pa_decode(out, q, kcs[l], vcs[l], d_tables, d_lens, w.scale, B, max_context_len=width * B,
-                         partition_size=part, workspace=workspace)
+                         partition_size=part, workspace=workspace, seq_order=d_order)
         return ctx
 
     for i in range(W):
@@ -234,7 +238,7 @@ def main():
     for i in range(K):
         for l in range(L):
             pa.pa_decode(out, q, kcs[l], vcs[l], d_tables, d_lens, w.scale, B, max_context_len=width * B,
-                         partition_size=part, workspace=workspace)
+                         partition_size=part, workspace=workspace, seq_order=d_order)
         sweep_ev[i + 1].record(stream)
     torch.cuda.synchronize()
     dec_ms = [sweep_ev[i].elapsed_time(sweep_ev[i + 1]) / L for i in range(K)]
@@ -287,7 +291,7 @@ def main():
         "config": {"workload": wl_name, "batch": S, "block_size": B, "num_heads": H, "num_kv_heads": Hkv,
                    "head_dim": D, "context": ctx_desc, "layers_resident": L, "pool_blocks_per_layer": NB,
                    "partition_size": part or pa.pa_decode_default_partition(S, H, Hkv, D, B, width * B),
-                   "step": "host append+tables, H2D, per layer reshape_and_cache + decode"},
+                   "step": "host append+tables, H2D, decode order, per layer reshape_and_cache + decode"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "cpu_baseline": cpu,

@@ -122,13 +122,21 @@ int pa_reshape_and_cache(const void *key, const void *value,
  *                  a default).  Sequences longer than one partition are split
  *                  across workgroups and merged by a second kernel.
  *   workspace      device scratch of at least pa_decode_workspace_size()
- *                  bytes, 16-byte aligned.  It holds the longest-first order
- *                  in which the sequences are dispatched (written by a small
- *                  kernel launched first) and, when a sequence is split, the
- *                  partial results.  With one partition it may be NULL (or
- *                  smaller): the sequences then run in index order, with the
- *                  same results.  Contents on entry are ignored; calls
- *                  sharing a workspace must be stream-ordered.
+ *                  bytes, 16-byte aligned.  It holds the partial results
+ *                  when a sequence is split and, when seq_order is NULL, the
+ *                  longest-first dispatch order (written by a small kernel
+ *                  launched first).  With one partition it may be NULL (or
+ *                  smaller): without seq_order the sequences then run in
+ *                  index order, with the same results.  Contents on entry are
+ *                  ignored; calls sharing a workspace must be stream-ordered.
+ *   seq_order      device, int32 [num_seqs], or NULL: the order in which
+ *                  the sequences are dispatched, as pa_decode_order writes
+ *                  it (longest first, so that no long sequence starts last
+ *                  and runs alone at the end).  Every layer of a step shares
+ *                  one order: computing it once per step saves the small
+ *                  kernel on every call.  The order never changes a result;
+ *                  an entry outside [0, num_seqs) is skipped, and a sequence
+ *                  the array leaves out keeps its output rows untouched.
  * Table entries outside [0, num_blocks) are skipped: their tokens take no
  * part in the softmax.
  * ------------------------------------------------------------------------ */
@@ -138,8 +146,16 @@ int pa_decode(void *out, const void *q, const void *k_cache,
               int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
               int32_t head_dim, int32_t block_size, int32_t num_blocks,
               float scale, int32_t max_context_len, int32_t partition_size,
-              void *workspace, size_t workspace_bytes, int32_t dtype,
-              void *stream);
+              void *workspace, size_t workspace_bytes,
+              const int32_t *seq_order, int32_t dtype, void *stream);
+
+/* Longest-first dispatch order for pa_decode: seq_order (device, int32
+ * [num_seqs], written) becomes a permutation of 0 .. num_seqs - 1 with the
+ * sequences sorted by context_lens into 1024 classes of
+ * max_context_len / 1024 + 1 tokens, longest class first (order within a
+ * class unspecified).  Stream-ordered with the calls that use it. */
+int pa_decode_order(int32_t *seq_order, const int32_t *context_lens,
+                    int32_t num_seqs, int32_t max_context_len, void *stream);
 
 /* ------------------------------------------------------------------------
  * Paged prefill / chunked prefill: several new tokens per sequence, each

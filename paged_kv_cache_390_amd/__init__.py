@@ -9,7 +9,7 @@ current HIP stream.  There is no fallback: if the library is not built, every
 call raises.
 
 Functions carry the C names: ``pa_reshape_and_cache``, ``pa_decode``,
-``pa_decode_workspace_size``, ``pa_prefill``, ``pa_copy_blocks``, ``pa_swap_blocks``;
+``pa_decode_order``, ``pa_decode_workspace_size``, ``pa_prefill``, ``pa_copy_blocks``, ``pa_swap_blocks``;
 ``BlockManager`` wraps the ``pa_bm_*`` calls.
 """
 from __future__ import annotations
@@ -63,10 +63,11 @@ def lib() -> ctypes.CDLL:
     sig = {
         "pa_last_error": ([], ctypes.c_char_p),
         "pa_reshape_and_cache": ([P, P, i64, P, i32, P, P, i32, i32, i32, i32, i32, P], ctypes.c_int),
-        "pa_decode": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P, sz, i32, P],
+        "pa_decode": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P, sz, P, i32, P],
                       ctypes.c_int),
         "pa_prefill": ([P, P, i32, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P],
                        ctypes.c_int),
+        "pa_decode_order": ([P, P, i32, i32, P], ctypes.c_int),
         "pa_decode_workspace_size": ([i32, i32, i32, i32, i32, i32, i32], sz),
         "pa_decode_default_partition": ([i32, i32, i32, i32, i32, i32], i32),
         "pa_copy_blocks": ([P, P, i32, P, i32, i32, i64, i32, P], ctypes.c_int),
@@ -192,13 +193,15 @@ def pa_decode_default_partition(num_seqs: int, num_heads: int, num_kv_heads: int
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
               block_size: Optional[int] = None, max_context_len: Optional[int] = None,
-              partition_size: int = 0, workspace=None) -> None:
+              partition_size: int = 0, workspace=None, seq_order=None) -> None:
     """out[S, H, D] = softmax(scale * K q) V for each sequence over its first
     context_lens[s] cached tokens, found through block_tables[S, W].
 
     max_context_len defaults to W * block_size (a bound known without reading
     context_lens back).  workspace (a uint8 device tensor) is allocated from
-    torch's caching allocator when needed and not given."""
+    torch's caching allocator when needed and not given.  seq_order (int32
+    device tensor [S], from pa_decode_order) is the dispatch order shared by
+    the layers of a step; without it pa_decode computes one per call."""
     torch = _torch()
     _dev_tensor(k_cache, "k_cache", torch.float16, 4)
     _dev_tensor(v_cache, "v_cache", torch.float16, 4)
@@ -226,10 +229,33 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
         _dev_tensor(workspace, "workspace", torch.uint8, 1)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    order_ptr = None
+    if seq_order is not None:
+        _dev_tensor(seq_order, "seq_order", torch.int32, 1)
+        if seq_order.shape[0] != S:
+            raise ValueError("seq_order must have one entry per sequence")
+        order_ptr = seq_order.data_ptr()
     _check(lib().pa_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                            block_tables.data_ptr(), W, context_lens.data_ptr(), S, H, Hkv, D, B, NB,
                            float(scale), int(max_context_len), int(partition_size), ws_ptr, ws_bytes,
-                           PA_DTYPE_F16, _stream(q.device)), "pa_decode")
+                           order_ptr, PA_DTYPE_F16, _stream(q.device)), "pa_decode")
+
+
+def pa_decode_order(context_lens, max_context_len: int, out=None):
+    """Longest-first dispatch order of the sequences (int32 device tensor
+    [S]) for pa_decode's seq_order; compute it once per step, after
+    context_lens is final, and pass it to every layer."""
+    torch = _torch()
+    _dev_tensor(context_lens, "context_lens", torch.int32, 1)
+    S = context_lens.shape[0]
+    if out is None:
+        out = torch.empty(S, dtype=torch.int32, device=context_lens.device)
+    _dev_tensor(out, "out", torch.int32, 1)
+    if out.shape[0] != S:
+        raise ValueError("out must have one entry per sequence")
+    _check(lib().pa_decode_order(out.data_ptr(), context_lens.data_ptr(), S, int(max_context_len),
+                                 _stream(context_lens.device)), "pa_decode_order")
+    return out
 
 
 def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float,

@@ -179,6 +179,7 @@ decode_partition_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, f
 
     const int h = blockIdx.x;
     const int s = order ? order[blockIdx.y] : (int)blockIdx.y;   // longest sequences first
+    if ((uint32_t)s >= gridDim.y) return;                         // not a sequence: nothing to do
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform by construction
     const int row = lane / LPT;
@@ -351,10 +352,12 @@ decode_partition_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, f
 template <int D>
 __global__ void __launch_bounds__(D < 64 ? 64 : D)
 decode_reduce_kernel(_Float16* __restrict__ out, const float* __restrict__ ws_ml,
-                     const float* __restrict__ ws_acc, const int32_t* __restrict__ lens,
-                     int32_t num_heads, int32_t part_size, int32_t num_parts, int64_t len_cap) {
+                     const float* __restrict__ ws_acc, const int32_t* __restrict__ order,
+                     const int32_t* __restrict__ lens, int32_t num_heads, int32_t part_size, int32_t num_parts,
+                     int64_t len_cap) {
     const int h = blockIdx.x;
-    const int s = blockIdx.y;
+    const int s = order ? order[blockIdx.y] : (int)blockIdx.y;   // the sequences the first kernel did
+    if ((uint32_t)s >= gridDim.y) return;
     const int32_t n = lens[s];
     if (n < 0 || (int64_t)n > len_cap) return;   // written as NaN by the first kernel
     const int np = (n + part_size - 1) / part_size;
@@ -422,6 +425,11 @@ order_by_length_kernel(int32_t* __restrict__ order, const int32_t* __restrict__ 
     for (int s = t; s < num_seqs; s += kOrderClasses) order[atomicAdd(&count[cls(lens[s])], 1)] = s;
 }
 
+void launch_order(int32_t* order, const int32_t* lens, int32_t num_seqs, int32_t max_context_len, hipStream_t st) {
+    const int32_t width = max_context_len / kOrderClasses + 1;
+    hipLaunchKernelGGL(order_by_length_kernel, dim3(1), dim3(kOrderClasses), 0, st, order, lens, num_seqs, width);
+}
+
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace: the longest-first sequence order (int32 per sequence, when
@@ -454,8 +462,8 @@ Layout workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim, i
 using MainFn = void (*)(_Float16*, float*, float*, const int32_t*, const _Float16*, const _Float16*, const _Float16*,
                         const int32_t*, int32_t, const int32_t*, int32_t, int32_t, int32_t, float, int32_t,
                         int32_t, int64_t);
-using ReduceFn = void (*)(_Float16*, const float*, const float*, const int32_t*, int32_t, int32_t, int32_t,
-                          int64_t);
+using ReduceFn = void (*)(_Float16*, const float*, const float*, const int32_t*, const int32_t*, int32_t, int32_t,
+                          int32_t, int64_t);
 
 template <int D>
 MainFn pick_main(int32_t b) {
@@ -553,12 +561,24 @@ extern "C" size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, 
     return workspace_layout(num_seqs, num_heads, head_dim, max_context_len, p).total;
 }
 
+extern "C" int pa_decode_order(int32_t* seq_order, const int32_t* context_lens, int32_t num_seqs,
+                               int32_t max_context_len, void* stream) {
+    if (num_seqs < 0 || num_seqs > 65535 || max_context_len < 0)
+        return pa::fail(PA_ERR_INVALID, "pa_decode_order: bad sizes (S=%d max_len=%d)", num_seqs, max_context_len);
+    if (num_seqs == 0) return PA_OK;
+    if (!seq_order || !context_lens) return pa::fail(PA_ERR_INVALID, "pa_decode_order: null pointer");
+    launch_order(seq_order, context_lens, num_seqs, max_context_len, static_cast<hipStream_t>(stream));
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "pa_decode_order: %s", hipGetErrorString(e));
+    return PA_OK;
+}
+
 extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, int32_t max_blocks_per_seq,
                          const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                          float scale, int32_t max_context_len, int32_t partition_size, void* workspace,
-                         size_t workspace_bytes, int32_t dtype, void* stream) {
+                         size_t workspace_bytes, const int32_t* seq_order, int32_t dtype, void* stream) {
     if (dtype != PA_DTYPE_F16) return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: dtype %d", dtype);
     if (!supported_head_dim(head_dim)) return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d", head_dim);
     if (!supported_block_size(block_size))
@@ -591,9 +611,10 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const vo
     }
     if (workspace && !aligned16(workspace))
         return pa::fail(PA_ERR_INVALID, "pa_decode: workspace must be 16-byte aligned");
-    // one partition: the workspace only holds the longest-first order, and
-    // without one (NULL or smaller) the sequences run in grid order
-    const bool ordered = L.order_bytes > 0 && workspace && workspace_bytes >= L.total;
+    // the caller's order if given; else one computed here into the
+    // workspace (with one partition the workspace only holds that order, and
+    // without one -- NULL or smaller -- the sequences run in index order)
+    const bool compute_order = !seq_order && L.order_bytes > 0 && workspace && workspace_bytes >= L.total;
     if (L.num_parts > 65535)
         return pa::fail(PA_ERR_INVALID, "pa_decode: max_context_len %d needs %d partitions of %d (limit 65535)",
                         max_context_len, L.num_parts, p);
@@ -602,17 +623,16 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const vo
     const int64_t len_cap = len_cap_tables < len_cap_grid ? len_cap_tables : len_cap_grid;
 
     char* wsb = static_cast<char*>(workspace);
-    int32_t* order = ordered ? reinterpret_cast<int32_t*>(wsb) : nullptr;
+    int32_t* own_order = compute_order ? reinterpret_cast<int32_t*>(wsb) : nullptr;
+    const int32_t* order = seq_order ? seq_order : own_order;
     float* ws_ml = L.num_parts > 1 ? reinterpret_cast<float*>(wsb + L.order_bytes) : nullptr;
     float* ws_acc = L.num_parts > 1 ? reinterpret_cast<float*>(wsb + L.order_bytes + L.ml_bytes) : nullptr;
     const float scale_log2 = (float)((double)scale * kLog2e);
     auto st = static_cast<hipStream_t>(stream);
 
     hipError_t e;
-    if (order) {
-        const int32_t width = max_context_len / kOrderClasses + 1;
-        hipLaunchKernelGGL(order_by_length_kernel, dim3(1), dim3(kOrderClasses), 0, st, order, context_lens,
-                           num_seqs, width);
+    if (own_order) {
+        launch_order(own_order, context_lens, num_seqs, max_context_len, st);
         e = hipGetLastError();
         if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "pa_decode: %s", hipGetErrorString(e));
     }
@@ -638,7 +658,7 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const vo
     if (L.num_parts > 1) {
         const unsigned threads = head_dim < 64 ? 64u : (unsigned)head_dim;
         hipLaunchKernelGGL(pick_reduce(head_dim), dim3((unsigned)num_heads, (unsigned)num_seqs), dim3(threads), 0,
-                           st, static_cast<_Float16*>(out), (const float*)ws_ml, (const float*)ws_acc,
+                           st, static_cast<_Float16*>(out), (const float*)ws_ml, (const float*)ws_acc, order,
                            context_lens, num_heads, p, L.num_parts, len_cap);
         e = hipGetLastError();
         if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "pa_decode: %s", hipGetErrorString(e));

@@ -65,6 +65,7 @@ decode_gqa_mfma_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, fl
                        int32_t num_parts, int64_t len_cap) {
     const int kvh = blockIdx.x;
     const int s = order ? order[blockIdx.y] : (int)blockIdx.y;   // longest sequences first
+    if ((uint32_t)s >= gridDim.y) return;                         // not a sequence: nothing to do
     const int part = blockIdx.z;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

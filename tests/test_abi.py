@@ -43,10 +43,10 @@ def test_no_oracle_in_the_product():
 
 def _decode_args(**kw):
     a = dict(out=16, q=16, k=16, v=16, tables=16, W=4, lens=16, S=1, H=2, Hkv=2, D=128, B=16, NB=8,
-             scale=0.1, maxlen=64, P=0, ws=None, wsb=0, dtype=0, stream=None)
+             scale=0.1, maxlen=64, P=0, ws=None, wsb=0, order=None, dtype=0, stream=None)
     a.update(kw)
     return (a["out"], a["q"], a["k"], a["v"], a["tables"], a["W"], a["lens"], a["S"], a["H"], a["Hkv"],
-            a["D"], a["B"], a["NB"], a["scale"], a["maxlen"], a["P"], a["ws"], a["wsb"], a["dtype"],
+            a["D"], a["B"], a["NB"], a["scale"], a["maxlen"], a["P"], a["ws"], a["wsb"], a["order"], a["dtype"],
             a["stream"])
 
 
@@ -70,6 +70,15 @@ def test_decode_rejects_bad_arguments_before_launch(kw, code):
 
 def test_decode_with_no_sequences_is_a_no_op():
     assert pa.lib().pa_decode(*_decode_args(S=0, out=None)) == pa.PA_OK
+
+
+def test_decode_order_checks_arguments():
+    L = pa.lib()
+    assert L.pa_decode_order(None, None, 0, 2048, None) == pa.PA_OK           # nothing to order
+    assert L.pa_decode_order(None, 16, 4, 2048, None) == pa.PA_ERR_INVALID
+    assert L.pa_decode_order(16, 16, -1, 2048, None) == pa.PA_ERR_INVALID
+    assert L.pa_decode_order(16, 16, 4, -5, None) == pa.PA_ERR_INVALID
+    assert L.pa_decode_order(16, 16, 70000, 2048, None) == pa.PA_ERR_INVALID
 
 
 def test_workspace_size():

@@ -152,12 +152,46 @@ def test_longest_first_order_changes_no_bit(H, Hkv):
     plain = torch.full((S, H, D), float("nan"), dtype=torch.float16, device=dev)
     rc = pa.lib().pa_decode(plain.data_ptr(), d_q.data_ptr(), d_k.data_ptr(), d_v.data_ptr(), d_t.data_ptr(),
                             tables.shape[1], d_l.data_ptr(), S, H, Hkv, D, 16, case.num_blocks, case.scale, 2048,
-                            2048, None, 0, pa.PA_DTYPE_F16, None)
+                            2048, None, 0, None, pa.PA_DTYPE_F16, None)
     assert rc == pa.PA_OK
     torch.cuda.synchronize()
     assert np.array_equal(bits(ordered), bits(plain))
     ref = oracle.decode(case.q, kc, vc, tables, lens, case.scale)
     assert_attention_close(ordered, ref, f"ordered H={H}/{Hkv}")
+    # the order pa_decode_order computes: a permutation, longest class first
+    order = pa.pa_decode_order(d_l, 2048).cpu().numpy()
+    assert sorted(order.tolist()) == list(range(S))
+    cls = np.minimum(lens[order] // (2048 // 1024 + 1), 1023)
+    assert np.all(np.diff(cls) <= 0)
+    # any permutation passed as seq_order, and a split into partitions, change no bit
+    for perm in (torch.from_numpy(order).to(dev), torch.from_numpy(rng.permutation(S).astype(np.int32)).to(dev)):
+        given = torch.full((S, H, D), float("nan"), dtype=torch.float16, device=dev)
+        pa.pa_decode(given, d_q, d_k, d_v, d_t, d_l, case.scale, partition_size=2048, max_context_len=2048,
+                     seq_order=perm)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(given), bits(plain))
+    split = torch.full((S, H, D), float("nan"), dtype=torch.float16, device=dev)
+    pa.pa_decode(split, d_q, d_k, d_v, d_t, d_l, case.scale, partition_size=512, max_context_len=2048,
+                 seq_order=torch.from_numpy(order).to(dev))
+    torch.cuda.synchronize()
+    assert_attention_close(split, ref, f"split, given order H={H}/{Hkv}")
+
+
+def test_seq_order_entries_outside_the_batch_are_skipped():
+    """A sequence the order leaves out keeps its rows untouched; an entry
+    outside [0, S) does nothing."""
+    dev = device()
+    case = workloads.random_case(88, [300, 17, 900, 1], 4, 4, 128, 16)
+    kc, vc, tables, lens = _oracle_cache(case)
+    out = torch.zeros((4, 4, 128), dtype=torch.float16, device=dev)
+    order = torch.tensor([2, -1, 0, 7], dtype=torch.int32, device=dev)
+    pa.pa_decode(out, torch.from_numpy(case.q).to(dev), torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev),
+                 torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), case.scale, seq_order=order)
+    torch.cuda.synchronize()
+    ref = oracle.decode(case.q, kc, vc, tables, lens, case.scale)
+    o = out.float().cpu().numpy()
+    assert np.all(o[[1, 3]] == 0)
+    assert_attention_close(out[[0, 2]], ref[[0, 2]], "ordered subset")
 
 
 def test_workspace_reused_across_calls_of_different_sizes():
