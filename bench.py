@@ -428,12 +428,12 @@ def prefix_bench(args, dev):
     q = torch.randn((R, H, D), generator=g, device=dev, dtype=torch.float16)
     d_tables, d_lens = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
     out = torch.empty_like(q)
-    ws = torch.zeros(max(1, pa.pa_decode_workspace_size(R, H, Hkv, D, B, width * B, 0)), dtype=torch.uint8,
-                     device=dev)
+    ws = torch.zeros(max(1, pa.pa_decode_workspace_size(R, H, Hkv, D, B, width * B, args.partition)),
+                     dtype=torch.uint8, device=dev)
 
     def call(l):
         pa.pa_decode(out, q, kcs[l], vcs[l], d_tables, d_lens, 1 / np.sqrt(D), B, max_context_len=width * B,
-                     workspace=ws)
+                     partition_size=args.partition, workspace=ws)
 
     for _ in range(args.warmup):
         for l in range(L):

@@ -502,30 +502,48 @@ ReduceFn pick_reduce(int32_t d) {
     }
 }
 
-// Default partition.  Rows are the workgroups one partition per sequence
-// gives (sequences x query heads, or x KV heads on the grouped-query
-// kernel); slots the workgroups resident at once (256 CUs x 4 for the
-// one-query-per-head kernel, x 2 for the grouped-query kernel, whose
-// registers allow two per CU).  With rows >= 2 x slots the batch fills the
-// GPU twice unsplit: 2048 (sequences are dispatched longest first, so the
-// drain stays short, and no merge kernel runs when every context fits).
-// Otherwise the longest of 2048 / 1024 / 512 / 256 tokens that gives at
-// least four workgroups per slot, counting full partitions of the longest
-// sequence.  Measured (KV GB/s per call): 64 x 32-head batch with U[1, 2048]
-// contexts 6.29 TB/s at 2048 against 6.10 at 1024; 256 x 8-KV-head batch
-// 5.84 against 5.61; 16 x 32-head batch at 4096 tokens 6.23 TB/s at 512,
-// 6.00 at 1024, 6.17 at 2048.
+bool uses_mfma(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size) {
+    const int32_t group = num_kv_heads > 0 ? num_heads / num_kv_heads : 1;
+    return pa::gqa_mfma_supported(head_dim, block_size, group);
+}
+
+// workgroups per partition index: one per (sequence, query head), or per
+// (sequence, KV head) on the grouped-query kernel
+int64_t grid_rows(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size) {
+    return (int64_t)num_seqs * (uses_mfma(num_heads, num_kv_heads, head_dim, block_size) ? num_kv_heads : num_heads);
+}
+
+// workgroups resident at once: 256 CUs x 4 (vector kernel, 108 VGPRs) or x 2
+// (grouped-query kernel, 232 VGPRs)
+int64_t resident_slots(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size) {
+    return 256LL * (uses_mfma(num_heads, num_kv_heads, head_dim, block_size) ? 2 : 4);
+}
+
+// Default partition.  Rows are the workgroups one partition index gives
+// (grid_rows), slots the workgroups resident at once (resident_slots).
+//  * 2048 tokens when the 2048-token grid fills the slots a whole number of
+//    times, at least twice (or leaves the last round at least 3/4 full),
+//    counting every sequence at the bound: with the sequences dispatched
+//    longest first the drain is short, and long partitions mean fewer
+//    partial states and, when every context fits, no merge kernel.
+//  * Otherwise the longest of 2048 / 1024 / 512 / 256 tokens that gives at
+//    least four workgroups per slot, counting full partitions of a longest
+//    sequence (the bound may exceed every actual length).
+// Measured (decode call, KV GB/s): 64 x 32-head batch, U[1, 2048] contexts,
+// 6.29 TB/s at 2048 against 5.99 at 1024; 256 x 8-KV-head batch 6.02
+// against 5.57; 100 requests of 1001..1200 tokens (3.1 rounds at 2048):
+// 512 beats 2048 by 10%; 16 x 32 heads at 4096 tokens: 256..2048 within 3%.
 int32_t default_partition(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                           int32_t block_size, int32_t max_context_len) {
-    const int32_t group = num_kv_heads > 0 ? num_heads / num_kv_heads : 1;
-    const bool mfma = pa::gqa_mfma_supported(head_dim, block_size, group);
-    const int64_t rows = (int64_t)num_seqs * (mfma ? num_kv_heads : num_heads);
-    const int64_t slots = 256LL * (mfma ? 2 : 4);
-    if (rows >= 2 * slots) return 2048;
+    const int64_t rows = grid_rows(num_seqs, num_heads, num_kv_heads, head_dim, block_size);
+    const int64_t slots = resident_slots(num_heads, num_kv_heads, head_dim, block_size);
+    {
+        const int64_t wgs = rows * (max_context_len > 2048 ? ((int64_t)max_context_len + 2047) / 2048 : 1);
+        const int64_t tail = wgs % slots;
+        if (wgs >= 2 * slots && (tail == 0 || 4 * tail >= 3 * slots)) return 2048;
+    }
     const int32_t cands[] = {2048, 1024, 512, 256};
     for (int32_t p : cands) {
-        // full partitions of a longest sequence: the bound may exceed every
-        // actual length, so a partial last partition is not counted on
         const int64_t parts = max_context_len / p > 0 ? max_context_len / p : 1;
         if (rows * parts >= 4 * slots) return p;
     }
@@ -613,8 +631,12 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const vo
         return pa::fail(PA_ERR_INVALID, "pa_decode: workspace must be 16-byte aligned");
     // the caller's order if given; else one computed here into the
     // workspace (with one partition the workspace only holds that order, and
-    // without one -- NULL or smaller -- the sequences run in index order)
-    const bool compute_order = !seq_order && L.order_bytes > 0 && workspace && workspace_bytes >= L.total;
+    // without one -- NULL or smaller -- the sequences run in index order).
+    // When every workgroup is resident at once the order cannot matter, and
+    // the small kernel is skipped.
+    const bool compute_order = !seq_order && L.order_bytes > 0 && workspace && workspace_bytes >= L.total &&
+                               (int64_t)grid_rows(num_seqs, num_heads, num_kv_heads, head_dim, block_size) *
+                                       L.num_parts > resident_slots(num_heads, num_kv_heads, head_dim, block_size);
     if (L.num_parts > 65535)
         return pa::fail(PA_ERR_INVALID, "pa_decode: max_context_len %d needs %d partitions of %d (limit 65535)",
                         max_context_len, L.num_parts, p);

@@ -96,16 +96,20 @@ def test_workspace_size():
 
 
 def test_default_partition_keeps_the_gpu_busy():
-    """2048 when one workgroup per row (sequence x query head, or x KV head
-    on the grouped path) fills the resident slots twice (1024 slots for one
-    query per KV head, 512 for groups of 2..16 at head_dim 128); otherwise
-    the longest of 2048/1024/512/256 tokens with >= 4 workgroups per slot,
-    counting full partitions of the longest sequence; 256 when even that is
-    not reached."""
+    """2048 when rows x ceil(max_len / 2048) workgroups (rows: sequence x
+    query head, or x KV head on the grouped path) fill the resident slots
+    (1024 for one query per KV head, 512 for groups of 2..16 at head_dim
+    128) at least twice, a whole number of times or with the last round at
+    least 3/4 full; otherwise the longest of 2048/1024/512/256 tokens with
+    >= 4 workgroups per slot, counting full partitions of the longest
+    sequence; 256 when even that is not reached."""
     L = pa.lib()
-    assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2048) == 2048     # 2048 rows = 2 x 1024
-    assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 8192) == 2048
-    assert L.pa_decode_default_partition(63, 32, 32, 128, 16, 2048) == 512      # 2016 rows x 4 partitions
+    assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2048) == 2048     # 2048 workgroups = 2 rounds
+    assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2112) == 2048     # 4096 = 4 rounds
+    assert L.pa_decode_default_partition(100, 32, 32, 128, 16, 1216) == 512     # 3.125 rounds at 2048
+    assert L.pa_decode_default_partition(120, 32, 32, 128, 16, 1216) == 2048    # 3.75: last round 3/4 full
+    assert L.pa_decode_default_partition(112, 32, 32, 128, 16, 1216) == 512     # 3.5: last round half full
+    assert L.pa_decode_default_partition(63, 32, 32, 128, 16, 2048) == 512      # 2016 < 2 rounds; 2016 x 4
     assert L.pa_decode_default_partition(256, 64, 8, 128, 16, 2048) == 2048     # grouped: 2048 rows, 512 slots
     assert L.pa_decode_default_partition(64, 64, 8, 128, 16, 2048) == 512       # 512 rows x 4
     assert L.pa_decode_default_partition(16, 32, 32, 128, 16, 4096) == 512      # 512 rows x 8

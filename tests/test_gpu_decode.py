@@ -137,44 +137,49 @@ def test_deterministic_and_blind_to_physical_placement():
 
 @pytest.mark.parametrize("H,Hkv", [(8, 8), (8, 1)])
 def test_longest_first_order_changes_no_bit(H, Hkv):
-    """With one partition the workspace only carries the longest-first
-    dispatch order; without it (NULL) the sequences run in index order.
-    Both give the same bits, and both match the oracle."""
+    """The dispatch order never changes a bit: index order (one partition,
+    no workspace), the order pa_decode computes itself (128-token
+    partitions: more workgroups than resident slots), the order
+    pa_decode_order writes, and an arbitrary permutation, all against the
+    oracle."""
     dev = device()
     rng = np.random.default_rng(17)
     lens_l = [int(x) for x in rng.integers(0, 2049, size=40)]
     case = workloads.random_case(77 + Hkv, lens_l, H, Hkv, 128, 16)
     kc, vc, tables, lens = _oracle_cache(case)
-    ordered = _gpu_decode(dev, case.q, kc, vc, tables, lens, case.scale, partition_size=2048, max_context_len=2048)
     S, D = len(lens_l), 128
     d_q, d_k, d_v = (torch.from_numpy(x).to(dev) for x in (case.q, kc, vc))
     d_t, d_l = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
+    ref = oracle.decode(case.q, kc, vc, tables, lens, case.scale)
+
+    def run(P, **kw):
+        o = torch.full((S, H, D), float("nan"), dtype=torch.float16, device=dev)
+        pa.pa_decode(o, d_q, d_k, d_v, d_t, d_l, case.scale, partition_size=P, max_context_len=2048, **kw)
+        torch.cuda.synchronize()
+        return o
+
+    # one partition: index order (NULL workspace) against given orders
     plain = torch.full((S, H, D), float("nan"), dtype=torch.float16, device=dev)
     rc = pa.lib().pa_decode(plain.data_ptr(), d_q.data_ptr(), d_k.data_ptr(), d_v.data_ptr(), d_t.data_ptr(),
                             tables.shape[1], d_l.data_ptr(), S, H, Hkv, D, 16, case.num_blocks, case.scale, 2048,
                             2048, None, 0, None, pa.PA_DTYPE_F16, None)
     assert rc == pa.PA_OK
     torch.cuda.synchronize()
-    assert np.array_equal(bits(ordered), bits(plain))
-    ref = oracle.decode(case.q, kc, vc, tables, lens, case.scale)
-    assert_attention_close(ordered, ref, f"ordered H={H}/{Hkv}")
-    # the order pa_decode_order computes: a permutation, longest class first
-    order = pa.pa_decode_order(d_l, 2048).cpu().numpy()
-    assert sorted(order.tolist()) == list(range(S))
-    cls = np.minimum(lens[order] // (2048 // 1024 + 1), 1023)
-    assert np.all(np.diff(cls) <= 0)
-    # any permutation passed as seq_order, and a split into partitions, change no bit
-    for perm in (torch.from_numpy(order).to(dev), torch.from_numpy(rng.permutation(S).astype(np.int32)).to(dev)):
-        given = torch.full((S, H, D), float("nan"), dtype=torch.float16, device=dev)
-        pa.pa_decode(given, d_q, d_k, d_v, d_t, d_l, case.scale, partition_size=2048, max_context_len=2048,
-                     seq_order=perm)
-        torch.cuda.synchronize()
-        assert np.array_equal(bits(given), bits(plain))
-    split = torch.full((S, H, D), float("nan"), dtype=torch.float16, device=dev)
-    pa.pa_decode(split, d_q, d_k, d_v, d_t, d_l, case.scale, partition_size=512, max_context_len=2048,
-                 seq_order=torch.from_numpy(order).to(dev))
-    torch.cuda.synchronize()
-    assert_attention_close(split, ref, f"split, given order H={H}/{Hkv}")
+    assert_attention_close(plain, ref, f"index order H={H}/{Hkv}")
+    order = pa.pa_decode_order(d_l, 2048)
+    o = order.cpu().numpy()
+    assert sorted(o.tolist()) == list(range(S))                           # a permutation,
+    cls = np.minimum(lens[o] // (2048 // 1024 + 1), 1023)
+    assert np.all(np.diff(cls) <= 0)                                      # longest class first
+    for perm in (order, torch.from_numpy(rng.permutation(S).astype(np.int32)).to(dev)):
+        assert np.array_equal(bits(run(2048, seq_order=perm)), bits(plain))
+    # 128-token partitions: pa_decode orders the sequences itself (the
+    # workgroups outnumber the resident slots); same bits as index order
+    ident = torch.arange(S, dtype=torch.int32, device=dev)
+    own = run(128)
+    assert np.array_equal(bits(own), bits(run(128, seq_order=ident)))
+    assert np.array_equal(bits(own), bits(run(128, seq_order=order)))
+    assert_attention_close(own, ref, f"128-token partitions H={H}/{Hkv}")
 
 
 def test_seq_order_entries_outside_the_batch_are_skipped():
