@@ -435,9 +435,12 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
             // uniform: tile below the wave's first row and wholly valid
             bool interior = k * kKvTile + kKvTile - 1 <= first_pos;
             if (interior) {
-                const uint32_t f0 = *reinterpret_cast<const uint32_t*>(lds_flags[cur] + 4 * jg);
-                const uint32_t f1 = *reinterpret_cast<const uint32_t*>(lds_flags[cur] + 16 + 4 * jg);
-                interior = __all(f0 == 0x01010101u && f1 == 0x01010101u);
+                bool all_ok = true;          // the flags of tokens 16h + 4*jg .. +3, for every h
+#pragma unroll
+                for (int h = 0; h < kKvTile / 16; ++h)
+                    all_ok = all_ok && *reinterpret_cast<const uint32_t*>(lds_flags[cur] + 16 * h + 4 * jg) ==
+                                           0x01010101u;
+                interior = __all(all_ok);
             }
             consume_lds_tile(st, lds[cur], lds_flags[cur], k * kKvTile, interior, qb, c_log2, lane, rw);
         }
