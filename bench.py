@@ -53,7 +53,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="llama7b", choices=["llama7b", "gqa", "long", "copy", "swap", "prefix", "prefill", "sweep", "sampling"],
+    p.add_argument("--workload", default="llama7b", choices=["llama7b", "gqa", "long", "copy", "swap", "prefix", "prefill", "chunked", "sweep", "sampling"],
                    help="llama7b: the Llama-2-7B decode batch (default); gqa: 64 query heads over 8 KV "
                         "heads (matrix-core kernel); long: 16 x 4096 tokens; copy: block-copy calibration; "
                         "swap: block swaps between HBM and pinned host memory; prefix: 100 requests "
@@ -126,6 +126,8 @@ def main():
         return prefix_bench(args, dev)
     if args.workload == "prefill":
         return prefill_bench(args, dev)
+    if args.workload == "chunked":
+        return chunked_bench(args, dev)
     if args.workload == "sweep":
         return sweep_bench(args, dev)
     if args.workload == "sampling":
@@ -540,6 +542,77 @@ def prefill_bench(args, dev):
                       "config": {"workload": "prefill", "prompts": S, "tokens": T, "max_prompt": mq,
                                  "num_heads": H, "num_kv_heads": Hkv, "head_dim": D, "block_size": B,
                                  "layers_resident": L}}), flush=True)
+
+
+def chunked_bench(args, dev):
+    """Chunked prefill: a short chunk of new tokens per sequence over a long
+    cached context, few sequences -- the shape that gives pa_prefill too few
+    workgroups unless the context is split.  Two batches: 4 sequences x 8192
+    cached tokens with 32 new each at Llama-2-7B heads (32 x 128), and 16 x
+    4096 with 16 new each at 32 query / 8 KV heads; B = 16, --layers layers
+    resident (default here 4).  K/V bytes = every cached token's K and V of
+    every KV head, read once; the kernel is HBM-bound at these shapes (16-32
+    new tokens per KV head: 4 x g x 128 x rows flops per 512 bytes)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_390_amd as pa
+
+    L = args.layers if args.layers != 32 else 4
+    B, D = args.block_size, 128
+    results = []
+    for S, n, m, H, Hkv in ((4, 8192, 32, 32, 32), (16, 4096, 16, 32, 8)):
+        nbps = -(-n // B)
+        NB = S * nbps + 8
+        g = torch.Generator(device=dev)
+        g.manual_seed(args.seed)
+        kcs = [torch.randn((NB, Hkv, B, D), generator=g, device=dev, dtype=torch.float16) for _ in range(L)]
+        vcs = [torch.randn((NB, Hkv, B, D), generator=g, device=dev, dtype=torch.float16) for _ in range(L)]
+        perm = np.random.default_rng(args.seed).permutation(NB)[:S * nbps].reshape(S, nbps).astype(np.int32)
+        T = S * m
+        q = torch.randn((T, H, D), generator=g, device=dev, dtype=torch.float16)
+        out = torch.empty_like(q)
+        d_t = torch.from_numpy(perm).to(dev)
+        d_l = torch.full((S,), n, dtype=torch.int32, device=dev)
+        d_q = torch.arange(0, T + 1, m, dtype=torch.int32, device=dev)
+        ws_n = pa.pa_prefill_workspace_size(T, S, H, Hkv, D, B, nbps, m)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+
+        def call(l, split=True):
+            pa.pa_prefill(out, q, kcs[l], vcs[l], d_t, d_l, d_q, 1 / np.sqrt(D), max_query_len=m,
+                          workspace=ws, split=split)
+
+        timed = {}
+        for split in (False, True):
+            for _ in range(max(args.warmup, 3)):
+                for l in range(L):
+                    call(l, split)
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps * L)]
+            for i in range(args.steps):
+                for l in range(L):
+                    a, b = ev[i * L + l]
+                    a.record()
+                    call(l, split)
+                    b.record()
+            torch.cuda.synchronize()
+            timed[split] = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+        kv = S * n * Hkv * D * 2 * 2
+        gbs = kv / timed[True] / 1e3
+        log(f"[bench] chunked: {S} x {n} cached, {m} new, {H}/{Hkv} heads: {timed[True]:.1f} us split "
+            f"({ws_n >> 20} MiB workspace) = {gbs:.0f} GB/s of K/V ({100 * gbs / HBM_PEAK_GBS:.1f}% of peak); "
+            f"unsplit {timed[False]:.1f} us")
+        results.append({"batch": f"{S}x{n}+{m}, {H}/{Hkv} heads", "us_split": round(timed[True], 2),
+                        "us_unsplit": round(timed[False], 2), "kv_GB_s": round(gbs, 1)})
+    best = results[0]
+    print(json.dumps({"metric": "chunked prefill K/V GB/s (split context)", "value": best["kv_GB_s"],
+                      "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "higher_is_better": True, "dtype": "f16", "batches": results,
+                      "roofline": {"bound": "hbm", "achieved": best["kv_GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": round(best["kv_GB_s"] / HBM_PEAK_GBS, 4), "traffic": None},
+                      "config": {"workload": "chunked", "block_size": B, "head_dim": D, "layers_resident": L}}),
+          flush=True)
 
 
 def sweep_bench(args, dev):

@@ -180,9 +180,17 @@ int pa_decode_order(int32_t *seq_order, const int32_t *context_lens,
  *   max_query_len  host-known bound on every m_s; it sizes the grid.  A
  *                  sequence with m_s > max_query_len, m_s > n_s or n_s beyond
  *                  its table gets its first max_query_len rows as NaN.
+ *   workspace      device scratch of pa_prefill_workspace_size() bytes,
+ *                  16-byte aligned, or NULL.  When the batch gives too few
+ *                  workgroups to fill the GPU (few sequences or KV heads,
+ *                  short chunks over long contexts) the context is split
+ *                  into parts whose partial results it holds, merged by a
+ *                  second kernel; without it (NULL or smaller) the context
+ *                  is not split.  Contents on entry are ignored; calls
+ *                  sharing a workspace must be stream-ordered.
  * head_dim 128 only (PA_ERR_UNSUPPORTED otherwise); any num_heads multiple of
  * num_kv_heads.  Runs on the matrix cores (v_mfma_f32_16x16x32_f16, fp32
- * accumulation); no workspace.
+ * accumulation).
  * ------------------------------------------------------------------------ */
 int pa_prefill(void *out, const void *q, int32_t num_tokens,
                const void *k_cache, const void *v_cache,
@@ -190,8 +198,19 @@ int pa_prefill(void *out, const void *q, int32_t num_tokens,
                const int32_t *context_lens, const int32_t *query_start,
                int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                int32_t head_dim, int32_t block_size, int32_t num_blocks,
-               float scale, int32_t max_query_len, int32_t dtype,
-               void *stream);
+               float scale, int32_t max_query_len, void *workspace,
+               size_t workspace_bytes, int32_t dtype, void *stream);
+
+/* Bytes of workspace pa_prefill uses for these sizes: 0 when the batch
+ * fills the GPU without splitting the context, else (2 + head_dim) x 4 bytes
+ * per (token, head, context part), in two 256-byte aligned regions.  The
+ * context bound is max_blocks_per_seq x block_size.  (size_t)-1 for invalid
+ * arguments. */
+size_t pa_prefill_workspace_size(int32_t num_tokens, int32_t num_seqs,
+                                 int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size,
+                                 int32_t max_blocks_per_seq,
+                                 int32_t max_query_len);
 
 /* Bytes of workspace pa_decode uses for these sizes: the dispatch order
  * (4 bytes per sequence, rounded up to 256; none for a single sequence) plus,

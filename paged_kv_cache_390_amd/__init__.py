@@ -9,7 +9,7 @@ current HIP stream.  There is no fallback: if the library is not built, every
 call raises.
 
 Functions carry the C names: ``pa_reshape_and_cache``, ``pa_decode``,
-``pa_decode_order``, ``pa_decode_workspace_size``, ``pa_prefill``, ``pa_copy_blocks``, ``pa_swap_blocks``;
+``pa_decode_order``, ``pa_decode_workspace_size``, ``pa_prefill``, ``pa_prefill_workspace_size``, ``pa_copy_blocks``, ``pa_swap_blocks``;
 ``BlockManager`` wraps the ``pa_bm_*`` calls.
 """
 from __future__ import annotations
@@ -65,9 +65,10 @@ def lib() -> ctypes.CDLL:
         "pa_reshape_and_cache": ([P, P, i64, P, i32, P, P, i32, i32, i32, i32, i32, P], ctypes.c_int),
         "pa_decode": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P, sz, P, i32, P],
                       ctypes.c_int),
-        "pa_prefill": ([P, P, i32, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P],
+        "pa_prefill": ([P, P, i32, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, f32, i32, P, sz, i32, P],
                        ctypes.c_int),
         "pa_decode_order": ([P, P, i32, i32, P], ctypes.c_int),
+        "pa_prefill_workspace_size": ([i32, i32, i32, i32, i32, i32, i32, i32], sz),
         "pa_decode_workspace_size": ([i32, i32, i32, i32, i32, i32, i32], sz),
         "pa_decode_default_partition": ([i32, i32, i32, i32, i32, i32], i32),
         "pa_copy_blocks": ([P, P, i32, P, i32, i32, i64, i32, P], ctypes.c_int),
@@ -258,12 +259,23 @@ def pa_decode_order(context_lens, max_context_len: int, out=None):
     return out
 
 
+def pa_prefill_workspace_size(num_tokens: int, num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                              block_size: int, max_blocks_per_seq: int, max_query_len: int) -> int:
+    n = lib().pa_prefill_workspace_size(num_tokens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                                        max_blocks_per_seq, max_query_len)
+    if n == ctypes.c_size_t(-1).value:
+        raise PAError(PA_ERR_INVALID, "pa_prefill_workspace_size: invalid arguments")
+    return n
+
+
 def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float,
-               max_query_len: Optional[int] = None) -> None:
+               max_query_len: Optional[int] = None, workspace=None, split: bool = True) -> None:
     """Causal attention of the packed new tokens q[T, H, D] over the paged
     cache: sequence s's rows query_start[s] .. query_start[s+1]-1 are its
     last m tokens (K/V already cached), row i at position context_lens[s] -
-    m + i.  max_query_len defaults to T."""
+    m + i.  max_query_len defaults to T.  workspace (uint8 device tensor)
+    is allocated when the batch is small enough for the context to be split
+    and none is given; split=False passes none (no split)."""
     torch = _torch()
     _dev_tensor(k_cache, "k_cache", torch.float16, 4)
     _dev_tensor(v_cache, "v_cache", torch.float16, 4)
@@ -283,10 +295,18 @@ def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start
         raise ValueError("block_tables / context_lens / query_start disagree on the number of sequences")
     if max_query_len is None:
         max_query_len = T
+    ws_ptr, ws_bytes = None, 0
+    if split:
+        need = pa_prefill_workspace_size(T, S, H, Hkv, D, B, block_tables.shape[1], int(max_query_len))
+        if need:
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            _dev_tensor(workspace, "workspace", torch.uint8, 1)
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
     _check(lib().pa_prefill(out.data_ptr(), q.data_ptr(), T, k_cache.data_ptr(), v_cache.data_ptr(),
                             block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
                             query_start.data_ptr(), S, H, Hkv, D, B, NB, float(scale), int(max_query_len),
-                            PA_DTYPE_F16, _stream(q.device)), "pa_prefill")
+                            ws_ptr, ws_bytes, PA_DTYPE_F16, _stream(q.device)), "pa_prefill")
 
 
 def pa_copy_blocks(k_caches: Sequence, v_caches: Sequence, src_dst_pairs) -> None:

@@ -328,12 +328,16 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
                     const _Float16* __restrict__ k_cache, const _Float16* __restrict__ v_cache,
                     const int32_t* __restrict__ tables, int32_t max_blocks, const int32_t* __restrict__ lens,
                     const int32_t* __restrict__ query_start, int32_t num_heads, int32_t num_kv_heads,
-                    int32_t num_blocks, float scale_log2, int32_t max_query_len, int64_t len_cap) {
+                    int32_t num_blocks, float scale_log2, int32_t max_query_len, int64_t len_cap,
+                    float* __restrict__ ws_ml, float* __restrict__ ws_acc, int32_t tiles_per_part,
+                    int32_t num_parts) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[2][2 * kTileBytes];
     __shared__ __attribute__((aligned(4))) unsigned char lds_flags[2][kKvTile];
     const int kvh = blockIdx.x;
     const int s = blockIdx.y;
-    const int rtile = gridDim.z - 1 - blockIdx.z;          // last row tile first
+    // grid z = (row tile, context part), parts fastest; last row tile first
+    const int rtile = (int)(gridDim.z / num_parts) - 1 - (int)blockIdx.z / num_parts;
+    const int part = (int)blockIdx.z % num_parts;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = num_heads / num_kv_heads;
@@ -354,7 +358,7 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
     const int nrow = lane & 15;
     const int jg = lane >> 4;
     if (bad) {                                             // the sequence's rows come out as NaN
-        if (jg == 0)
+        if (jg == 0 && part == 0)
             for (int t = 0; t < kNT; ++t) {
                 if (16 * t + nrow >= rows) continue;
                 const int r = row0 + 16 * t + nrow;
@@ -395,6 +399,11 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
     const int wg_rows = min(rows_all - grow0, kRowsPerGroup);
     const int ntiles = (base_pos + (grow0 + wg_rows - 1) / g) / kKvTile + 1;
     const int my_tiles = rows > 0 ? (base_pos + (row0 + rows - 1) / g) / kKvTile + 1 : 0;
+    // this workgroup's share of the context: tiles [k_begin, k_end)
+    const int k_begin = part * tiles_per_part;
+    if (k_begin >= ntiles) return;                         // uniform: nothing of this part is visible
+    const int k_end = min(ntiles, k_begin + tiles_per_part);
+    const int my_end = min(k_end, my_tiles);
     const int first_pos = base_pos + row0 / g;
 
     const int32_t* trow = tables + (int64_t)s * max_blocks;
@@ -420,18 +429,19 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
     // never used), so the waits before a store count only the older tile.
     Staged R0, R1;
     int32_t e[kStageRows] = {};
-    if constexpr (B >= 4) table_entries<B>(e, 0, wave, n, trow);
-    fetch_tile<B>(R0, 0, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
-    if constexpr (B >= 4) table_entries<B>(e, 1, wave, n, trow);
-    fetch_tile<B>(R1, 1, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
-    if constexpr (B >= 4) table_entries<B>(e, 2, wave, n, trow);
-    store_tile(R0, lds[0], lds_flags[0], wave, lane);
+    const int kb = k_begin;
+    if constexpr (B >= 4) table_entries<B>(e, kb, wave, n, trow);
+    fetch_tile<B>(R0, kb, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
+    if constexpr (B >= 4) table_entries<B>(e, kb + 1, wave, n, trow);
+    fetch_tile<B>(R1, kb + 1, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
+    if constexpr (B >= 4) table_entries<B>(e, kb + 2, wave, n, trow);
+    store_tile(R0, lds[kb & 1], lds_flags[kb & 1], wave, lane);
     __syncthreads();
     auto step = [&](int k, Staged& fetch_into, const Staged& next) {
         const int cur = k & 1;
         fetch_tile<B>(fetch_into, k + 2, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
         if constexpr (B >= 4) table_entries<B>(e, k + 3, wave, n, trow);
-        if (k < my_tiles) {
+        if (k < my_end) {
             // uniform: tile below the wave's first row and wholly valid
             bool interior = k * kKvTile + kKvTile - 1 <= first_pos;
             if (interior) {
@@ -447,9 +457,34 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
         store_tile(next, lds[cur ^ 1], lds_flags[cur ^ 1], wave, lane);
         __syncthreads();
     };
-    for (int k = 0; k < ntiles; k += 2) {   // an odd count runs one idle step at the end
+    for (int k = kb; k < k_end; k += 2) {   // an odd count runs one idle step at the end
         step(k, R0, R1);                    // R0 (tile k, now in LDS) refills with k+2; R1 holds k+1
         step(k + 1, R1, R0);
+    }
+
+    if (num_parts > 1) {
+        // unnormalised partial state of every row for the merge kernel:
+        // (m, l) and O at [output row][part]
+#pragma unroll
+        for (int t = 0; t < kNT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int rr = 4 * jg + e;
+                const float L = __shfl(st[t].l, rr);
+                const float M = __shfl(st[t].m, rr);
+                if (16 * t + rr >= rows) continue;
+                const int rwi = row0 + 16 * t + rr;
+                const int64_t orow = ((int64_t)q0 + rwi / g) * num_heads + (int64_t)kvh * g + rwi % g;
+                const int64_t slot = orow * num_parts + part;
+                float* acc = ws_acc + slot * kD + 8 * nrow;
+#pragma unroll
+                for (int c = 0; c < kDTiles; ++c) acc[c] = st[t].o[c][e];
+                if (nrow == 0) {
+                    ws_ml[2 * slot] = M;
+                    ws_ml[2 * slot + 1] = L;
+                }
+            }
+        return;
     }
 
     // Rows 16t + 4*jg + e of the wave live in this lane's st[t].o[c][e] at
@@ -471,9 +506,55 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
         }
 }
 
+// Merge of the context parts: output row (token i of sequence s, head h)
+// combines the (m, l, O) its row tile's parts left, weighted by exp2(m_p -
+// max m).  One 128-thread workgroup (one thread per column) per (head,
+// sequence, 16 tokens).
+constexpr int kMergeTokens = 16;
+
+__global__ void __launch_bounds__(kD)
+prefill_merge_kernel(_Float16* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
+                     int32_t num_tokens, const int32_t* __restrict__ lens, const int32_t* __restrict__ query_start,
+                     int32_t num_heads, int32_t num_kv_heads, int32_t max_query_len, int64_t len_cap,
+                     int32_t tiles_per_part, int32_t num_parts) {
+    const int h = blockIdx.x;
+    const int s = blockIdx.y;
+    const int d = threadIdx.x;
+    const int g = num_heads / num_kv_heads;
+    const int32_t q0 = query_start[s];
+    const int32_t q1 = query_start[s + 1];
+    if (q0 < 0 || q1 < q0 || q1 > num_tokens) return;      // skipped by the first kernel too
+    const int32_t m = q1 - q0;
+    const int32_t n = lens[s];
+    if (m > max_query_len || n < m || (int64_t)n > len_cap) return;   // NaN rows, written by the first kernel
+    const int base_pos = n - m;
+    const int rows_all = m * g;
+    const int i_end = min(m, (int)(blockIdx.z + 1) * kMergeTokens);
+    for (int i = blockIdx.z * kMergeTokens; i < i_end; ++i) {
+        // the row tile of this row, and how many parts its workgroups covered
+        const int r = i * g + h % g;
+        const int grow0 = (r / kRowsPerGroup) * kRowsPerGroup;
+        const int wg_rows = min(rows_all - grow0, kRowsPerGroup);
+        const int ntiles = (base_pos + (grow0 + wg_rows - 1) / g) / kKvTile + 1;
+        const int np = min(num_parts, (ntiles + tiles_per_part - 1) / tiles_per_part);
+        const int64_t orow = ((int64_t)q0 + i) * num_heads + h;
+        const int64_t base = orow * num_parts;
+        float M = -INFINITY;
+        for (int p = 0; p < np; ++p) M = fmaxf(M, ws_ml[2 * (base + p)]);
+        float L = 0.f, o = 0.f;
+        for (int p = 0; p < np; ++p) {
+            const float mp = ws_ml[2 * (base + p)];
+            const float w = mp == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mp - M);
+            L = fmaf(w, ws_ml[2 * (base + p) + 1], L);
+            o = fmaf(w, ws_acc[(base + p) * kD + d], o);
+        }
+        out[orow * kD + d] = (_Float16)(L > 0.f ? o / L : 0.f);
+    }
+}
+
 using PrefillFn = void (*)(_Float16*, const _Float16*, int32_t, const _Float16*, const _Float16*, const int32_t*,
                            int32_t, const int32_t*, const int32_t*, int32_t, int32_t, int32_t, float, int32_t,
-                           int64_t);
+                           int64_t, float*, float*, int32_t, int32_t);
 
 PrefillFn pick(int32_t b) {
     switch (b) {
@@ -491,13 +572,67 @@ PrefillFn pick(int32_t b) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Context split.  Workgroups per part: one per (KV head, sequence, row
+// tile).  When they are fewer than the resident slots (2 per CU, 512), the
+// context is cut into parts of at least 4 tiles (128 tokens) so that about
+// 1024 workgroups run, each leaving the partial (m, l, O) of its rows for a
+// merge kernel.  The bound on the context is max_blocks_per_seq *
+// block_size (host-known).
+struct SplitPlan {
+    int32_t row_tiles;
+    int32_t num_parts;
+    int32_t tiles_per_part;
+    size_t ml_bytes;
+    size_t total;
+};
+
+SplitPlan split_plan(int32_t num_tokens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                     int64_t len_cap, int32_t max_query_len) {
+    SplitPlan P{};
+    const int64_t g = num_heads / num_kv_heads;
+    P.row_tiles = (int32_t)(((int64_t)max_query_len * g + kRowsPerGroup - 1) / kRowsPerGroup);
+    const int64_t max_tiles = len_cap / kKvTile + 1;
+    const int64_t wgs = (int64_t)num_kv_heads * num_seqs * P.row_tiles;
+    int64_t parts = 1;
+    if (wgs > 0 && wgs < 512 && max_tiles >= 8) {
+        parts = (1024 + wgs - 1) / wgs;
+        if (parts > max_tiles / 4) parts = max_tiles / 4;
+        if (parts * P.row_tiles > 65535) parts = 65535 / P.row_tiles;
+        if (parts < 1) parts = 1;
+    }
+    P.tiles_per_part = (int32_t)((max_tiles + parts - 1) / parts);
+    P.num_parts = (int32_t)((max_tiles + P.tiles_per_part - 1) / P.tiles_per_part);
+    if (P.num_parts <= 1) {
+        P.num_parts = 1;
+        return P;
+    }
+    const size_t rows = (size_t)num_tokens * num_heads * P.num_parts;
+    P.ml_bytes = align_up(rows * 2 * sizeof(float), 256);
+    P.total = P.ml_bytes + align_up(rows * kD * sizeof(float), 256);
+    return P;
+}
+
 }  // namespace
+
+extern "C" size_t pa_prefill_workspace_size(int32_t num_tokens, int32_t num_seqs, int32_t num_heads,
+                                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                            int32_t max_blocks_per_seq, int32_t max_query_len) {
+    if (head_dim != kD || !pick(block_size) || num_tokens < 0 || num_seqs < 0 || num_heads <= 0 ||
+        num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || max_blocks_per_seq < 0 || max_query_len < 0)
+        return (size_t)-1;
+    return split_plan(num_tokens, num_seqs, num_heads, num_kv_heads, (int64_t)max_blocks_per_seq * block_size,
+                      max_query_len)
+        .total;
+}
 
 extern "C" int pa_prefill(void* out, const void* q, int32_t num_tokens, const void* k_cache, const void* v_cache,
                           const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                           const int32_t* query_start, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                           int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
-                          int32_t max_query_len, int32_t dtype, void* stream) {
+                          int32_t max_query_len, void* workspace, size_t workspace_bytes, int32_t dtype,
+                          void* stream) {
     if (dtype != PA_DTYPE_F16) return pa::fail(PA_ERR_UNSUPPORTED, "pa_prefill: dtype %d", dtype);
     if (head_dim != kD) return pa::fail(PA_ERR_UNSUPPORTED, "pa_prefill: head_dim %d (only %d)", head_dim, kD);
     if (!pick(block_size)) return pa::fail(PA_ERR_UNSUPPORTED, "pa_prefill: block_size %d", block_size);
@@ -505,27 +640,49 @@ extern "C" int pa_prefill(void* out, const void* q, int32_t num_tokens, const vo
         num_blocks <= 0 || max_blocks_per_seq < 0 || max_query_len < 0)
         return pa::fail(PA_ERR_INVALID, "pa_prefill: bad sizes (S=%d H=%d Hkv=%d NB=%d W=%d max_q=%d)", num_seqs,
                         num_heads, num_kv_heads, num_blocks, max_blocks_per_seq, max_query_len);
-    if (num_seqs > 65535 || num_kv_heads > 65535)
-        return pa::fail(PA_ERR_INVALID, "pa_prefill: num_seqs and num_kv_heads must be <= 65535");
+    if (num_seqs > 65535 || num_kv_heads > 65535 || num_heads > 65535)
+        return pa::fail(PA_ERR_INVALID, "pa_prefill: num_seqs and the head counts must be <= 65535");
     if (!std::isfinite(scale)) return pa::fail(PA_ERR_INVALID, "pa_prefill: scale is not finite");
     if (num_seqs == 0 || max_query_len == 0 || num_tokens == 0) return PA_OK;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
         return pa::fail(PA_ERR_INVALID, "pa_prefill: null pointer");
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
         return pa::fail(PA_ERR_INVALID, "pa_prefill: out, q and caches must be 16-byte aligned");
+    if (workspace && !aligned16(workspace))
+        return pa::fail(PA_ERR_INVALID, "pa_prefill: workspace must be 16-byte aligned");
     const int64_t g = num_heads / num_kv_heads;
     const int64_t row_tiles = ((int64_t)max_query_len * g + kRowsPerGroup - 1) / kRowsPerGroup;
     if (row_tiles > 65535)
         return pa::fail(PA_ERR_INVALID, "pa_prefill: max_query_len %d x %lld heads needs %lld row tiles (limit 65535)",
                         max_query_len, (long long)g, (long long)row_tiles);
     const int64_t len_cap = (int64_t)max_blocks_per_seq * block_size;
+    SplitPlan P = split_plan(num_tokens, num_seqs, num_heads, num_kv_heads, len_cap, max_query_len);
+    if (P.num_parts > 1 && (!workspace || workspace_bytes < P.total)) {
+        // no room for the partial states: one part per row tile
+        P.num_parts = 1;
+        P.tiles_per_part = (int32_t)(len_cap / kKvTile + 1);
+    }
+    float* ws_ml = P.num_parts > 1 ? static_cast<float*>(workspace) : nullptr;
+    float* ws_acc = P.num_parts > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + P.ml_bytes) : nullptr;
     const float scale_log2 = (float)((double)scale * kLog2e);
-    hipLaunchKernelGGL(pick(block_size), dim3((unsigned)num_kv_heads, (unsigned)num_seqs, (unsigned)row_tiles),
-                       dim3(kThreads), 0, static_cast<hipStream_t>(stream), static_cast<_Float16*>(out),
-                       static_cast<const _Float16*>(q), num_tokens, static_cast<const _Float16*>(k_cache),
-                       static_cast<const _Float16*>(v_cache), block_tables, max_blocks_per_seq, context_lens,
-                       query_start, num_heads, num_kv_heads, num_blocks, scale_log2, max_query_len, len_cap);
-    const hipError_t e = hipGetLastError();
+    auto st = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(pick(block_size),
+                       dim3((unsigned)num_kv_heads, (unsigned)num_seqs, (unsigned)(row_tiles * P.num_parts)),
+                       dim3(kThreads), 0, st, static_cast<_Float16*>(out), static_cast<const _Float16*>(q), num_tokens,
+                       static_cast<const _Float16*>(k_cache), static_cast<const _Float16*>(v_cache), block_tables,
+                       max_blocks_per_seq, context_lens, query_start, num_heads, num_kv_heads, num_blocks, scale_log2,
+                       max_query_len, len_cap, ws_ml, ws_acc, P.tiles_per_part, P.num_parts);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "pa_prefill: %s", hipGetErrorString(e));
+    if (P.num_parts > 1) {
+        hipLaunchKernelGGL(prefill_merge_kernel,
+                           dim3((unsigned)num_heads, (unsigned)num_seqs,
+                                (unsigned)((max_query_len + kMergeTokens - 1) / kMergeTokens)),
+                           dim3(kD), 0, st, static_cast<_Float16*>(out), (const float*)ws_ml, (const float*)ws_acc,
+                           num_tokens, context_lens, query_start, num_heads, num_kv_heads, max_query_len, len_cap,
+                           P.tiles_per_part, P.num_parts);
+        e = hipGetLastError();
+        if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "pa_prefill: %s", hipGetErrorString(e));
+    }
     return PA_OK;
 }

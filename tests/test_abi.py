@@ -138,10 +138,10 @@ def test_copy_blocks_rejects_bad_arguments():
 
 def _prefill_args(**kw):
     a = dict(out=16, q=16, T=4, k=16, v=16, tables=16, W=4, lens=16, qs=16, S=1, H=2, Hkv=2, D=128, B=16, NB=8,
-             scale=0.1, maxq=4, dtype=0, stream=None)
+             scale=0.1, maxq=4, ws=None, wsb=0, dtype=0, stream=None)
     a.update(kw)
     return (a["out"], a["q"], a["T"], a["k"], a["v"], a["tables"], a["W"], a["lens"], a["qs"], a["S"], a["H"],
-            a["Hkv"], a["D"], a["B"], a["NB"], a["scale"], a["maxq"], a["dtype"], a["stream"])
+            a["Hkv"], a["D"], a["B"], a["NB"], a["scale"], a["maxq"], a["ws"], a["wsb"], a["dtype"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -156,6 +156,7 @@ def _prefill_args(**kw):
     (dict(qs=None), pa.PA_ERR_INVALID),
     (dict(out=8), pa.PA_ERR_INVALID),               # misaligned
     (dict(maxq=1 << 30), pa.PA_ERR_INVALID),        # more row tiles than a grid holds
+    (dict(ws=8, wsb=4096), pa.PA_ERR_INVALID),      # misaligned workspace
 ])
 def test_prefill_rejects_bad_arguments_before_launch(kw, code):
     assert pa.lib().pa_prefill(*_prefill_args(**kw)) == code
@@ -166,6 +167,19 @@ def test_prefill_with_nothing_to_do_is_a_no_op():
     L = pa.lib()
     assert L.pa_prefill(*_prefill_args(S=0, out=None)) == pa.PA_OK
     assert L.pa_prefill(*_prefill_args(T=0, out=None)) == pa.PA_OK
+
+
+def test_prefill_workspace_size():
+    """Zero when the batch fills the GPU unsplit; otherwise (2 + D) x 4 bytes
+    per (token, head, context part), two 256-byte aligned regions."""
+    L = pa.lib()
+    assert L.pa_prefill_workspace_size(15360, 32, 32, 32, 128, 16, 49, 774) == 0        # 32 x 32 x 7 = 7168 workgroups
+    n = L.pa_prefill_workspace_size(64, 4, 32, 32, 128, 16, 512, 16)                  # 128 workgroups, 8192 tokens
+    parts = n // (64 * 32 * (128 + 2) * 4)
+    assert parts >= 2 and n % 256 == 0 and n >= 64 * 32 * parts * (128 + 2) * 4
+    assert L.pa_prefill_workspace_size(64, 4, 32, 32, 128, 16, 1, 16) == 0            # too short to split
+    assert L.pa_prefill_workspace_size(64, 4, 32, 32, 100, 16, 512, 16) == ctypes.c_size_t(-1).value
+    assert L.pa_prefill_workspace_size(64, 4, 32, 7, 128, 16, 512, 16) == ctypes.c_size_t(-1).value
 
 
 def test_swap_blocks_rejects_bad_arguments_before_launch():

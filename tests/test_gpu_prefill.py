@@ -23,11 +23,11 @@ def _queries(seed, ms, H, D):
     return q, np.concatenate([[0], np.cumsum(ms)]).astype(np.int32)
 
 
-def _gpu_prefill(dev, q, kc, vc, tables, lens, qs, scale, max_query_len=None):
+def _gpu_prefill(dev, q, kc, vc, tables, lens, qs, scale, max_query_len=None, split=True, workspace=None):
     out = torch.full(q.shape, float("nan"), dtype=torch.float16, device=dev)
     pa.pa_prefill(out, torch.from_numpy(q).to(dev), torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev),
                   torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), torch.from_numpy(qs).to(dev),
-                  scale, max_query_len=max_query_len)
+                  scale, max_query_len=max_query_len, split=split, workspace=workspace)
     torch.cuda.synchronize()
     return out
 
@@ -140,6 +140,56 @@ def test_prefill_rising_scores_move_the_running_maximum():
     out = _gpu_prefill(dev, q, kc, vc, tables, lens, qs, case.scale)
     ref = oracle.prefill(q, kc, vc, tables, lens, qs, case.scale)
     assert_attention_close(out, ref, "rising scores")
+
+
+@pytest.mark.parametrize("H,Hkv", [(8, 2), (4, 4)])
+def test_prefill_split_context(H, Hkv):
+    """Short chunks over long contexts with few sequences: the context is
+    split into parts merged by a second kernel.  Against the oracle, against
+    the unsplit kernel (same math, other summation order), bit for bit when
+    repeated, and through one workspace reused by a smaller call."""
+    dev = device()
+    lens_l = [3000, 2500, 1777]
+    ms = [8, 40, 1]
+    case = workloads.random_case(91 + H, lens_l, H, Hkv, 128, 16)
+    kc, vc, tables, lens = _oracle_cache(case)
+    q, qs = _queries(91, ms, H, 128)
+    T, W = int(qs[-1]), tables.shape[1]
+    need = pa.pa_prefill_workspace_size(T, 3, H, Hkv, 128, 16, W, max(ms))
+    assert need > 0                                                  # this batch splits
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    split = _gpu_prefill(dev, q, kc, vc, tables, lens, qs, case.scale, workspace=ws)
+    ref = oracle.prefill(q, kc, vc, tables, lens, qs, case.scale)
+    assert_attention_close(split, ref, f"split H={H}/{Hkv}")
+    whole = _gpu_prefill(dev, q, kc, vc, tables, lens, qs, case.scale, split=False)
+    assert_attention_close(whole, ref, f"unsplit H={H}/{Hkv}")
+    again = _gpu_prefill(dev, q, kc, vc, tables, lens, qs, case.scale, workspace=ws)
+    assert np.array_equal(bits(split), bits(again))
+    # the same workspace for a smaller batch (first two sequences)
+    q2, qs2 = np.ascontiguousarray(q[:48]), np.array([0, 8, 48], np.int32)
+    t2, l2 = np.ascontiguousarray(tables[:2]), np.ascontiguousarray(lens[:2])
+    small = _gpu_prefill(dev, q2, kc, vc, t2, l2, qs2, case.scale, workspace=ws)
+    assert_attention_close(small, oracle.prefill(q2, kc, vc, t2, l2, qs2, case.scale), "split, smaller batch")
+
+
+def test_prefill_split_with_bad_and_empty_sequences():
+    """Split context with a sequence whose new tokens exceed its context
+    (NaN rows), an empty one, and one skipped for a range outside [0, T)."""
+    dev = device()
+    case = workloads.random_case(95, [2000, 10, 1500, 1800], 4, 2, 128, 16)
+    kc, vc, tables, lens = _oracle_cache(case)
+    ms = [16, 0, 5, 7]
+    q, qs = _queries(95, ms, 4, 128)
+    lens_bad = lens.copy()
+    lens_bad[2] = 3                                                  # 5 new tokens > 3 cached
+    out = _gpu_prefill(dev, q, kc, vc, tables, lens_bad, qs, case.scale)
+    assert pa.pa_prefill_workspace_size(int(qs[-1]), 4, 4, 2, 128, 16, tables.shape[1], 16) > 0
+    o = out.float().cpu().numpy()
+    assert np.all(np.isnan(o[16:21]))
+    sel = np.r_[0:16, 21:28]
+    ref = oracle.prefill(np.ascontiguousarray(q[sel]), kc, vc, np.ascontiguousarray(tables[[0, 3]]),
+                         np.ascontiguousarray(lens[[0, 3]]), np.array([0, 16, 23], np.int32), case.scale)
+    assert_attention_close(out[sel], ref, "split, other sequences")
 
 
 def test_prefill_is_deterministic_and_blind_to_placement():
