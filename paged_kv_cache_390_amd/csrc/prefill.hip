@@ -575,11 +575,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Context split.  Workgroups per part: one per (KV head, sequence, row
-// tile).  When they are fewer than the resident slots (2 per CU, 512), the
-// context is cut into parts of at least 4 tiles (128 tokens) so that about
-// 1024 workgroups run, each leaving the partial (m, l, O) of its rows for a
-// merge kernel.  The bound on the context is max_blocks_per_seq *
-// block_size (host-known).
+// tile).  When they fill at most half the resident slots (2 per CU, 512),
+// the context is cut into floor(512 / workgroups) parts of at least 4 tiles
+// (128 tokens): one full round of workgroups, each leaving the partial
+// (m, l, O) of its rows for a merge kernel.  (A second, partial round costs
+// more than it brings: on 4 x 8192 cached + 32 new, 512 workgroups run in
+// 113 us, 768 in 149, 1024 in 147, 2048 in 203.)  The bound on the context
+// is max_blocks_per_seq * block_size (host-known).
 struct SplitPlan {
     int32_t row_tiles;
     int32_t num_parts;
@@ -596,8 +598,8 @@ SplitPlan split_plan(int32_t num_tokens, int32_t num_seqs, int32_t num_heads, in
     const int64_t max_tiles = len_cap / kKvTile + 1;
     const int64_t wgs = (int64_t)num_kv_heads * num_seqs * P.row_tiles;
     int64_t parts = 1;
-    if (wgs > 0 && wgs < 512 && max_tiles >= 8) {
-        parts = (1024 + wgs - 1) / wgs;
+    if (wgs > 0 && 2 * wgs <= 512 && max_tiles >= 8) {
+        parts = 512 / wgs;
         if (parts > max_tiles / 4) parts = max_tiles / 4;
         if (parts * P.row_tiles > 65535) parts = 65535 / P.row_tiles;
         if (parts < 1) parts = 1;
