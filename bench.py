@@ -100,8 +100,8 @@ def traffic_from_profiles(workload: str):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the decode path shards by sequence or KV head with no exchange, see DESIGN.md", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); the decode path would shard "
+              "by sequence or by KV head with no exchange between GPUs", file=sys.stderr)
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:
         sys.exit("bench.py: --steps >= 1 and --warmup >= 0 required")

@@ -41,7 +41,7 @@ Rules modelled:
     and back ("swap": [lpnh-1824136] 4.2 names it as a supported, slow
     option for serving very long contexts when latency can be traded).
 
-Readings where the pages leave a step open (also listed in the design doc):
+Readings where the pages leave a step open:
   * Fill level is tracked per sequence (its length) rather than per block;
     for an unshared block the two agree, and for a shared block the
     per-sequence length is what decides whether the writer's next slot is

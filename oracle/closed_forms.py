@@ -35,8 +35,8 @@ def block_bytes(block_size: int, num_layers: int, num_kv_heads: int,
     """Bytes one block id pins across all layers, K and V.
 
     The pool-size passage lists block_size x layers x KV heads x head_dim x 2
-    and drops the element width; it is restored here (reading noted in
-    DESIGN.md)."""
+    and drops the element width; it is restored here (a reading: the
+    listed factors count elements, the size asked for is in bytes)."""
     return block_size * num_layers * num_kv_heads * head_dim * 2 * dtype_bytes
 
 

@@ -194,7 +194,7 @@ def test_set_table_rejects_bad_tables():
 
 # ---------------------------------------------------------------------------
 # swap to / from the host pool ([lpnh-1824136] 4.2 names the operation; the
-# group semantics are this build's reading, pinned here by counting)
+# group semantics are a reading of that passage, pinned here by counting)
 # ---------------------------------------------------------------------------
 def _forked_group(nb=16, nh=16, B=4, prompt=10, samples=3):
     """A prompt of 10 tokens (2 full blocks + a 2-token tail) forked into
