@@ -40,9 +40,9 @@
 //    wave's first row and wholly valid skip the masks; the running maximum
 //    moves lazily (only when a tile's exceeds it by a factor above 2^8), so
 //    O is rarely rescaled.
-//  * PV: output column n of d-tile c is d = 8n + c; the lane reads its 8
-//    token rows' columns 8n..8n+7 and builds each B operand with 4
-//    v_perm_b32 (an 8 x 8 transpose of halves).
+//  * PV: output column n of d-tile c is d = 16c + n; the B operand (8
+//    tokens of one V column per lane) comes straight from the row-major V
+//    tile through two LDS transpose reads (ds_read_b64_tr_b16) per d-tile.
 //  * Each wave walks the tiles up to its own last row's position and writes
 //    its rows itself: 16 bytes per row, normalised by the row sums fetched
 //    with a cross-lane shuffle.
@@ -69,8 +69,10 @@ constexpr double kLog2e = 1.4426950408889634073599246810019;
 // touches fall in different banks), plus a flag per token (inside the
 // context and the pool).
 constexpr int kKvTile = 32;
-constexpr int kPitch = kD * 2 + 16;
+constexpr int kPitch = kD * 2 + 16;           // K rows
+constexpr int kPitchV = kD * 2 + 32;          // V rows (see pv in consume_lds_tile)
 constexpr int kTileBytes = kKvTile * kPitch;
+constexpr int kTileBytesV = kKvTile * kPitchV;
 
 typedef _Float16 half8_t_ __attribute__((ext_vector_type(8)));
 
@@ -154,7 +156,7 @@ __device__ __forceinline__ void store_tile(const Staged& st, unsigned char* buf,
         for (int i = 0; i < kStageRows; ++i) {
             const int row = stage_token0(0, wave, i) + (lane >> 4);
             *reinterpret_cast<u32x4*>(buf + row * kPitch + col * 16) = st.k[i];
-            *reinterpret_cast<u32x4*>(buf + kTileBytes + row * kPitch + col * 16) = st.v[i];
+            *reinterpret_cast<u32x4*>(buf + kTileBytes + row * kPitchV + col * 16) = st.v[i];
         }
     } else {
 #pragma unroll
@@ -162,7 +164,7 @@ __device__ __forceinline__ void store_tile(const Staged& st, unsigned char* buf,
             const int row = stage_token0(0, wave, i) + (lane >> 4);
             const u32x4 z = {0u, 0u, 0u, 0u};
             *reinterpret_cast<u32x4*>(buf + row * kPitch + col * 16) = st.ok[i] ? st.k[i] : z;
-            *reinterpret_cast<u32x4*>(buf + kTileBytes + row * kPitch + col * 16) = st.ok[i] ? st.v[i] : z;
+            *reinterpret_cast<u32x4*>(buf + kTileBytes + row * kPitchV + col * 16) = st.ok[i] ? st.v[i] : z;
         }
     }
 #pragma unroll
@@ -205,7 +207,7 @@ __device__ __forceinline__ float row_sum4(float x) {
 //     MFMA c takes d = 32c + 8*(l/16) + 0..7 in lane l (one 16-byte LDS read).
 //   PV: k = 32 tokens; lane (n, j) supplies P[row n][tokens 4j..4j+3 and
 //     16+4j..16+4j+3] -- exactly the scores it holds -- and V rows of the
-//     same tokens at columns 8n..8n+7; output column n of d-tile c is d = 8n+c.
+//     same tokens at column 16c + n for d-tile c (LDS transpose reads).
 // `interior` (uniform): every token of the tile is valid and at or before
 // the first row's position, so no score is masked.  The exponent of a
 // weight is one FMA of the raw score: c = scale * log2(e) > 0, so the raw
@@ -294,30 +296,33 @@ __device__ __forceinline__ void consume_lds_tile(Softmax (&st)[kNT], const unsig
                 for (int e = 0; e < 4; ++e) st[t].o[c][e] *= ar[e];
         }
     }
-    // V rows of the lane's 8 tokens of each sub-tile, columns 8n..8n+7; the
-    // B operand of d-tile c is element c of each -- an 8 x 8 transpose of
-    // halves, one v_perm_b32 per output dword (byte selectors: low halves of
-    // two dwords, or high halves)
+    // PV with the V operand read by ds_read_b64_tr_b16: within each 16 lanes
+    // it hands lane i element i%4 of the 8-byte pieces of lanes i/4 + 4e,
+    // e = 0..3.  Lane 4e + q of lane group j points at V[token tb + e][16c +
+    // 4q] (tb = 4j for k 0..3 of the B operand, 16 + 4j for k 4..7: the
+    // tokens whose weights the lane holds in P), so lane (n, j) receives
+    // V[tb + e][16c + n]: the B operand of d-tile c, output column n of d-tile
+    // c being d = 16c + n.  V rows are 288 bytes apart so that the 4 rows x 4
+    // pieces of one lane group fall in 32 different banks.
+    typedef short v4s_ __attribute__((ext_vector_type(4)));
+    const int e4 = (lane & 15) >> 2;
+    const int q4 = lane & 3;
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
-        u32x4 vv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int tok = 32 * u + ((i < 4) ? 4 * j + i : 16 + 4 * j + (i - 4));
-            vv[i] = *reinterpret_cast<const u32x4*>(vb + tok * kPitch + 16 * n);
-        }
+        const unsigned char* lo = vb + (32 * u + 4 * j + e4) * kPitchV + 8 * q4;
+        const unsigned char* hi = lo + 16 * kPitchV;
 #pragma unroll
         for (int c = 0; c < kDTiles; ++c) {
-            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-            const int dw = c >> 1;
-            const u32x4 b = {__builtin_amdgcn_perm(vv[1][dw], vv[0][dw], sel),
-                             __builtin_amdgcn_perm(vv[3][dw], vv[2][dw], sel),
-                             __builtin_amdgcn_perm(vv[5][dw], vv[4][dw], sel),
-                             __builtin_amdgcn_perm(vv[7][dw], vv[6][dw], sel)};
+            const v4s_ b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s_*)(lo + 32 * c));
+            const v4s_ b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4s_*)(hi + 32 * c));
+            const half4_t h0 = __builtin_bit_cast(half4_t, b0);
+            const half4_t h1 = __builtin_bit_cast(half4_t, b1);
+            const half8_t_ b = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
 #pragma unroll
             for (int t = 0; t < kNT; ++t)
-                st[t].o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p[t][u], __builtin_bit_cast(half8_t_, b),
-                                                                    st[t].o[c], 0, 0, 0);
+                st[t].o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p[t][u], b, st[t].o[c], 0, 0, 0);
         }
     }
 }
@@ -331,7 +336,7 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
                     int32_t num_blocks, float scale_log2, int32_t max_query_len, int64_t len_cap,
                     float* __restrict__ ws_ml, float* __restrict__ ws_acc, int32_t tiles_per_part,
                     int32_t num_parts) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2][2 * kTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2][kTileBytes + kTileBytesV];
     __shared__ __attribute__((aligned(4))) unsigned char lds_flags[2][kKvTile];
     const int kvh = blockIdx.x;
     const int s = blockIdx.y;
@@ -476,9 +481,9 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
                 const int rwi = row0 + 16 * t + rr;
                 const int64_t orow = ((int64_t)q0 + rwi / g) * num_heads + (int64_t)kvh * g + rwi % g;
                 const int64_t slot = orow * num_parts + part;
-                float* acc = ws_acc + slot * kD + 8 * nrow;
+                float* acc = ws_acc + slot * kD + nrow;
 #pragma unroll
-                for (int c = 0; c < kDTiles; ++c) acc[c] = st[t].o[c][e];
+                for (int c = 0; c < kDTiles; ++c) acc[16 * c] = st[t].o[c][e];
                 if (nrow == 0) {
                     ws_ml[2 * slot] = M;
                     ws_ml[2 * slot + 1] = L;
@@ -488,7 +493,7 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
     }
 
     // Rows 16t + 4*jg + e of the wave live in this lane's st[t].o[c][e] at
-    // column 8*nrow + c; their sums sit in lanes 4*jg + e.
+    // column 16c + nrow; their sums sit in lanes 4*jg + e.
 #pragma unroll
     for (int t = 0; t < kNT; ++t)
 #pragma unroll
@@ -499,10 +504,8 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
             const int rwi = row0 + 16 * t + rr;
             const int64_t orow = ((int64_t)q0 + rwi / g) * num_heads + (int64_t)kvh * g + rwi % g;
             const float inv = L > 0.f ? 1.f / L : 0.f;
-            half8_t h;
 #pragma unroll
-            for (int c = 0; c < kDTiles; ++c) h[c] = (_Float16)(st[t].o[c][e] * inv);
-            *reinterpret_cast<half8_t*>(out + orow * kD + 8 * nrow) = h;
+            for (int c = 0; c < kDTiles; ++c) out[orow * kD + 16 * c + nrow] = (_Float16)(st[t].o[c][e] * inv);
         }
 }
 
