@@ -337,6 +337,8 @@ def copy_bench(args, dev):
                       "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
                       "bytes_read_per_call": moved, "bytes_written_per_call": moved,
                       "us_per_call": round(avg * 1e6, 2),
+                      "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
                       "config": {"workload": "copy-blocks", "pairs": npairs, "block_bytes": block_bytes}}),
           flush=True)
 
