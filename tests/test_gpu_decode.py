@@ -182,6 +182,22 @@ def test_longest_first_order_changes_no_bit(H, Hkv):
     assert_attention_close(own, ref, f"128-token partitions H={H}/{Hkv}")
 
 
+def test_decode_order_of_a_large_batch():
+    """pa_decode_order over more sequences than its workgroup has threads
+    (each thread sorts several), lengths past the bound included: a
+    permutation, longest class first."""
+    dev = device()
+    rng = np.random.default_rng(23)
+    S, bound = 5000, 4096
+    lens = rng.integers(0, bound + 1, size=S).astype(np.int32)
+    lens[::97] = bound + 500                                      # beyond the bound: the longest class
+    order = pa.pa_decode_order(torch.from_numpy(lens).to(dev), bound).cpu().numpy()
+    assert sorted(order.tolist()) == list(range(S))
+    cls = np.minimum(np.maximum(lens[order], 0) // (bound // 1024 + 1), 1023)
+    assert np.all(np.diff(cls) <= 0)
+    assert pa.pa_decode_order(torch.zeros(0, dtype=torch.int32, device=dev), bound).numel() == 0
+
+
 def test_seq_order_entries_outside_the_batch_are_skipped():
     """A sequence the order leaves out keeps its rows untouched; an entry
     outside [0, S) does nothing."""
