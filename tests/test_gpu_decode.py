@@ -268,11 +268,13 @@ def test_table_entries_outside_the_pool_are_skipped():
     assert_attention_close(out, ref, "skipped ids")
 
 
-@pytest.mark.parametrize("P", [0, 256])
-def test_llama7b_decode_full_size(P):
+@pytest.mark.parametrize("P,given_order", [(0, True), (0, False), (256, False)])
+def test_llama7b_decode_full_size(P, given_order):
     """64 sequences, 32 heads x 128, B=16, n ~ U[1, 2048], pool of 8192 blocks
     filled N(0, 1), tables from one permutation; the new token of every
-    sequence is written by the product's scatter, then decoded."""
+    sequence is written by the product's scatter, then decoded -- with the
+    benchmark's launch configuration (default partition, the dispatch order
+    from pa_decode_order passed in), and with pa_decode ordering itself."""
     dev = device()
     w = workloads.llama7b_decode(seed=0)
     S, B, NB = len(w.lens), w.block_size, w.num_blocks
@@ -298,15 +300,17 @@ def test_llama7b_decode_full_size(P):
 
     pa.pa_reshape_and_cache(key, val, torch.from_numpy(slots).to(dev), kc, vc)
     out = torch.empty((S, w.num_heads, w.head_dim), dtype=torch.float16, device=dev)
-    pa.pa_decode(out, q, kc, vc, torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), w.scale, B,
-                 partition_size=P)
+    d_lens = torch.from_numpy(lens).to(dev)
+    order = pa.pa_decode_order(d_lens, width * B) if given_order else None
+    pa.pa_decode(out, q, kc, vc, torch.from_numpy(tables).to(dev), d_lens, w.scale, B, partition_size=P,
+                 seq_order=order)
     torch.cuda.synchronize()
 
     oracle.reshape_and_cache(key_h, val_h, slots, kc_h, vc_h)
     assert torch.equal(kc.view(torch.int16), torch.from_numpy(kc_h.view(np.int16)).to(dev))
     assert torch.equal(vc.view(torch.int16), torch.from_numpy(vc_h.view(np.int16)).to(dev))
     ref = oracle.decode(q_h, kc_h, vc_h, tables, lens, w.scale)
-    assert_attention_close(out, ref, f"llama7b P={P}")
+    assert_attention_close(out, ref, f"llama7b P={P} given order={given_order}")
 
 
 def test_long_context_split_partitions():

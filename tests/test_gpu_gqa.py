@@ -110,8 +110,10 @@ def test_gqa_decode_full_size(P):
     tables, lens = bm.get_tables(range(S), w.perm_tables.shape[1])
     pa.pa_reshape_and_cache(key, val, torch.from_numpy(slots).to(dev), kc, vc)
     out = torch.empty((S, w.num_heads, w.head_dim), dtype=torch.float16, device=dev)
-    pa.pa_decode(out, q, kc, vc, torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), w.scale, B,
-                 partition_size=P)
+    d_lens = torch.from_numpy(lens).to(dev)
+    order = pa.pa_decode_order(d_lens, w.perm_tables.shape[1] * B) if P == 0 else None   # as the benchmark runs it
+    pa.pa_decode(out, q, kc, vc, torch.from_numpy(tables).to(dev), d_lens, w.scale, B, partition_size=P,
+                 seq_order=order)
     torch.cuda.synchronize()
     oracle.reshape_and_cache(key_h, val_h, slots, kc_h, vc_h)
     assert torch.equal(kc.view(torch.int16), torch.from_numpy(kc_h.view(np.int16)).to(dev))
