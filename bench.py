@@ -74,11 +74,40 @@ def parse():
 KERNEL_SOURCES = {"llama7b": ("decode.hip",), "gqa": ("decode.hip", "decode_gqa.hip", "mfma_tile.h")}
 
 
+def code_tokens(text: str) -> str:
+    """The source with comments removed and whitespace runs folded to one
+    space: what the compiler sees, so that an edit of a comment keeps counter
+    summaries taken on the same code valid.  String and character literals
+    are kept whole (a '//' inside one is not a comment)."""
+    out = []
+    i, n = 0, len(text)
+    while i < n:
+        c = text[i]
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+            out.append(" ")
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(workload: str) -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES.get(workload, ("decode.hip",)):
-        with open(os.path.join(ROOT, "paged_kv_cache_390_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_390_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_tokens(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -17,6 +17,12 @@
 //    contexts still spread over all 256 CUs, and a second kernel merges the
 //    partial softmax states.  Sequences that fit one partition are finished
 //    by the first kernel directly.
+//  * Longest first: grid row y works on sequence order[y], a permutation
+//    that sorts the sequences by length (order_by_length_kernel, once per
+//    step via pa_decode_order or inside the call).  Workgroups start in grid
+//    order, and with a couple of workgroups per resident slot a long
+//    sequence that started last would run alone through the drain; longest
+//    processing time first keeps the drain short.
 //  * XCD balance: workgroups are dealt round-robin to the 8 XCDs in linear
 //    order, so the query head is the fastest grid dimension: every XCD then
 //    gets the same heads of every (sequence, partition), i.e. the same bytes
