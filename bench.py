@@ -14,15 +14,16 @@ One step = one decode iteration over the whole path:
   order  pa_decode_order sorts the sequences longest first (one small
          kernel, shared by every layer of the step);
   per layer (x32)
-         pa_reshape_and_cache writes the new token's K/V,
-         pa_decode runs attention for all 64 sequences.
+         pa_decode_append writes the new token's K/V into the cache and
+         runs attention for all 64 sequences in one launch (--fused 0:
+         pa_reshape_and_cache, then pa_decode).
 
 Printed: one JSON line.  `value` is KV GB/s over the whole step (bytes of
 cached K/V that decode must read, summed over layers, divided by wall time per
 step; no events inside the steps -- on this stack each recorded event costs
 several microseconds between kernels); `roofline` is the decode call alone:
-after the timed steps, --steps sweeps of pa_decode over the layers of the last
-step's batch run back to back, bracketed by HIP events on the launch stream,
+after the timed steps, --steps sweeps of the step's decode call over the
+layers of the last step's batch run back to back, bracketed by HIP events on the launch stream,
 and the average call duration divides the call's algorithmic KV bytes;
 `cpu_baseline` times the fp64 oracle on one layer of the same workload on the
 host cores.
@@ -64,6 +65,9 @@ def parse():
     p.add_argument("--batch", type=int, default=0, help="sequences (0: 64 for llama7b, 256 for gqa)")
     p.add_argument("--block-size", type=int, default=16)
     p.add_argument("--partition", type=int, default=0, help="decode partition size (0 = library default)")
+    p.add_argument("--fused", type=int, default=1,
+                   help="decode workloads: 1 writes the new K/V inside the decode call (pa_decode_append), "
+                        "0 runs pa_reshape_and_cache then pa_decode")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the oracle timing")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -220,6 +224,15 @@ def main():
 
     kv_per_token = 2 * Hkv * D * 2           # K and V, fp16, one layer
 
+    def decode_call(l):
+        if args.fused:
+            pa.pa_decode_append(out, q, key, val, kcs[l], vcs[l], d_tables, d_lens, w.scale, B,
+                                max_context_len=width * B, partition_size=part, workspace=workspace,
+                                seq_order=d_order)
+        else:
+            pa.pa_decode(out, q, kcs[l], vcs[l], d_tables, d_lens, w.scale, B, max_context_len=width * B,
+                         partition_size=part, workspace=workspace, seq_order=d_order)
+
     def step(i):
         b = i % nbuf
         if copied[b] is not None:
@@ -231,15 +244,18 @@ def main():
         ctx = int(h_lens[b].numpy().astype(np.int64).sum())
         d_tables.copy_(h_tables[b], non_blocking=True)
         d_lens.copy_(h_lens[b], non_blocking=True)
-        d_slots.copy_(h_slots[b], non_blocking=True)
+        if not args.fused:                   # the fused call takes each slot from the table
+            d_slots.copy_(h_slots[b], non_blocking=True)
         e = torch.cuda.Event()
         e.record(stream)
         copied[b] = e
         pa.pa_decode_order(d_lens, width * B, out=d_order)     # one dispatch order for every layer
         for l in range(L):
-            pa.pa_reshape_and_cache(key, val, d_slots, kcs[l], vcs[l])
-            pa.pa_decode(out, q, kcs[l], vcs[l], d_tables, d_lens, w.scale, B, max_context_len=width * B,
-                         partition_size=part, workspace=workspace, seq_order=d_order)
+            if args.fused:
+                decode_call(l)
+            else:
+                pa.pa_reshape_and_cache(key, val, d_slots, kcs[l], vcs[l])
+                decode_call(l)
         return ctx
 
     for i in range(W):
@@ -263,13 +279,13 @@ def main():
     tokens_per_s_layer = S * L / (wall / K)
 
     # ---- the decode call alone: K sweeps over the layers of the last step's
-    # batch, back to back, events only between sweeps
+    # batch, back to back, events only between sweeps (in fused mode each
+    # call writes the same new K/V into the same slots again)
     sweep_ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     sweep_ev[0].record(stream)
     for i in range(K):
         for l in range(L):
-            pa.pa_decode(out, q, kcs[l], vcs[l], d_tables, d_lens, w.scale, B, max_context_len=width * B,
-                         partition_size=part, workspace=workspace, seq_order=d_order)
+            decode_call(l)
         sweep_ev[i + 1].record(stream)
     torch.cuda.synchronize()
     dec_ms = [sweep_ev[i].elapsed_time(sweep_ev[i + 1]) / L for i in range(K)]
@@ -322,7 +338,9 @@ def main():
         "config": {"workload": wl_name, "batch": S, "block_size": B, "num_heads": H, "num_kv_heads": Hkv,
                    "head_dim": D, "context": ctx_desc, "layers_resident": L, "pool_blocks_per_layer": NB,
                    "partition_size": part or pa.pa_decode_default_partition(S, H, Hkv, D, B, width * B),
-                   "step": "host append+tables, H2D, decode order, per layer reshape_and_cache + decode"},
+                   "step": ("host append+tables, H2D, decode order, per layer pa_decode_append (new K/V "
+                            "written inside the decode call)" if args.fused else
+                            "host append+tables, H2D, decode order, per layer reshape_and_cache + decode")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "cpu_baseline": cpu,

@@ -149,6 +149,45 @@ int pa_decode(void *out, const void *q, const void *k_cache,
               void *workspace, size_t workspace_bytes,
               const int32_t *seq_order, int32_t dtype, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Decode with the step's cache write folded in: pa_reshape_and_cache of one
+ * new token per sequence followed by pa_decode, in one launch (the write
+ * scatters the token into its block, [lpnh-1824136] 3.1; the attention is
+ * pa_decode's).  Sequence s's new token sits at position n - 1 (n =
+ * context_lens[s], which counts it):
+ *
+ *   key, value     device, fp16; the token of sequence s, KV head h at
+ *                  element s * kv_token_stride + h * head_dim (head_dim
+ *                  contiguous); 16-byte aligned
+ *   kv_token_stride elements between consecutive sequences' tokens, a
+ *                  multiple of 8 and >= num_kv_heads * head_dim
+ *   k_cache, v_cache  as for pa_decode, and written: the token goes to
+ *                  block block_tables[s][(n-1) / block_size], row (n-1) %
+ *                  block_size -- the slot the block manager's append
+ *                  reserved -- bit for bit.  A table entry outside
+ *                  [0, num_blocks) writes nothing and, as in pa_decode,
+ *                  the token takes no part in the softmax.
+ * Every other argument, the output and the error behaviour are those of
+ * pa_decode.  The cache is read for positions < n - 1 only; the new token's
+ * K/V come from key / value, so the result does not depend on the slot's
+ * contents before the call.  Sequences with n == 0, or with n above
+ * max_context_len or the table width, write nothing.  The written block
+ * must not be shared with another sequence of the call (the block
+ * manager's copy-on-write guarantees that for the last block of a
+ * sequence).
+ * ------------------------------------------------------------------------ */
+int pa_decode_append(void *out, const void *q, const void *key,
+                     const void *value, int64_t kv_token_stride,
+                     void *k_cache, void *v_cache,
+                     const int32_t *block_tables, int32_t max_blocks_per_seq,
+                     const int32_t *context_lens, int32_t num_seqs,
+                     int32_t num_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                     float scale, int32_t max_context_len,
+                     int32_t partition_size, void *workspace,
+                     size_t workspace_bytes, const int32_t *seq_order,
+                     int32_t dtype, void *stream);
+
 /* Longest-first dispatch order for pa_decode: seq_order (device, int32
  * [num_seqs], written) becomes a permutation of 0 .. num_seqs - 1 with the
  * sequences sorted by context_lens into 1024 classes of

@@ -8,7 +8,7 @@ slots and copy-on-write pairs.  PyTorch only provides device memory and the
 current HIP stream.  There is no fallback: if the library is not built, every
 call raises.
 
-Functions carry the C names: ``pa_reshape_and_cache``, ``pa_decode``,
+Functions carry the C names: ``pa_reshape_and_cache``, ``pa_decode``, ``pa_decode_append``,
 ``pa_decode_order``, ``pa_decode_workspace_size``, ``pa_prefill``, ``pa_prefill_workspace_size``, ``pa_copy_blocks``, ``pa_swap_blocks``;
 ``BlockManager`` wraps the ``pa_bm_*`` calls.
 """
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         "pa_reshape_and_cache": ([P, P, i64, P, i32, P, P, i32, i32, i32, i32, i32, P], ctypes.c_int),
         "pa_decode": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P, sz, P, i32, P],
                       ctypes.c_int),
+        "pa_decode_append": ([P, P, P, P, i64, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P,
+                              sz, P, i32, P], ctypes.c_int),
         "pa_prefill": ([P, P, i32, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, f32, i32, P, sz, i32, P],
                        ctypes.c_int),
         "pa_decode_order": ([P, P, i32, i32, P], ctypes.c_int),
@@ -192,17 +194,10 @@ def pa_decode_default_partition(num_seqs: int, num_heads: int, num_kv_heads: int
     return p
 
 
-def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
-              block_size: Optional[int] = None, max_context_len: Optional[int] = None,
-              partition_size: int = 0, workspace=None, seq_order=None) -> None:
-    """out[S, H, D] = softmax(scale * K q) V for each sequence over its first
-    context_lens[s] cached tokens, found through block_tables[S, W].
-
-    max_context_len defaults to W * block_size (a bound known without reading
-    context_lens back).  workspace (a uint8 device tensor) is allocated from
-    torch's caching allocator when needed and not given.  seq_order (int32
-    device tensor [S], from pa_decode_order) is the dispatch order shared by
-    the layers of a step; without it pa_decode computes one per call."""
+def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, block_size, max_context_len,
+                 partition_size, workspace, seq_order):
+    """Checks shared by pa_decode and pa_decode_append; returns the sizes
+    and the workspace / order pointers."""
     torch = _torch()
     _dev_tensor(k_cache, "k_cache", torch.float16, 4)
     _dev_tensor(v_cache, "v_cache", torch.float16, 4)
@@ -236,10 +231,52 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float
         if seq_order.shape[0] != S:
             raise ValueError("seq_order must have one entry per sequence")
         order_ptr = seq_order.data_ptr()
+    return S, H, Hkv, D, B, NB, W, int(max_context_len), ws_ptr, ws_bytes, order_ptr
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+              block_size: Optional[int] = None, max_context_len: Optional[int] = None,
+              partition_size: int = 0, workspace=None, seq_order=None) -> None:
+    """out[S, H, D] = softmax(scale * K q) V for each sequence over its first
+    context_lens[s] cached tokens, found through block_tables[S, W].
+
+    max_context_len defaults to W * block_size (a bound known without reading
+    context_lens back).  workspace (a uint8 device tensor) is allocated from
+    torch's caching allocator when needed and not given.  seq_order (int32
+    device tensor [S], from pa_decode_order) is the dispatch order shared by
+    the layers of a step; without it pa_decode computes one per call."""
+    S, H, Hkv, D, B, NB, W, mcl, ws_ptr, ws_bytes, order_ptr = _decode_args(
+        out, q, k_cache, v_cache, block_tables, context_lens, block_size, max_context_len, partition_size,
+        workspace, seq_order)
     _check(lib().pa_decode(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                            block_tables.data_ptr(), W, context_lens.data_ptr(), S, H, Hkv, D, B, NB,
-                           float(scale), int(max_context_len), int(partition_size), ws_ptr, ws_bytes,
+                           float(scale), mcl, int(partition_size), ws_ptr, ws_bytes,
                            order_ptr, PA_DTYPE_F16, _stream(q.device)), "pa_decode")
+
+
+def pa_decode_append(out, q, key, value, k_cache, v_cache, block_tables, context_lens, scale: float,
+                     block_size: Optional[int] = None, max_context_len: Optional[int] = None,
+                     partition_size: int = 0, workspace=None, seq_order=None) -> None:
+    """pa_reshape_and_cache of one new token per sequence followed by
+    pa_decode, in one call: key/value [S, Hkv, D] (fp16, head_dim
+    contiguous, any 16-byte-aligned token stride) hold sequence s's token at
+    position context_lens[s] - 1; it is written into the cache at that
+    position's slot of block_tables and attended to with the cached ones."""
+    torch = _torch()
+    S, H, Hkv, D, B, NB, W, mcl, ws_ptr, ws_bytes, order_ptr = _decode_args(
+        out, q, k_cache, v_cache, block_tables, context_lens, block_size, max_context_len, partition_size,
+        workspace, seq_order)
+    _dev_tensor(key, "key", torch.float16, 3, contiguous=False)
+    _dev_tensor(value, "value", torch.float16, 3, contiguous=False)
+    if tuple(key.shape) != (S, Hkv, D) or tuple(value.shape) != (S, Hkv, D):
+        raise ValueError(f"key/value must be [{S}, {Hkv}, {D}]")
+    if key.stride() != value.stride() or key.stride(2) != 1 or key.stride(1) != D:
+        raise ValueError("key and value need equal strides with contiguous [Hkv, D] rows")
+    _check(lib().pa_decode_append(out.data_ptr(), q.data_ptr(), key.data_ptr(), value.data_ptr(), key.stride(0),
+                                  k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), W,
+                                  context_lens.data_ptr(), S, H, Hkv, D, B, NB, float(scale), mcl,
+                                  int(partition_size), ws_ptr, ws_bytes, order_ptr, PA_DTYPE_F16,
+                                  _stream(q.device)), "pa_decode_append")
 
 
 def pa_decode_order(context_lens, max_context_len: int, out=None):

@@ -30,26 +30,28 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One lane per (token, head, VEC-element chunk); K and V move together.
+// One lane per (head, VEC-element chunk) of a token; K and V move together.
+// Grid x = token, y = group of lanes (64 to kThreads per workgroup) over the
+// token's (head, chunk) pairs: the token's slot is read once per workgroup (a uniform, scalar
+// load), and the chunk count and -- when it is a power of two -- the block
+// size turn divisions into shifts, so the stores wait on one load only.
 template <int VEC>
 __global__ void __launch_bounds__(kThreads)
 scatter_kv_kernel(const uint16_t* __restrict__ key, const uint16_t* __restrict__ value,
-                  int64_t token_stride, const int64_t* __restrict__ slots, int64_t work,
+                  int64_t token_stride, const int64_t* __restrict__ slots,
                   uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
-                  int64_t pool_slots, int32_t num_kv_heads, int32_t block_size,
-                  int32_t head_dim) {
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (i >= work) return;
-    const int32_t chunks = head_dim / VEC;
-    const int64_t per_token = (int64_t)num_kv_heads * chunks;
-    const int64_t t = i / per_token;
-    const int32_t r = (int32_t)(i - t * per_token);
-    const int32_t h = r / chunks;
-    const int32_t c = r - h * chunks;
+                  int64_t pool_slots, int32_t per_token, int32_t chunk_shift, int32_t block_size,
+                  int32_t block_shift, int32_t head_dim) {
+    const int64_t t = blockIdx.x;
+    const int32_t r = (int32_t)(blockIdx.y * blockDim.x + threadIdx.x);
+    if (r >= per_token) return;
     const int64_t slot = slots[t];
     if (slot < 0 || slot >= pool_slots) return;            // padding / outside the pool
-    const int64_t blk = slot / block_size;
+    const int64_t blk = block_shift >= 0 ? slot >> block_shift : slot / block_size;
     const int64_t row = slot - blk * block_size;
+    const int32_t h = r >> chunk_shift;
+    const int32_t c = r - (h << chunk_shift);
+    const int32_t num_kv_heads = per_token >> chunk_shift;
     const int64_t src = t * token_stride + (int64_t)h * head_dim + (int64_t)c * VEC;
     const int64_t dst = ((blk * num_kv_heads + h) * block_size + row) * head_dim + (int64_t)c * VEC;
     if constexpr (VEC == 8) {
@@ -164,21 +166,27 @@ extern "C" int pa_reshape_and_cache(const void* key, const void* value, int64_t 
     const bool vec = aligned16(key) && aligned16(value) && aligned16(k_cache) && aligned16(v_cache) &&
                      kv_token_stride % 8 == 0;
     const int vecw = vec ? 8 : 1;
-    const int64_t work = (int64_t)num_tokens * num_kv_heads * (head_dim / vecw);
-    const int64_t blocks = (work + kThreads - 1) / kThreads;
-    if (blocks > 0x7fffffff) return pa::fail(PA_ERR_INVALID, "pa_reshape_and_cache: too many tokens");
+    const int64_t per_token = (int64_t)num_kv_heads * (head_dim / vecw);
+    int32_t threads = 64;                                  // lanes per workgroup: up to one per pair
+    while (threads < kThreads && threads < per_token) threads *= 2;
+    const int64_t groups = (per_token + threads - 1) / threads;
+    if (groups > 65535)
+        return pa::fail(PA_ERR_INVALID, "pa_reshape_and_cache: num_kv_heads * head_dim too large");
+    const int32_t chunk_shift = __builtin_ctz((unsigned)(head_dim / vecw));   // head_dim / vecw: a power of two
+    const int32_t block_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
     const int64_t pool_slots = (int64_t)num_blocks * block_size;
     auto st = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)num_tokens, (unsigned)groups);
     if (vec)
-        hipLaunchKernelGGL(scatter_kv_kernel<8>, dim3((unsigned)blocks), dim3(kThreads), 0, st,
-                           static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
-                           kv_token_stride, slot_mapping, work, static_cast<uint16_t*>(k_cache),
-                           static_cast<uint16_t*>(v_cache), pool_slots, num_kv_heads, block_size, head_dim);
+        hipLaunchKernelGGL(scatter_kv_kernel<8>, grid, dim3((unsigned)threads), 0, st, static_cast<const uint16_t*>(key),
+                           static_cast<const uint16_t*>(value), kv_token_stride, slot_mapping,
+                           static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), pool_slots,
+                           (int32_t)per_token, chunk_shift, block_size, block_shift, head_dim);
     else
-        hipLaunchKernelGGL(scatter_kv_kernel<1>, dim3((unsigned)blocks), dim3(kThreads), 0, st,
-                           static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
-                           kv_token_stride, slot_mapping, work, static_cast<uint16_t*>(k_cache),
-                           static_cast<uint16_t*>(v_cache), pool_slots, num_kv_heads, block_size, head_dim);
+        hipLaunchKernelGGL(scatter_kv_kernel<1>, grid, dim3((unsigned)threads), 0, st, static_cast<const uint16_t*>(key),
+                           static_cast<const uint16_t*>(value), kv_token_stride, slot_mapping,
+                           static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), pool_slots,
+                           (int32_t)per_token, chunk_shift, block_size, block_shift, head_dim);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "pa_reshape_and_cache: %s", hipGetErrorString(e));
     return PA_OK;

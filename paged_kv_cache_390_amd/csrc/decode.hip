@@ -168,14 +168,23 @@ __device__ __forceinline__ void consume(RowState& r, const StepBuf& b, const Fra
     r.m = m_new;
 }
 
-template <int D, int B>
+// kAppend: the last position n - 1 of every sequence holds the token of
+// this step, whose K/V come from new_k / new_v (token s, KV head h at s *
+// new_stride + h * D) instead of the cache; the workgroup whose partition
+// holds it folds it in as a one-row step and -- for the first query head of
+// its KV head -- writes it into the cache through k_write / v_write.  The
+// cache is read for positions < n - 1 only, so no workgroup reads the row
+// being written.
+template <int D, int B, bool kAppend>
 __global__ void __launch_bounds__(kThreads)
 decode_partition_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
                         const int32_t* __restrict__ order, const _Float16* __restrict__ q, const _Float16* __restrict__ k_cache,
                         const _Float16* __restrict__ v_cache, const int32_t* __restrict__ tables,
                         int32_t max_blocks, const int32_t* __restrict__ lens, int32_t num_heads,
                         int32_t num_kv_heads, int32_t num_blocks, float scale_log2, int32_t part_size,
-                        int32_t num_parts, int64_t len_cap) {
+                        int32_t num_parts, int64_t len_cap, const _Float16* __restrict__ new_k,
+                        const _Float16* __restrict__ new_v, int64_t new_stride, _Float16* __restrict__ k_write,
+                        _Float16* __restrict__ v_write) {
     using G = Geo<D, B>;
     constexpr int LPT = G::LPT;
     constexpr int TPL = G::TPL;
@@ -197,7 +206,8 @@ decode_partition_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, f
     const int part = blockIdx.z;
     const int start = part * part_size;
     if (part > 0 && start >= n) return;
-    const int end = min(start + part_size, n);
+    const int cached = kAppend && n > 0 ? n - 1 : n;   // positions read from the cache
+    const int end = min(start + part_size, cached);
     const int np = (n + part_size - 1) / part_size;   // partitions of this sequence
     const int kvh = h / (num_heads / num_kv_heads);
 
@@ -213,6 +223,15 @@ decode_partition_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, f
     r.l = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) r.acc[i] = 0.f;
+
+    // append mode: the new token's K/V, loaded now by every lane (a valid
+    // address for all) so that the load hides under the main loop
+    u32x4 new_kf = {0u, 0u, 0u, 0u}, new_vf = {0u, 0u, 0u, 0u};
+    if constexpr (kAppend) {
+        const int64_t src = (int64_t)s * new_stride + (int64_t)kvh * D + col * 8;
+        new_kf = *reinterpret_cast<const u32x4*>(new_k + src);
+        new_vf = *reinterpret_cast<const u32x4*>(new_v + src);
+    }
 
     const int ntok = end > start ? end - start : 0;
     const int nsteps = ntok / CH;               // steps whose CH tokens are all < end
@@ -305,6 +324,31 @@ decode_partition_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, f
             }
         }
         consume<D>(r, b, qf, scale_log2);
+    }
+    if constexpr (kAppend) {
+        const int pos = n - 1;                  // the new token
+        if (n > 0 && pos >= start && pos < start + part_size && wave == kWaves - 1) {
+            const int32_t phys = trow[pos / B];
+            const bool ok = (uint32_t)phys < (uint32_t)num_blocks;   // as a cached row behind a skipped id
+            StepBuf b;
+#pragma unroll
+            for (int j = 0; j < kLoadsPerStep; ++j) {
+                b.k[j] = u32x4{0, 0, 0, 0};
+                b.v[j] = u32x4{0, 0, 0, 0};
+                b.valid[j] = false;
+            }
+            if (row == 0) {
+                b.k[0] = new_kf;
+                b.v[0] = new_vf;
+                b.valid[0] = ok;
+            }
+            consume<D>(r, b, qf, scale_log2);
+            if (row == 0 && ok && h % (num_heads / num_kv_heads) == 0) {
+                const int64_t off = (int64_t)kvh * G::SLAB + (int64_t)phys * blk_stride + (int64_t)(pos % B) * D + col * 8;
+                *reinterpret_cast<u32x4*>(k_write + off) = b.k[0];
+                *reinterpret_cast<u32x4*>(v_write + off) = b.v[0];
+            }
+        }
     }
     const float m = r.m, l = r.l;
     const float* acc = r.acc;
@@ -467,32 +511,33 @@ Layout workspace_layout(int32_t num_seqs, int32_t num_heads, int32_t head_dim, i
 
 using MainFn = void (*)(_Float16*, float*, float*, const int32_t*, const _Float16*, const _Float16*, const _Float16*,
                         const int32_t*, int32_t, const int32_t*, int32_t, int32_t, int32_t, float, int32_t,
-                        int32_t, int64_t);
+                        int32_t, int64_t, const _Float16*, const _Float16*, int64_t, _Float16*, _Float16*);
 using ReduceFn = void (*)(_Float16*, const float*, const float*, const int32_t*, const int32_t*, int32_t, int32_t,
                           int32_t, int64_t);
 
-template <int D>
+template <int D, bool kAppend>
 MainFn pick_main(int32_t b) {
     switch (b) {
-        case 1: return decode_partition_kernel<D, 1>;
-        case 2: return decode_partition_kernel<D, 2>;
-        case 4: return decode_partition_kernel<D, 4>;
-        case 8: return decode_partition_kernel<D, 8>;
-        case 16: return decode_partition_kernel<D, 16>;
-        case 32: return decode_partition_kernel<D, 32>;
-        case 64: return decode_partition_kernel<D, 64>;
-        case 128: return decode_partition_kernel<D, 128>;
+        case 1: return decode_partition_kernel<D, 1, kAppend>;
+        case 2: return decode_partition_kernel<D, 2, kAppend>;
+        case 4: return decode_partition_kernel<D, 4, kAppend>;
+        case 8: return decode_partition_kernel<D, 8, kAppend>;
+        case 16: return decode_partition_kernel<D, 16, kAppend>;
+        case 32: return decode_partition_kernel<D, 32, kAppend>;
+        case 64: return decode_partition_kernel<D, 64, kAppend>;
+        case 128: return decode_partition_kernel<D, 128, kAppend>;
         default: return nullptr;
     }
 }
 
+template <bool kAppend>
 MainFn pick_main(int32_t d, int32_t b) {
     switch (d) {
-        case 16: return pick_main<16>(b);
-        case 32: return pick_main<32>(b);
-        case 64: return pick_main<64>(b);
-        case 128: return pick_main<128>(b);
-        case 256: return pick_main<256>(b);
+        case 16: return pick_main<16, kAppend>(b);
+        case 32: return pick_main<32, kAppend>(b);
+        case 64: return pick_main<64, kAppend>(b);
+        case 128: return pick_main<128, kAppend>(b);
+        case 256: return pick_main<256, kAppend>(b);
         default: return nullptr;
     }
 }
@@ -597,44 +642,61 @@ extern "C" int pa_decode_order(int32_t* seq_order, const int32_t* context_lens, 
     return PA_OK;
 }
 
-extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                         const int32_t* block_tables, int32_t max_blocks_per_seq,
-                         const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
-                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                         float scale, int32_t max_context_len, int32_t partition_size, void* workspace,
-                         size_t workspace_bytes, const int32_t* seq_order, int32_t dtype, void* stream) {
-    if (dtype != PA_DTYPE_F16) return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: dtype %d", dtype);
-    if (!supported_head_dim(head_dim)) return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d", head_dim);
+namespace {
+
+// The step's new tokens when pa_decode_append folds their write into the
+// call (null otherwise).
+struct Append {
+    const _Float16* key;
+    const _Float16* value;
+    int64_t stride;
+};
+
+int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                int32_t num_blocks, float scale, int32_t max_context_len, int32_t partition_size, void* workspace,
+                size_t workspace_bytes, const int32_t* seq_order, int32_t dtype, void* stream, const Append* app) {
+    if (dtype != PA_DTYPE_F16) return pa::fail(PA_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
+    if (!supported_head_dim(head_dim)) return pa::fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d", fn, head_dim);
     if (!supported_block_size(block_size))
-        return pa::fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d", block_size);
+        return pa::fail(PA_ERR_UNSUPPORTED, "%s: block_size %d", fn, block_size);
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
         num_blocks <= 0 || max_blocks_per_seq < 0 || max_context_len < 0 || partition_size < 0)
-        return pa::fail(PA_ERR_INVALID, "pa_decode: bad sizes (S=%d H=%d Hkv=%d NB=%d W=%d max_len=%d P=%d)",
+        return pa::fail(PA_ERR_INVALID, "%s: bad sizes (S=%d H=%d Hkv=%d NB=%d W=%d max_len=%d P=%d)", fn,
                         num_seqs, num_heads, num_kv_heads, num_blocks, max_blocks_per_seq, max_context_len,
                         partition_size);
     if (partition_size % kPartitionQuantum != 0)
-        return pa::fail(PA_ERR_INVALID, "pa_decode: partition_size %d is not a multiple of %d", partition_size,
+        return pa::fail(PA_ERR_INVALID, "%s: partition_size %d is not a multiple of %d", fn, partition_size,
                         kPartitionQuantum);
     if (num_seqs > 65535 || num_heads > 65535)
-        return pa::fail(PA_ERR_INVALID, "pa_decode: num_seqs and num_heads must be <= 65535");
-    if (!std::isfinite(scale)) return pa::fail(PA_ERR_INVALID, "pa_decode: scale is not finite");
+        return pa::fail(PA_ERR_INVALID, "%s: num_seqs and num_heads must be <= 65535", fn);
+    if (!std::isfinite(scale)) return pa::fail(PA_ERR_INVALID, "%s: scale is not finite", fn);
     if (num_seqs == 0) return PA_OK;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
-        return pa::fail(PA_ERR_INVALID, "pa_decode: null pointer");
+        return pa::fail(PA_ERR_INVALID, "%s: null pointer", fn);
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
-        return pa::fail(PA_ERR_INVALID, "pa_decode: out, q and caches must be 16-byte aligned");
+        return pa::fail(PA_ERR_INVALID, "%s: out, q and caches must be 16-byte aligned", fn);
+    if (app) {
+        if (!app->key || !app->value) return pa::fail(PA_ERR_INVALID, "%s: null key or value", fn);
+        if (!aligned16(app->key) || !aligned16(app->value) || app->stride % 8 != 0)
+            return pa::fail(PA_ERR_INVALID, "%s: key, value and kv_token_stride must be 16-byte aligned", fn);
+        if (app->stride < (int64_t)num_kv_heads * head_dim)
+            return pa::fail(PA_ERR_INVALID, "%s: kv_token_stride %lld < num_kv_heads * head_dim", fn,
+                            (long long)app->stride);
+    }
 
     const int32_t p = partition_size ? partition_size
                                      : default_partition(num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                                                          max_context_len);
     const Layout L = workspace_layout(num_seqs, num_heads, head_dim, max_context_len, p);
     if (L.num_parts > 1) {
-        if (!workspace) return pa::fail(PA_ERR_INVALID, "pa_decode: workspace of %zu bytes required", L.total);
+        if (!workspace) return pa::fail(PA_ERR_INVALID, "%s: workspace of %zu bytes required", fn, L.total);
         if (workspace_bytes < L.total)
-            return pa::fail(PA_ERR_INVALID, "pa_decode: workspace %zu < %zu bytes", workspace_bytes, L.total);
+            return pa::fail(PA_ERR_INVALID, "%s: workspace %zu < %zu bytes", fn, workspace_bytes, L.total);
     }
     if (workspace && !aligned16(workspace))
-        return pa::fail(PA_ERR_INVALID, "pa_decode: workspace must be 16-byte aligned");
+        return pa::fail(PA_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
     // the caller's order if given; else one computed here into the
     // workspace (with one partition the workspace only holds that order, and
     // without one -- NULL or smaller -- the sequences run in index order).
@@ -644,7 +706,7 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const vo
                                (int64_t)grid_rows(num_seqs, num_heads, num_kv_heads, head_dim, block_size) *
                                        L.num_parts > resident_slots(num_heads, num_kv_heads, head_dim, block_size);
     if (L.num_parts > 65535)
-        return pa::fail(PA_ERR_INVALID, "pa_decode: max_context_len %d needs %d partitions of %d (limit 65535)",
+        return pa::fail(PA_ERR_INVALID, "%s: max_context_len %d needs %d partitions of %d (limit 65535)", fn,
                         max_context_len, L.num_parts, p);
     const int64_t len_cap_tables = (int64_t)max_blocks_per_seq * block_size;
     const int64_t len_cap_grid = (int64_t)L.num_parts * p;
@@ -662,7 +724,7 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const vo
     if (own_order) {
         launch_order(own_order, context_lens, num_seqs, max_context_len, st);
         e = hipGetLastError();
-        if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "pa_decode: %s", hipGetErrorString(e));
+        if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
     }
 
     const int32_t group = num_heads / num_kv_heads;
@@ -671,25 +733,58 @@ extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const vo
         pa::DecodeLaunch a{static_cast<_Float16*>(out), ws_ml, ws_acc, order, static_cast<const _Float16*>(q),
                            static_cast<const _Float16*>(k_cache), static_cast<const _Float16*>(v_cache),
                            block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads,
-                           num_blocks, block_size, scale_log2, p, L.num_parts, len_cap, st};
+                           num_blocks, block_size, scale_log2, p, L.num_parts, len_cap, st,
+                           app ? app->key : nullptr, app ? app->value : nullptr, app ? app->stride : 0};
         e = pa::launch_gqa_mfma(a);
     } else {
-        MainFn main_fn = pick_main(head_dim, block_size);
+        MainFn main_fn = app ? pick_main<true>(head_dim, block_size) : pick_main<false>(head_dim, block_size);
+        // the cache pointers double as write pointers in append mode: the
+        // kernel writes only the row of each sequence's last position, which
+        // no workgroup reads from the cache
         hipLaunchKernelGGL(main_fn, dim3((unsigned)num_heads, (unsigned)num_seqs, (unsigned)L.num_parts),
                            dim3(kThreads), 0, st, static_cast<_Float16*>(out), ws_ml, ws_acc, order,
                            static_cast<const _Float16*>(q), static_cast<const _Float16*>(k_cache),
                            static_cast<const _Float16*>(v_cache), block_tables, max_blocks_per_seq, context_lens,
-                           num_heads, num_kv_heads, num_blocks, scale_log2, p, L.num_parts, len_cap);
+                           num_heads, num_kv_heads, num_blocks, scale_log2, p, L.num_parts, len_cap,
+                           app ? app->key : nullptr, app ? app->value : nullptr, app ? app->stride : (int64_t)0,
+                           app ? static_cast<_Float16*>(const_cast<void*>(k_cache)) : nullptr,
+                           app ? static_cast<_Float16*>(const_cast<void*>(v_cache)) : nullptr);
         e = hipGetLastError();
     }
-    if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "pa_decode: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
     if (L.num_parts > 1) {
         const unsigned threads = head_dim < 64 ? 64u : (unsigned)head_dim;
         hipLaunchKernelGGL(pick_reduce(head_dim), dim3((unsigned)num_heads, (unsigned)num_seqs), dim3(threads), 0,
                            st, static_cast<_Float16*>(out), (const float*)ws_ml, (const float*)ws_acc, order,
                            context_lens, num_heads, p, L.num_parts, len_cap);
         e = hipGetLastError();
-        if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "pa_decode: %s", hipGetErrorString(e));
+        if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
     }
     return PA_OK;
+}
+
+}  // namespace
+
+extern "C" int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                         float scale, int32_t max_context_len, int32_t partition_size, void* workspace,
+                         size_t workspace_bytes, const int32_t* seq_order, int32_t dtype, void* stream) {
+    return decode_impl("pa_decode", out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                       num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, max_context_len,
+                       partition_size, workspace, workspace_bytes, seq_order, dtype, stream, nullptr);
+}
+
+extern "C" int pa_decode_append(void* out, const void* q, const void* key, const void* value,
+                                int64_t kv_token_stride, void* k_cache, void* v_cache, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                                int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                int32_t num_blocks, float scale, int32_t max_context_len, int32_t partition_size,
+                                void* workspace, size_t workspace_bytes, const int32_t* seq_order, int32_t dtype,
+                                void* stream) {
+    const Append app{static_cast<const _Float16*>(key), static_cast<const _Float16*>(value), kv_token_stride};
+    return decode_impl("pa_decode_append", out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                       context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                       max_context_len, partition_size, workspace, workspace_bytes, seq_order, dtype, stream, &app);
 }

@@ -55,14 +55,21 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 
-template <int B>
+// kAppend: the last position n - 1 of every sequence holds the token of
+// this step, whose K/V come from new_k / new_v (token s, KV head h at s *
+// new_stride + h * 128) instead of the cache; the workgroup whose partition
+// holds it folds it in as a one-token tile and writes it into the cache
+// through k_write / v_write.  The cache is read for positions < n - 1 only.
+template <int B, bool kAppend>
 __global__ void __launch_bounds__(kThreads)
 decode_gqa_mfma_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
                        const int32_t* __restrict__ order, const _Float16* __restrict__ q, const _Float16* __restrict__ k_cache,
                        const _Float16* __restrict__ v_cache, const int32_t* __restrict__ tables,
                        int32_t max_blocks, const int32_t* __restrict__ lens, int32_t num_heads,
                        int32_t num_kv_heads, int32_t num_blocks, float scale_log2, int32_t part_size,
-                       int32_t num_parts, int64_t len_cap) {
+                       int32_t num_parts, int64_t len_cap, const _Float16* __restrict__ new_k,
+                       const _Float16* __restrict__ new_v, int64_t new_stride, _Float16* __restrict__ k_write,
+                       _Float16* __restrict__ v_write) {
     const int kvh = blockIdx.x;
     const int s = order ? order[blockIdx.y] : (int)blockIdx.y;   // longest sequences first
     if ((uint32_t)s >= gridDim.y) return;                         // not a sequence: nothing to do
@@ -76,7 +83,8 @@ decode_gqa_mfma_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, fl
     const int n = bad_len ? 0 : n_raw;
     const int start = part * part_size;
     if (part > 0 && start >= n) return;
-    const int end = min(start + part_size, n);
+    const int cached = kAppend && n > 0 ? n - 1 : n;   // positions read from the cache
+    const int end = min(start + part_size, cached);
     const int np = (n + part_size - 1) / part_size;
 
     // Q^T operands of query head kvh*g + l%16 (zero past g)
@@ -98,6 +106,17 @@ decode_gqa_mfma_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, fl
     st.l = 0.f;
 #pragma unroll
     for (int c = 0; c < kDTiles; ++c) st.o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    // append mode: the new token's K/V pieces this lane would hold as token
+    // 0 of a tile, loaded now by every lane (a valid address for all) so
+    // that the load hides under the main loop
+    u32x4 new_kf[4], new_vf;
+    if constexpr (kAppend) {
+        const _Float16* kn = new_k + (int64_t)s * new_stride + (int64_t)kvh * kD;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) new_kf[u] = *reinterpret_cast<const u32x4*>(kn + 8 * (4 * u + (lane >> 4)));
+        new_vf = *reinterpret_cast<const u32x4*>(new_v + (int64_t)s * new_stride + (int64_t)kvh * kD + 8 * (lane & 15));
+    }
 
     const int ntok = end > start ? end - start : 0;
     const int nsteps = (ntok + kTile - 1) / kTile;
@@ -166,6 +185,35 @@ decode_gqa_mfma_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, fl
         }
     }
 
+    if constexpr (kAppend) {
+        const int pos = n - 1;                  // the new token, as token 0 of a tile
+        if (n > 0 && pos >= start && pos < start + part_size && wave == kWaves - 1) {
+            const int32_t phys = trow[pos / B];
+            const bool ok = (uint32_t)phys < (uint32_t)num_blocks;   // as a cached row behind a skipped id
+            const int nn = lane & 15;
+            const int j = lane >> 4;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            Tile t;
+            // K row of token l%16 (d = 8*(4u + l/16) ..): token 0 only
+#pragma unroll
+            for (int u = 0; u < 4; ++u) t.k[u] = nn == 0 ? new_kf[u] : z;
+            // V rows of tokens 4*(l/16) + i (d = 8*(l%16) ..): token 0 is i = 0 of lane group 0
+            t.v[0] = j == 0 ? new_vf : z;
+#pragma unroll
+            for (int i = 1; i < 4; ++i) t.v[i] = z;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t.valid[i] = ok && j == 0 && i == 0;
+            consume_tile(st, t, qb, scale_log2, lane, t.valid);
+            if (ok) {
+                const int64_t row = (int64_t)kvh * slab + (int64_t)phys * blk_stride + (int64_t)(pos % B) * kD;
+                if (nn == 0)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) *reinterpret_cast<u32x4*>(k_write + row + 8 * (4 * u + j)) = t.k[u];
+                if (j == 0) *reinterpret_cast<u32x4*>(v_write + row + 8 * nn) = t.v[0];
+            }
+        }
+    }
+
     // Merge the 4 waves.  s_o[w][q][d] holds wave w's unnormalised output.
     __shared__ float s_m[kWaves][16];
     __shared__ float s_l[kWaves][16];
@@ -216,18 +264,19 @@ decode_gqa_mfma_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, fl
 
 using GqaFn = void (*)(_Float16*, float*, float*, const int32_t*, const _Float16*, const _Float16*, const _Float16*,
                        const int32_t*, int32_t, const int32_t*, int32_t, int32_t, int32_t, float, int32_t,
-                       int32_t, int64_t);
+                       int32_t, int64_t, const _Float16*, const _Float16*, int64_t, _Float16*, _Float16*);
 
+template <bool kAppend>
 GqaFn pick(int32_t b) {
     switch (b) {
-        case 1: return decode_gqa_mfma_kernel<1>;
-        case 2: return decode_gqa_mfma_kernel<2>;
-        case 4: return decode_gqa_mfma_kernel<4>;
-        case 8: return decode_gqa_mfma_kernel<8>;
-        case 16: return decode_gqa_mfma_kernel<16>;
-        case 32: return decode_gqa_mfma_kernel<32>;
-        case 64: return decode_gqa_mfma_kernel<64>;
-        case 128: return decode_gqa_mfma_kernel<128>;
+        case 1: return decode_gqa_mfma_kernel<1, kAppend>;
+        case 2: return decode_gqa_mfma_kernel<2, kAppend>;
+        case 4: return decode_gqa_mfma_kernel<4, kAppend>;
+        case 8: return decode_gqa_mfma_kernel<8, kAppend>;
+        case 16: return decode_gqa_mfma_kernel<16, kAppend>;
+        case 32: return decode_gqa_mfma_kernel<32, kAppend>;
+        case 64: return decode_gqa_mfma_kernel<64, kAppend>;
+        case 128: return decode_gqa_mfma_kernel<128, kAppend>;
         default: return nullptr;
     }
 }
@@ -237,15 +286,21 @@ GqaFn pick(int32_t b) {
 namespace pa {
 
 bool gqa_mfma_supported(int32_t head_dim, int32_t block_size, int32_t group) {
-    return head_dim == kD && group >= 2 && group <= 16 && pick(block_size) != nullptr;
+    return head_dim == kD && group >= 2 && group <= 16 && pick<false>(block_size) != nullptr;
 }
 
 hipError_t launch_gqa_mfma(const DecodeLaunch& a) {
-    GqaFn fn = pick(a.block_size);
+    const bool app = a.new_k != nullptr;
+    GqaFn fn = app ? pick<true>(a.block_size) : pick<false>(a.block_size);
+    // in append mode the cache pointers double as write pointers: the kernel
+    // writes only the row of each sequence's last position, which no
+    // workgroup reads from the cache
     hipLaunchKernelGGL(fn, dim3((unsigned)a.num_kv_heads, (unsigned)a.num_seqs, (unsigned)a.num_parts),
                        dim3(kThreads), 0, a.stream, a.out, a.ws_ml, a.ws_acc, a.order, a.q, a.k_cache, a.v_cache,
                        a.tables, a.max_blocks, a.lens, a.num_heads, a.num_kv_heads, a.num_blocks, a.scale_log2,
-                       a.part_size, a.num_parts, a.len_cap);
+                       a.part_size, a.num_parts, a.len_cap, a.new_k, a.new_v, a.new_stride,
+                       app ? const_cast<_Float16*>(a.k_cache) : nullptr,
+                       app ? const_cast<_Float16*>(a.v_cache) : nullptr);
     return hipGetLastError();
 }
 

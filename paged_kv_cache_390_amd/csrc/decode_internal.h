@@ -33,6 +33,12 @@ struct DecodeLaunch {
     int32_t num_parts;
     int64_t len_cap;
     hipStream_t stream;
+    // append mode (pa_decode_append): the new token of sequence s, KV head
+    // h at s * new_stride + h * head_dim; null otherwise.  The kernel then
+    // writes it into k_cache / v_cache at the sequence's last position.
+    const _Float16* new_k;
+    const _Float16* new_v;
+    int64_t new_stride;
 };
 
 // Grouped-query decode on the matrix cores: head_dim 128, 2 <= group <= 16.

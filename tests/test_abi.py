@@ -68,8 +68,32 @@ def test_decode_rejects_bad_arguments_before_launch(kw, code):
     assert pa.last_error()
 
 
+def _append_args(key=16, value=16, stride=256, **kw):
+    d = _decode_args(**kw)
+    # pa_decode_append: out, q, key, value, kv_token_stride, k_cache, v_cache, then pa_decode's tail
+    return (d[0], d[1], key, value, stride) + d[2:]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=1), pa.PA_ERR_UNSUPPORTED),
+    (dict(D=96), pa.PA_ERR_UNSUPPORTED),
+    (dict(H=3, Hkv=2), pa.PA_ERR_INVALID),
+    (dict(out=None), pa.PA_ERR_INVALID),
+    (dict(key=None), pa.PA_ERR_INVALID),
+    (dict(value=None), pa.PA_ERR_INVALID),
+    (dict(key=24), pa.PA_ERR_INVALID),              # misaligned
+    (dict(stride=260), pa.PA_ERR_INVALID),          # not a multiple of 8 elements
+    (dict(stride=128), pa.PA_ERR_INVALID),          # < num_kv_heads * head_dim
+    (dict(maxlen=4096), pa.PA_ERR_INVALID),         # needs a workspace
+])
+def test_decode_append_rejects_bad_arguments_before_launch(kw, code):
+    assert pa.lib().pa_decode_append(*_append_args(**kw)) == code
+    assert "pa_decode_append" in pa.last_error()
+
+
 def test_decode_with_no_sequences_is_a_no_op():
     assert pa.lib().pa_decode(*_decode_args(S=0, out=None)) == pa.PA_OK
+    assert pa.lib().pa_decode_append(*_append_args(S=0, out=None, key=None)) == pa.PA_OK
 
 
 def test_decode_order_checks_arguments():

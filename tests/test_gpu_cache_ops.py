@@ -15,13 +15,14 @@ def _random_pool(rng, NB, Hkv, B, D):
     return rng.integers(0, 1 << 16, size=(NB, Hkv, B, D), dtype=np.uint16).view(np.float16)
 
 
-@pytest.mark.parametrize("D,B,T", [(128, 16, 64), (128, 16, 3000), (16, 4, 19), (256, 1, 40),
-                                   (64, 64, 500), (32, 128, 257)])
+@pytest.mark.parametrize("D,B,T,Hkv", [(128, 16, 64, 4), (128, 16, 3000, 4), (16, 4, 19, 4), (256, 1, 40, 4),
+                                       (64, 64, 500, 4), (32, 128, 257, 4),
+                                       # several lane groups per token; a block size that is no power of two
+                                       (128, 16, 64, 32), (256, 16, 33, 40), (64, 12, 100, 3), (16, 48, 70, 5)])
 @pytest.mark.parametrize("layout", ["contiguous", "strided", "misaligned"])
-def test_scatter_bit_exact(D, B, T, layout):
+def test_scatter_bit_exact(D, B, T, Hkv, layout):
     dev = device()
-    rng = np.random.default_rng(D + B + T)
-    Hkv = 4
+    rng = np.random.default_rng(D + B + T + Hkv)
     NB = (T + B - 1) // B + 5
     kc_h, vc_h = _random_pool(rng, NB, Hkv, B, D), _random_pool(rng, NB, Hkv, B, D)
     slots = rng.permutation(NB * B)[:T].astype(np.int64)
@@ -43,7 +44,7 @@ def test_scatter_bit_exact(D, B, T, layout):
     key_h = np.ascontiguousarray(key_d.cpu().numpy())
     val_h = np.ascontiguousarray(val_d.cpu().numpy())
     kc, vc = torch.from_numpy(kc_h).to(dev), torch.from_numpy(vc_h).to(dev)
-    say(f"scatter D={D} B={B} T={T} {layout}")
+    say(f"scatter D={D} B={B} T={T} Hkv={Hkv} {layout}")
     pa.pa_reshape_and_cache(key_d, val_d, torch.from_numpy(slots).to(dev), kc, vc)
     torch.cuda.synchronize()
     valid = (slots >= 0) & (slots < NB * B)

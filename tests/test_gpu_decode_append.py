@@ -1,0 +1,175 @@
+"""GPU parity of pa_decode_append (through the C ABI): one call that writes
+each sequence's new token into the cache and attends over the context with
+it, against the oracle's scatter followed by the oracle's attention.
+
+The cache is built on the host with every position but each sequence's last
+one written (oracle scatter, NaN in every other slot), so a kernel that read
+the new token's slot from the cache instead of the key/value inputs would
+come out NaN.  After the call the caches must equal, bit for bit, the
+oracle's scatter of every token; the outputs must match the oracle's
+attention over the full contexts, and the result of pa_reshape_and_cache
+followed by pa_decode, within the attention tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_390_amd as pa
+import workloads
+from gpu_common import assert_attention_close, bits, device, poisoned_cache, say
+from oracle.block_manager import BlockManagerModel
+
+pytestmark = pytest.mark.gpu
+
+
+def _caches(case, bad_last=()):
+    """(cache without the last tokens, cache with every token, tables, lens,
+    new key, new value); sequences in bad_last get an id outside the pool
+    as their last table entry (their new token is then neither written nor
+    attended to)."""
+    m = BlockManagerModel(case.num_blocks, case.block_size)
+    for s, (n, t) in enumerate(zip(case.lens, case.tables)):
+        m.set_table(s, t, n)
+    width = max(1, max(len(t) for t in case.tables))
+    rows, lens = m.tables(range(len(case.lens)), width)
+    tables = np.array(rows, dtype=np.int32)
+    lens = np.array(lens, dtype=np.int32)
+    S, Hkv, D = len(case.lens), case.num_kv_heads, case.head_dim
+    hist_slots, last_slots = [], []
+    new_k = np.zeros((S, Hkv, D), np.float16)
+    new_v = np.zeros((S, Hkv, D), np.float16)
+    hist_k, hist_v = [], []
+    for s, n in enumerate(case.lens):
+        if n == 0:
+            continue
+        base = int(case.seq_start[s])
+        for p in range(n - 1):
+            hist_slots.append(m.slot(s, p))
+        hist_k.append(case.k_tokens[base:base + n - 1])
+        hist_v.append(case.v_tokens[base:base + n - 1])
+        new_k[s] = case.k_tokens[base + n - 1]
+        new_v[s] = case.v_tokens[base + n - 1]
+        if s in bad_last:
+            tables[s, (n - 1) // case.block_size] = case.num_blocks + 5
+        else:
+            last_slots.append((s, m.slot(s, n - 1)))
+    kc0 = poisoned_cache(case.num_blocks, Hkv, case.block_size, D)
+    vc0 = kc0.copy()
+    if hist_slots:
+        oracle.reshape_and_cache(np.concatenate(hist_k), np.concatenate(hist_v),
+                                 np.array(hist_slots, np.int64), kc0, vc0)
+    kc1, vc1 = kc0.copy(), vc0.copy()
+    if last_slots:
+        idx = [s for s, _ in last_slots]
+        oracle.reshape_and_cache(np.ascontiguousarray(new_k[idx]), np.ascontiguousarray(new_v[idx]),
+                                 np.array([sl for _, sl in last_slots], np.int64), kc1, vc1)
+    return kc0, vc0, kc1, vc1, tables, lens, new_k, new_v
+
+
+def _run_append(dev, case, kc0, vc0, tables, lens, new_k, new_v, P=0, order=False, kv_stride_pad=0):
+    S, H, D = case.q.shape
+    q = torch.from_numpy(case.q).to(dev)
+    kc, vc = torch.from_numpy(kc0).to(dev), torch.from_numpy(vc0).to(dev)
+    t, l = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
+    Hkv = case.num_kv_heads
+    if kv_stride_pad:
+        # key and value as views into wider rows (a fused QKV-like buffer)
+        wide = torch.zeros((S, 2, Hkv * D + kv_stride_pad), dtype=torch.float16, device=dev)
+        wide[:, 0, :Hkv * D] = torch.from_numpy(new_k).to(dev).reshape(S, Hkv * D)
+        wide[:, 1, :Hkv * D] = torch.from_numpy(new_v).to(dev).reshape(S, Hkv * D)
+        key = wide[:, 0].narrow(1, 0, Hkv * D).unflatten(1, (Hkv, D))
+        value = wide[:, 1].narrow(1, 0, Hkv * D).unflatten(1, (Hkv, D))
+    else:
+        key, value = torch.from_numpy(new_k).to(dev), torch.from_numpy(new_v).to(dev)
+    seq_order = pa.pa_decode_order(l, int(tables.shape[1] * case.block_size)) if order else None
+    out = torch.full((S, H, D), float("nan"), dtype=torch.float16, device=dev)
+    pa.pa_decode_append(out, q, key, value, kc, vc, t, l, case.scale, partition_size=P, seq_order=seq_order)
+    torch.cuda.synchronize()
+    return out, kc, vc
+
+
+LENS = [0, 1, 2, 15, 16, 17, 33, 128, 129, 256, 257, 383, 512, 513, 777, 1024, 1031]
+
+
+@pytest.mark.parametrize("D,B,H,Hkv", [
+    (128, 16, 4, 4),      # one query per KV head: vector kernel
+    (128, 1, 2, 2),       # rows of one load in several blocks
+    (64, 4, 4, 2),        # vector kernel, two query heads per KV head
+    (16, 8, 2, 1),
+    (256, 32, 2, 2),
+    (128, 16, 16, 2),     # grouped-query kernel (8 query heads per KV head)
+    (128, 8, 8, 4),       # grouped-query kernel, tiles across blocks
+    (128, 64, 32, 2),     # grouped-query kernel, 16 query heads per KV head
+    (128, 16, 40, 2),     # 20 query heads per KV head: vector kernel, one writer per KV head
+])
+@pytest.mark.parametrize("P", [0, 128, 256])
+def test_decode_append_matches_oracle(D, B, H, Hkv, P):
+    dev = device()
+    case = workloads.random_case(D * 100 + B + H + P, LENS, H, Hkv, D, B)
+    kc0, vc0, kc1, vc1, tables, lens, new_k, new_v = _caches(case)
+    say(f"decode_append D={D} B={B} H={H}/{Hkv} P={P} NB={case.num_blocks}")
+    out, kc, vc = _run_append(dev, case, kc0, vc0, tables, lens, new_k, new_v, P=P)
+    assert np.array_equal(bits(kc), kc1.view(np.uint16)), "K cache differs from the oracle's scatter"
+    assert np.array_equal(bits(vc), vc1.view(np.uint16)), "V cache differs from the oracle's scatter"
+    ref = oracle.decode(case.q, kc1, vc1, tables, lens, case.scale)
+    assert_attention_close(out, ref, f"append D={D} B={B} H={H}/{Hkv} P={P}")
+    assert np.all(bits(out)[0] == 0)                       # n == 0: zero row
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (16, 2)])
+def test_decode_append_equals_scatter_then_decode(H, Hkv):
+    """Same inputs through pa_reshape_and_cache + pa_decode (two launches)
+    and through pa_decode_append: the same cache bits, and outputs within
+    the tolerance of each other (the new token is summed last in one, in
+    position order in the other)."""
+    dev = device()
+    case = workloads.random_case(77 + H, LENS, H, Hkv, 128, 16)
+    kc0, vc0, kc1, vc1, tables, lens, new_k, new_v = _caches(case)
+    out_a, kc_a, vc_a = _run_append(dev, case, kc0, vc0, tables, lens, new_k, new_v, order=True)
+    S = len(LENS)
+    kc, vc = torch.from_numpy(kc0).to(dev), torch.from_numpy(vc0).to(dev)
+    slots = np.array([tables[s, (n - 1) // 16] * 16 + (n - 1) % 16 if n > 0 else -1 for s, n in enumerate(lens)],
+                     np.int64)
+    pa.pa_reshape_and_cache(torch.from_numpy(new_k).to(dev), torch.from_numpy(new_v).to(dev),
+                            torch.from_numpy(slots).to(dev), kc, vc)
+    out_b = torch.full((S, H, 128), float("nan"), dtype=torch.float16, device=dev)
+    pa.pa_decode(out_b, torch.from_numpy(case.q).to(dev), kc, vc, torch.from_numpy(tables).to(dev),
+                 torch.from_numpy(lens).to(dev), case.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(kc_a), bits(kc)) and np.array_equal(bits(vc_a), bits(vc))
+    assert_attention_close(out_a, out_b.float().cpu().numpy().astype(np.float64), "append vs two calls")
+
+
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (16, 2)])
+def test_decode_append_skipped_last_block(H, Hkv):
+    """A last table entry outside the pool: nothing is written, and every
+    token of that block -- the new one included -- takes no part in the
+    softmax, as pa_decode treats a skipped id."""
+    dev = device()
+    lens = [5, 16, 17, 300, 1]
+    case = workloads.random_case(91 + H, lens, H, Hkv, 128, 16)
+    bad = (2, 3, 4)
+    kc0, vc0, kc1, vc1, tables, lens_a, new_k, new_v = _caches(case, bad_last=bad)
+    out, kc, vc = _run_append(dev, case, kc0, vc0, tables, lens_a, new_k, new_v)
+    assert np.array_equal(bits(kc), kc1.view(np.uint16)) and np.array_equal(bits(vc), vc1.view(np.uint16))
+    keep, starts, kept = [], [], []
+    for s, n in enumerate(lens):
+        first_bad = (n - 1) // 16 * 16 if s in bad else n
+        starts.append(len(keep))
+        keep += [int(case.seq_start[s]) + p for p in range(first_bad)]
+        kept.append(first_bad)
+    ref = oracle.attention_contig(case.q, np.ascontiguousarray(case.k_tokens[keep]),
+                                  np.ascontiguousarray(case.v_tokens[keep]), np.array(starts, np.int64),
+                                  np.array(kept, np.int32), case.scale)
+    assert_attention_close(out, ref, "skipped last block")
+    assert np.all(bits(out)[4] == 0)                       # n = 1 with its only token skipped: zero row
+
+
+def test_decode_append_strided_inputs():
+    """key/value as views into wider rows (token stride above Hkv * D)."""
+    dev = device()
+    case = workloads.random_case(123, LENS, 8, 8, 128, 16)
+    kc0, vc0, kc1, vc1, tables, lens, new_k, new_v = _caches(case)
+    out, kc, vc = _run_append(dev, case, kc0, vc0, tables, lens, new_k, new_v, kv_stride_pad=256)
+    assert np.array_equal(bits(kc), kc1.view(np.uint16)) and np.array_equal(bits(vc), vc1.view(np.uint16))
+    assert_attention_close(out, oracle.decode(case.q, kc1, vc1, tables, lens, case.scale), "strided key/value")
