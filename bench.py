@@ -738,7 +738,8 @@ def sampling_bench(args, dev):
     blocks, the last holding 8 tokens) forked into 32 samples; every step
     appends one token per sample through the block manager (step 0: 31
     copy-on-write pairs -> pa_copy_blocks), writes the 32 new K/V rows and
-    decodes all 32 samples -- the lpnh.cn/news/2758356 section 4 scenario,
+    decodes all 32 samples (one pa_decode_append; --fused 0: scatter, then
+    decode) -- the lpnh.cn/news/2758356 section 4 scenario,
     Llama-2-7B heads, B = 16, one layer.  Reported: time per step, and the
     logical KV bytes the decodes attend over per second (shared prompt
     blocks counted once per sample; they are re-read from the caches)."""
@@ -774,10 +775,14 @@ def sampling_bench(args, dev):
         ncow += len(pairs)
         if len(pairs):
             pa.pa_copy_blocks([kc], [vc], torch.from_numpy(pairs).to(dev))
-        pa.pa_reshape_and_cache(key, val, torch.from_numpy(slots).to(dev), kc, vc)
         tables, lens = bm.get_tables(seqs, width)
-        pa.pa_decode(out, q, kc, vc, torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), w.scale, B,
-                     max_context_len=width * B, workspace=ws)
+        if args.fused:                       # the new K/V written inside the decode call
+            pa.pa_decode_append(out, q, key, val, kc, vc, torch.from_numpy(tables).to(dev),
+                                torch.from_numpy(lens).to(dev), w.scale, B, max_context_len=width * B, workspace=ws)
+        else:
+            pa.pa_reshape_and_cache(key, val, torch.from_numpy(slots).to(dev), kc, vc)
+            pa.pa_decode(out, q, kc, vc, torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), w.scale,
+                         B, max_context_len=width * B, workspace=ws)
         logical += int(lens.astype(np.int64).sum()) * kv_tok
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -791,7 +796,8 @@ def sampling_bench(args, dev):
                       "cow_pairs": ncow, "blocks_at_end": used,
                       "blocks_unshared": N * workloads.ceil_div(w.prompt_len + w.steps, B),
                       "config": {"workload": "parallel-sampling", "samples": N, "prompt": w.prompt_len,
-                                 "block_size": B, "num_heads": w.num_heads, "head_dim": w.head_dim}}), flush=True)
+                                 "block_size": B, "num_heads": w.num_heads, "head_dim": w.head_dim,
+                                 "fused": bool(args.fused)}}), flush=True)
 
 
 if __name__ == "__main__":

@@ -171,7 +171,9 @@ int pa_decode(void *out, const void *q, const void *k_cache,
  * pa_decode.  The cache is read for positions < n - 1 only; the new token's
  * K/V come from key / value, so the result does not depend on the slot's
  * contents before the call.  Sequences with n == 0, or with n above
- * max_context_len or the table width, write nothing.  The written block
+ * max_context_len or the table width, write nothing, and so does a
+ * sequence that seq_order leaves out (its output rows stay untouched, as
+ * in pa_decode).  The written block
  * must not be shared with another sequence of the call (the block
  * manager's copy-on-write guarantees that for the last block of a
  * sequence).

@@ -68,7 +68,11 @@ def test_block_size_sweep():
         assert np.max(np.abs(outs[B] - outs[8])) < 2 * (2e-3 + 1e-2 * np.max(np.abs(outs[8])))
 
 
-def test_parallel_sampling_copy_on_write():
+@pytest.mark.parametrize("fused", [False, True])
+def test_parallel_sampling_copy_on_write(fused):
+    """fused: each step's write goes through pa_decode_append (after the
+    step's copy-on-write copies) instead of pa_reshape_and_cache +
+    pa_decode."""
     dev = device()
     w = workloads.parallel_sampling(seed=0)
     NB, B, N = w.num_blocks, w.block_size, w.num_samples
@@ -104,17 +108,22 @@ def test_parallel_sampling_copy_on_write():
         if len(pairs):
             pa.pa_copy_blocks([kc], [vc], torch.from_numpy(pairs).to(dev))
             oracle.copy_blocks([kc_h], [vc_h], np.ascontiguousarray(pairs))
-        pa.pa_reshape_and_cache(key, val, torch.from_numpy(slots).to(dev), kc, vc)
+        if not fused:
+            pa.pa_reshape_and_cache(key, val, torch.from_numpy(slots).to(dev), kc, vc)
         oracle.reshape_and_cache(key.cpu().numpy(), val.cpu().numpy(), slots, kc_h, vc_h)
         tables, lens = bm.get_tables(seqs, width)
         rows, lens_m = m.tables(seqs, width)
         assert np.array_equal(tables, np.array(rows, np.int32)) and lens.tolist() == lens_m
         assert bm.free_list() == m.free
         out = torch.empty_like(q)
-        pa.pa_decode(out, q, kc, vc, torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), w.scale, B)
+        if fused:
+            pa.pa_decode_append(out, q, key, val, kc, vc, torch.from_numpy(tables).to(dev),
+                                torch.from_numpy(lens).to(dev), w.scale, B)
+        else:
+            pa.pa_decode(out, q, kc, vc, torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), w.scale, B)
         if step in checks:
             torch.cuda.synchronize()
-            say(f"  cow step {step}: len {lens[0]}, free {bm.num_free()}")
+            say(f"  cow step {step} fused={fused}: len {lens[0]}, free {bm.num_free()}")
             assert np.array_equal(bits(kc), kc_h.view(np.uint16)) and np.array_equal(bits(vc), vc_h.view(np.uint16))
             ref = oracle.decode(q.cpu().numpy(), kc_h, vc_h, tables, lens, w.scale)
             assert_attention_close(out, ref, f"cow step {step}")
