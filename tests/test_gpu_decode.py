@@ -268,13 +268,16 @@ def test_table_entries_outside_the_pool_are_skipped():
     assert_attention_close(out, ref, "skipped ids")
 
 
-@pytest.mark.parametrize("P,given_order", [(0, True), (0, False), (256, False)])
-def test_llama7b_decode_full_size(P, given_order):
+@pytest.mark.parametrize("P,given_order,fused", [(0, True, True), (0, True, False), (0, False, False),
+                                                 (256, False, False)])
+def test_llama7b_decode_full_size(P, given_order, fused):
     """64 sequences, 32 heads x 128, B=16, n ~ U[1, 2048], pool of 8192 blocks
     filled N(0, 1), tables from one permutation; the new token of every
-    sequence is written by the product's scatter, then decoded -- with the
-    benchmark's launch configuration (default partition, the dispatch order
-    from pa_decode_order passed in), and with pa_decode ordering itself."""
+    sequence is written by the product's scatter, then decoded, or by the
+    decode call itself (pa_decode_append) -- with the benchmark's launch
+    configuration (default partition, the dispatch order from
+    pa_decode_order passed in, one fused call), and with pa_decode ordering
+    itself."""
     dev = device()
     w = workloads.llama7b_decode(seed=0)
     S, B, NB = len(w.lens), w.block_size, w.num_blocks
@@ -298,19 +301,23 @@ def test_llama7b_decode_full_size(P, given_order):
     rows, lens_m = m.tables(range(S), width)
     assert np.array_equal(tables, np.array(rows, np.int32)) and lens.tolist() == lens_m
 
-    pa.pa_reshape_and_cache(key, val, torch.from_numpy(slots).to(dev), kc, vc)
     out = torch.empty((S, w.num_heads, w.head_dim), dtype=torch.float16, device=dev)
     d_lens = torch.from_numpy(lens).to(dev)
     order = pa.pa_decode_order(d_lens, width * B) if given_order else None
-    pa.pa_decode(out, q, kc, vc, torch.from_numpy(tables).to(dev), d_lens, w.scale, B, partition_size=P,
-                 seq_order=order)
+    if fused:
+        pa.pa_decode_append(out, q, key, val, kc, vc, torch.from_numpy(tables).to(dev), d_lens, w.scale, B,
+                            partition_size=P, seq_order=order)
+    else:
+        pa.pa_reshape_and_cache(key, val, torch.from_numpy(slots).to(dev), kc, vc)
+        pa.pa_decode(out, q, kc, vc, torch.from_numpy(tables).to(dev), d_lens, w.scale, B, partition_size=P,
+                     seq_order=order)
     torch.cuda.synchronize()
 
     oracle.reshape_and_cache(key_h, val_h, slots, kc_h, vc_h)
     assert torch.equal(kc.view(torch.int16), torch.from_numpy(kc_h.view(np.int16)).to(dev))
     assert torch.equal(vc.view(torch.int16), torch.from_numpy(vc_h.view(np.int16)).to(dev))
     ref = oracle.decode(q_h, kc_h, vc_h, tables, lens, w.scale)
-    assert_attention_close(out, ref, f"llama7b P={P} given order={given_order}")
+    assert_attention_close(out, ref, f"llama7b P={P} given order={given_order} fused={fused}")
 
 
 def test_long_context_split_partitions():

@@ -89,11 +89,12 @@ def test_gqa_rows_beyond_the_bound_and_skipped_ids():
     assert_attention_close(out[:1], ref0, "gqa skipped ids")
 
 
-@pytest.mark.parametrize("P", [0, 1024])
-def test_gqa_decode_full_size(P):
+@pytest.mark.parametrize("P,fused", [(0, True), (0, False), (1024, False)])
+def test_gqa_decode_full_size(P, fused):
     """256 sequences, 64 query heads over 8 KV heads x 128, B=16, n ~ U[1,
     2048]: product block manager tables, scatter of each sequence's new
-    token, decode; every output against the oracle."""
+    token, decode -- or both in one pa_decode_append call, as the benchmark
+    runs it; every output against the oracle."""
     dev = device()
     w = workloads.gqa_decode(seed=0)
     S, B, NB = len(w.lens), w.block_size, w.num_blocks
@@ -108,14 +109,19 @@ def test_gqa_decode_full_size(P):
         bm.set_table(s, w.perm_tables[s, :workloads.ceil_div(n, B)], n)
         slots[s] = bm.get_slots(s, n - 1, 1)[0]
     tables, lens = bm.get_tables(range(S), w.perm_tables.shape[1])
-    pa.pa_reshape_and_cache(key, val, torch.from_numpy(slots).to(dev), kc, vc)
     out = torch.empty((S, w.num_heads, w.head_dim), dtype=torch.float16, device=dev)
     d_lens = torch.from_numpy(lens).to(dev)
     order = pa.pa_decode_order(d_lens, w.perm_tables.shape[1] * B) if P == 0 else None   # as the benchmark runs it
-    pa.pa_decode(out, q, kc, vc, torch.from_numpy(tables).to(dev), d_lens, w.scale, B, partition_size=P,
-                 seq_order=order)
+    if fused:
+        pa.pa_decode_append(out, q, key, val, kc, vc, torch.from_numpy(tables).to(dev), d_lens, w.scale, B,
+                            partition_size=P, seq_order=order)
+    else:
+        pa.pa_reshape_and_cache(key, val, torch.from_numpy(slots).to(dev), kc, vc)
+        pa.pa_decode(out, q, kc, vc, torch.from_numpy(tables).to(dev), d_lens, w.scale, B, partition_size=P,
+                     seq_order=order)
     torch.cuda.synchronize()
     oracle.reshape_and_cache(key_h, val_h, slots, kc_h, vc_h)
     assert torch.equal(kc.view(torch.int16), torch.from_numpy(kc_h.view(np.int16)).to(dev))
+    assert torch.equal(vc.view(torch.int16), torch.from_numpy(vc_h.view(np.int16)).to(dev))
     ref = oracle.decode(q_h, kc_h, vc_h, tables, lens, w.scale)
-    assert_attention_close(out, ref, f"gqa full P={P}")
+    assert_attention_close(out, ref, f"gqa full P={P} fused={fused}")
