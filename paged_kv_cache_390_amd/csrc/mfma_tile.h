@@ -51,14 +51,18 @@ __device__ __forceinline__ void load_tile_block(Tile& t, int t0, int end, int32_
     const int j = lane >> 4;
     const bool ok = (uint32_t)phys < (uint32_t)num_blocks;
     const int64_t base = (int64_t)(ok ? phys : 0) * blk_stride + (int64_t)(t0 % B) * kD;
-    // rows past the context are read from the same block and masked later
+    // rows past the context read the context's last row again (the same
+    // cache lines: no extra HBM bytes) and are masked later
+    const int lim = end - 1 - t0;
+    const int rk = n < lim ? n : lim;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-        t.k[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + base + n * kD + 8 * (4 * u + j)));
+        t.k[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + base + rk * kD + 8 * (4 * u + j)));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        const int rv = 4 * j + i < lim ? 4 * j + i : lim;
         t.valid[i] = ok && t0 + 4 * j + i < end;
-        t.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + base + (4 * j + i) * kD + 8 * n));
+        t.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + base + rv * kD + 8 * n));
     }
 }
 
