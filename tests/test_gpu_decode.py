@@ -322,7 +322,7 @@ def test_llama7b_decode_full_size(P, given_order, fused):
 
 def test_long_context_split_partitions():
     """16 sequences x 4096 tokens, 32 x 128 heads, B=16, 512-token partitions
-    (8 per sequence) merged in-kernel by the last workgroup of each row; two
+    (8 per sequence) merged by the reduce kernel; two
     of the 32 layers."""
     dev = device()
     w = workloads.long_context(seed=0)
