@@ -31,8 +31,10 @@
  *     kernels skip any that fall outside the pool, so a bad index is never
  *     dereferenced (see each call for what the output then holds).
  *   - dtype: PA_DTYPE_F16 is the only element type.
- *   - head_dim in {16, 32, 64, 128, 256}; block_size in {1, 2, 4, 8, 16, 32,
- *     64, 128} (PA_ERR_UNSUPPORTED otherwise).
+ *   - head_dim in {16, 32, 64, 128, 256} (pa_prefill: 128); the attention
+ *     calls take block_size in {1, 2, 4, 8, 16, 32, 64, 128}
+ *     (PA_ERR_UNSUPPORTED otherwise); pa_reshape_and_cache and the block
+ *     copies take any block size.
  *
  * Every function returns PA_OK (0) or a negative PA_ERR_* code, except where
  * stated.  pa_last_error() gives a message for the calling thread's last
