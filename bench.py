@@ -54,12 +54,14 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="llama7b", choices=["llama7b", "gqa", "long", "copy", "swap", "prefix", "prefill", "chunked", "sweep", "sampling"],
+    p.add_argument("--workload", default="llama7b", choices=["llama7b", "gqa", "long", "copy", "swap", "prefix", "prefill", "prefill-long", "chunked",
+                            "sweep", "sampling"],
                    help="llama7b: the Llama-2-7B decode batch (default); gqa: 64 query heads over 8 KV "
                         "heads (matrix-core kernel); long: 16 x 4096 tokens; copy: block-copy calibration; "
                         "swap: block swaps between HBM and pinned host memory; prefix: 100 requests "
                         "sharing a 1000-token system prompt; prefill: causal attention of 32 prompts "
-                        "(mean 500 tokens) over the paged cache; sweep: decode of 256 sequences at "
+                        "(mean 500 tokens) over the paged cache; prefill-long: full causal prompts of 1k-8k "
+                        "tokens; sweep: decode of 256 sequences at "
                         "block_size 8/16/32/64; sampling: 32 samples of one prompt with copy-on-write")
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--batch", type=int, default=0, help="sequences (0: 64 for llama7b, 256 for gqa)")
@@ -161,6 +163,8 @@ def main():
         return prefill_bench(args, dev)
     if args.workload == "chunked":
         return chunked_bench(args, dev)
+    if args.workload == "prefill-long":
+        return prefill_long_bench(args, dev)
     if args.workload == "sweep":
         return sweep_bench(args, dev)
     if args.workload == "sampling":
@@ -661,6 +665,72 @@ def chunked_bench(args, dev):
                       "roofline": {"bound": "hbm", "achieved": best["kv_GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                    "frac": round(best["kv_GB_s"] / HBM_PEAK_GBS, 4), "traffic": None},
                       "config": {"workload": "chunked", "block_size": B, "head_dim": D, "layers_resident": L}}),
+          flush=True)
+
+
+def prefill_long_bench(args, dev):
+    """Prefill of long full prompts: every token new, causal, at Llama-2-7B
+    heads (32 x 128; one batch at 32 query / 8 KV heads), B = 16, --layers
+    layers resident (default here 4): 32 x 1024, 16 x 2048, 8 x 4096, 4 x
+    8192 tokens -- the steady state of the prefill loop, next to the
+    short-prompt mix of --workload prefill.  Flops as for that workload:
+    4 x 128 x heads x (positions each token attends to)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_390_amd as pa
+
+    L = args.layers if args.layers != 32 else 4
+    B, D = args.block_size, 128
+    results = []
+    for S, n, H, Hkv in ((32, 1024, 32, 32), (16, 2048, 32, 32), (8, 4096, 32, 32), (4, 8192, 32, 32),
+                         (8, 4096, 32, 8)):
+        nbps = -(-n // B)
+        NB = S * nbps + 8
+        g = torch.Generator(device=dev)
+        g.manual_seed(args.seed)
+        kcs = [torch.randn((NB, Hkv, B, D), generator=g, device=dev, dtype=torch.float16) for _ in range(L)]
+        vcs = [torch.randn((NB, Hkv, B, D), generator=g, device=dev, dtype=torch.float16) for _ in range(L)]
+        perm = np.random.default_rng(args.seed).permutation(NB)[:S * nbps].reshape(S, nbps).astype(np.int32)
+        T = S * n
+        q = torch.randn((T, H, D), generator=g, device=dev, dtype=torch.float16)
+        out = torch.empty_like(q)
+        d_t = torch.from_numpy(perm).to(dev)
+        d_l = torch.full((S,), n, dtype=torch.int32, device=dev)
+        d_q = torch.arange(0, T + 1, n, dtype=torch.int32, device=dev)
+        ws_n = pa.pa_prefill_workspace_size(T, S, H, Hkv, D, B, nbps, n)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+
+        def call(l):
+            pa.pa_prefill(out, q, kcs[l], vcs[l], d_t, d_l, d_q, 1 / np.sqrt(D), max_query_len=n, workspace=ws)
+
+        for _ in range(max(args.warmup, 3)):
+            for l in range(L):
+                call(l)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps * L)]
+        for i in range(args.steps):
+            for l in range(L):
+                a, b = ev[i * L + l]
+                a.record()
+                call(l)
+                b.record()
+        torch.cuda.synchronize()
+        us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+        flops = 4.0 * D * H * S * n * (n + 1) / 2
+        tf = flops / us / 1e6
+        log(f"[bench] prefill-long: {S} x {n} tokens, {H}/{Hkv} heads: {us:.1f} us = {tf:.1f} TFLOP/s "
+            f"({100 * tf / MFMA_F16_PEAK_TFLOPS:.1f}% of dense fp16 MFMA peak)")
+        results.append({"batch": f"{S}x{n}, {H}/{Hkv} heads", "us": round(us, 2), "TFLOP_s": round(tf, 1)})
+    best = results[3]
+    print(json.dumps({"metric": "paged prefill TFLOP/s, long full prompts", "value": best["TFLOP_s"],
+                      "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                      "higher_is_better": True, "dtype": "f16", "batches": results,
+                      "roofline": {"bound": "mfma", "achieved": best["TFLOP_s"], "peak": MFMA_F16_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": round(best["TFLOP_s"] / MFMA_F16_PEAK_TFLOPS, 4),
+                                   "traffic": None},
+                      "config": {"workload": "prefill-long", "block_size": B, "head_dim": D, "layers_resident": L}}),
           flush=True)
 
 
