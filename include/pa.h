@@ -268,9 +268,12 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
 /* The partition size pa_decode uses when given 0.  With rows =
  * num_seqs x num_heads (x num_kv_heads on the matrix-core path) and slots =
  * the resident workgroups of the kernel that serves these shapes (1024, or
- * 512 on the matrix-core path): 2048 when rows x ceil(max_context_len /
- * 2048) workgroups fill the slots at least twice and a whole number of times
- * (or leave the last round at least 3/4 full); otherwise the longest of
+ * 512 on the matrix-core path): P1 when rows x ceil(max_context_len / P1)
+ * workgroups fill the slots at least twice and a whole number of times (or
+ * leave the last round at least 3/4 full), where P1 is 2048, or
+ * max_context_len rounded up to a multiple of 128 when that lies in
+ * (2048, 2560] (one partition then covers every context and no merge kernel
+ * runs); otherwise the longest of
  * 2048, 1024, 512 and 256 tokens that gives at least four workgroups per
  * slot counting full partitions of a max_context_len sequence; 256 when none
  * does.  -1 for invalid arguments. */

@@ -572,11 +572,17 @@ int64_t resident_slots(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim
 
 // Default partition.  Rows are the workgroups one partition index gives
 // (grid_rows), slots the workgroups resident at once (resident_slots).
-//  * 2048 tokens when the 2048-token grid fills the slots a whole number of
-//    times, at least twice (or leaves the last round at least 3/4 full),
-//    counting every sequence at the bound: with the sequences dispatched
-//    longest first the drain is short, and long partitions mean fewer
-//    partial states and, when every context fits, no merge kernel.
+//  * Long partitions first: P1 = 2048 tokens, or -- when the bound is at
+//    most 2560 -- the bound rounded up to the partition quantum if that is
+//    longer, so that one partition covers every context.  P1 is taken when
+//    its grid fills the slots a whole number of times, at least twice (or
+//    leaves the last round at least 3/4 full), counting every sequence at
+//    the bound: with the sequences dispatched longest first the drain is
+//    short, and long partitions mean fewer partial states and, when every
+//    context fits, no merge kernel.  (A batch drawn up to 2048 tokens grows
+//    past it by one token per step; at 2048 its few longest sequences would
+//    get a second partition of a few tokens, and every call a merge kernel
+//    of ~4.6 us, 2.7% of the 64 x 32-head call.)
 //  * Otherwise the longest of 2048 / 1024 / 512 / 256 tokens that gives at
 //    least four workgroups per slot, counting full partitions of a longest
 //    sequence (the bound may exceed every actual length).
@@ -589,9 +595,11 @@ int32_t default_partition(int32_t num_seqs, int32_t num_heads, int32_t num_kv_he
     const int64_t rows = grid_rows(num_seqs, num_heads, num_kv_heads, head_dim, block_size);
     const int64_t slots = resident_slots(num_heads, num_kv_heads, head_dim, block_size);
     {
-        const int64_t wgs = rows * (max_context_len > 2048 ? ((int64_t)max_context_len + 2047) / 2048 : 1);
+        const int32_t whole = (max_context_len + kPartitionQuantum - 1) / kPartitionQuantum * kPartitionQuantum;
+        const int32_t p1 = max_context_len <= 2560 && whole > 2048 ? whole : 2048;
+        const int64_t wgs = rows * (max_context_len > p1 ? ((int64_t)max_context_len + p1 - 1) / p1 : 1);
         const int64_t tail = wgs % slots;
-        if (wgs >= 2 * slots && (tail == 0 || 4 * tail >= 3 * slots)) return 2048;
+        if (wgs >= 2 * slots && (tail == 0 || 4 * tail >= 3 * slots)) return p1;
     }
     const int32_t cands[] = {2048, 1024, 512, 256};
     for (int32_t p : cands) {

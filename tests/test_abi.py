@@ -120,8 +120,10 @@ def test_workspace_size():
 
 
 def test_default_partition_keeps_the_gpu_busy():
-    """2048 when rows x ceil(max_len / 2048) workgroups (rows: sequence x
-    query head, or x KV head on the grouped path) fill the resident slots
+    """P1 when rows x ceil(max_len / P1) workgroups (rows: sequence x
+    query head, or x KV head on the grouped path; P1 = 2048, or max_len
+    rounded up to a multiple of 128 when that lies in (2048, 2560]) fill the
+    resident slots
     (1024 for one query per KV head, 512 for groups of 2..16 at head_dim
     128) at least twice, a whole number of times or with the last round at
     least 3/4 full; otherwise the longest of 2048/1024/512/256 tokens with
@@ -129,7 +131,11 @@ def test_default_partition_keeps_the_gpu_busy():
     sequence; 256 when even that is not reached."""
     L = pa.lib()
     assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2048) == 2048     # 2048 workgroups = 2 rounds
-    assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2112) == 2048     # 4096 = 4 rounds
+    assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2049) == 2176     # one partition covers the bound
+    assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2112) == 2176
+    assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2560) == 2560
+    assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2561) == 2048     # 4096 = 4 rounds
+    assert L.pa_decode_default_partition(256, 64, 8, 128, 16, 2100) == 2176     # grouped: 2048 rows, 512 slots
     assert L.pa_decode_default_partition(100, 32, 32, 128, 16, 1216) == 512     # 3.125 rounds at 2048
     assert L.pa_decode_default_partition(120, 32, 32, 128, 16, 1216) == 2048    # 3.75: last round 3/4 full
     assert L.pa_decode_default_partition(112, 32, 32, 128, 16, 1216) == 512     # 3.5: last round half full

@@ -65,6 +65,23 @@ def test_decode_edge_lengths_match_oracle(D, B, P, H, Hkv):
     assert np.all(bits(out)[0] == 0)                       # n == 0 row is exactly zero
 
 
+@pytest.mark.parametrize("P", [384, 2176])
+@pytest.mark.parametrize("H,Hkv", [(4, 4), (16, 2)])
+def test_partitions_off_powers_of_two(P, H, Hkv):
+    """Partition sizes are any multiple of 128 (the default rule picks the
+    bound rounded up to 128 just past 2048): contexts on both sides of each
+    partition edge, vector and grouped-query kernels, against the oracle."""
+    dev = device()
+    lens = [0, 1, 383, 384, 385, 767, 769, 1000, 2175, 2176, 2177, 2600]
+    case = workloads.random_case(P + H, lens, H, Hkv, 128, 16)
+    kc, vc, tables, lens_arr = _oracle_cache(case)
+    say(f"decode P={P} H={H}/{Hkv} NB={case.num_blocks}")
+    out = _gpu_decode(dev, case.q, kc, vc, tables, lens_arr, case.scale, partition_size=P)
+    ref = oracle.decode(case.q, kc, vc, tables, lens_arr, case.scale)
+    assert_attention_close(out, ref, f"P={P} H={H}/{Hkv}")
+    assert np.all(bits(out)[0] == 0)
+
+
 def test_single_token_is_exact():
     dev = device()
     case = workloads.random_case(5, [1] * 8, 4, 2, 128, 16)

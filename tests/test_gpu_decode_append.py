@@ -102,7 +102,7 @@ LENS = [0, 1, 2, 15, 16, 17, 33, 128, 129, 256, 257, 383, 512, 513, 777, 1024, 1
     (128, 64, 32, 2),     # grouped-query kernel, 16 query heads per KV head
     (128, 16, 40, 2),     # 20 query heads per KV head: vector kernel, one writer per KV head
 ])
-@pytest.mark.parametrize("P", [0, 128, 256])
+@pytest.mark.parametrize("P", [0, 128, 256, 384])
 def test_decode_append_matches_oracle(D, B, H, Hkv, P):
     dev = device()
     case = workloads.random_case(D * 100 + B + H + P, LENS, H, Hkv, D, B)
