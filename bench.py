@@ -77,7 +77,8 @@ def parse():
     return p.parse_args()
 
 
-KERNEL_SOURCES = {"llama7b": ("decode.hip",), "gqa": ("decode.hip", "decode_gqa.hip", "mfma_tile.h")}
+KERNEL_SOURCES = {"llama7b": ("decode.hip",), "gqa": ("decode.hip", "decode_gqa.hip", "mfma_tile.h"),
+                  "prefill": ("prefill.hip", "mfma_tile.h")}
 
 
 def code_tokens(text: str) -> str:

@@ -21,14 +21,21 @@
 //    tile, issued last row tile first so the longest causal ranges start
 //    earliest.
 //  * K/V tiles of 32 tokens are staged through LDS once per workgroup and
-//    read by all 4 waves: each thread fetches 16 bytes of two token rows of
-//    K and of V (nontemporal loads) two tiles ahead into registers, and
-//    stores them one tile ahead into the other of two LDS buffers; one
-//    barrier per tile.  A wave's 4 rows of one fetch share a table entry
-//    (blocks of 4 or more tokens), read a tile ahead with a scalar load.
-//    Every step issues the same loads, so the waits before a store count
-//    only the older tile.  Rows are padded to 272 bytes so that the 16 rows
-//    one operand read touches fall in different banks.
+//    read by all 4 waves.  The loads go from HBM straight into LDS
+//    (global_load_lds_dwordx4: a wave instruction writes 1 KiB, 4 token rows
+//    of 256 bytes, 16 bytes per lane), two tiles ahead, into the third of
+//    three buffers -- no registers hold a tile in flight and no LDS store
+//    instructions run.  Each thread issues 4 such loads per tile (2 rows of
+//    K, 2 of V) and every step issues them (tiles past the last read
+//    clamped rows), so an explicit wait for all but the newest 4 is a wait
+//    for the next tile; one barrier per tile.  A wave's 4 rows of one load
+//    share a table entry (blocks of 4 or more tokens), read a tile ahead
+//    with a scalar load.  The DMA writes lane i's 16 bytes at byte 16i, so
+//    bank conflicts are avoided by choosing what each lane loads: position
+//    p of K row r holds the row's 16-byte chunk p ^ (r & 15), of V row r
+//    chunk p ^ 2(r & 3).  Rows past the context or with an id outside the
+//    pool are zeroed in LDS by the thread that loaded them, after its loads
+//    landed and before the barrier.
 //  * QK as S^T = K Q^T: MFMA c takes head_dim 32c + 8*(l/16) + 0..7 in lane
 //    l, one 16-byte LDS read of K per two MFMAs; Q^T operands stay in
 //    registers.  S^T lands with each lane holding 8 scores of one row
@@ -64,30 +71,36 @@ constexpr int kRowsPerWave = 16 * kNT;
 constexpr int kRowsPerGroup = kWaves * kRowsPerWave;
 constexpr double kLog2e = 1.4426950408889634073599246810019;
 
-// One K/V tile in LDS: kKvTile token rows of K and of V, kPitch bytes each
-// (256 bytes of data + 16 of padding, so the 16 rows one MFMA operand read
-// touches fall in different banks), plus a flag per token (inside the
-// context and the pool).
+// One K/V tile in LDS: kKvTile token rows of K and of V, 256 bytes each with
+// their 16-byte chunks permuted per row (see fetch_tile), plus a flag per
+// token (inside the context and the pool) in an array of its own.
 constexpr int kKvTile = 32;
-constexpr int kPitch = kD * 2 + 16;           // K rows
-constexpr int kPitchV = kD * 2 + 32;          // V rows (see pv in consume_lds_tile)
+constexpr int kPitch = kD * 2;                // K rows (16-byte chunks XOR-swizzled by row & 15)
+constexpr int kPitchV = kD * 2;               // V rows (chunks swizzled by 2 * (row & 3))
 constexpr int kTileBytes = kKvTile * kPitch;
 constexpr int kTileBytesV = kKvTile * kPitchV;
+constexpr int kBufBytes = kTileBytes + kTileBytesV;
 
 typedef _Float16 half8_t_ __attribute__((ext_vector_type(8)));
 
-// One thread's share of a K/V tile in flight: 16 bytes (columns 8*col ..
-// 8*col+7) of kStageRows token rows of K and of V.  Thread (wave w, lane l)
-// stages rows 4w + l/16 + (kThreads/16)*i, i < kStageRows: a wave's rows for
-// one i are 4 consecutive tokens starting at a multiple of 4, so with blocks
-// of 4 or more tokens they share one table entry, read with a scalar load.
+// One thread's share of a K/V tile in flight: the validity of the
+// kStageRows token rows whose 16 bytes at LDS position l%16 it loads.
+// Thread (wave w, lane l) stages rows 4w + l/16 + (kThreads/16)*i, i <
+// kStageRows: a wave's rows for one i are 4 consecutive tokens starting at a
+// multiple of 4, so with blocks of 4 or more tokens they share one table
+// entry, read with a scalar load.
 constexpr int kStageRows = kKvTile * 16 / kThreads;
 static_assert(kStageRows >= 1 && kKvTile * 16 == kStageRows * kThreads, "tile rows must split evenly");
 
 struct Staged {
-    u32x4 k[kStageRows], v[kStageRows];
     bool ok[kStageRows];
 };
+
+// s_waitcnt immediates (GFX9 encoding: vmcnt bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8): wait until at most N vector memory operations are
+// outstanding; wait for every LDS / scalar memory operation.
+#define PA_WAIT_VM(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8))
+#define PA_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8))
 
 // First token of the wave's stage row i of tile k.
 __device__ __forceinline__ int stage_token0(int k, int wave, int i) {
@@ -107,14 +120,21 @@ __device__ __forceinline__ void table_entries(int32_t (&e)[kStageRows], int k, i
     }
 }
 
-// Fetch tile k (tokens 32k .. 32k+31) from HBM into registers; `e` holds
-// its table entries when B >= 4 (read a step earlier), else every thread
-// looks up its own row.
-template <int B>
-__device__ __forceinline__ void fetch_tile(Staged& st, int k, const int32_t (&e)[kStageRows], int wave, int lane,
+// Fetch tile k (tokens 32k .. 32k+31) from HBM into the LDS buffer `buf`;
+// `e` holds its table entries when B >= 4 (read a step earlier), else every
+// thread looks up its own row.  Rows past the context or with an id outside
+// the pool read a row of some valid block (a fixed number of loads per
+// tile) and are zeroed by finish_tile.
+template <int B, bool kStream>
+__device__ __forceinline__ void fetch_tile(Staged& st, unsigned char* buf, int k, const int32_t (&e)[kStageRows], int wave, int lane,
                                            int n, const int32_t* __restrict__ trow,
                                            const _Float16* __restrict__ kbase, const _Float16* __restrict__ vbase,
                                            int64_t blk_stride, int32_t num_blocks) {
+    // kStream: every K/V byte is read by one workgroup only (all query rows
+    // of a sequence fit one row tile), so the loads are nontemporal (the nt
+    // bit of the cache policy); otherwise later row tiles of the sequence
+    // re-read the tile and the default policy keeps it for them
+    constexpr int kLoadPolicy = kStream ? 2 : 0;
     const int col = lane & 15;
 #pragma unroll
     for (int i = 0; i < kStageRows; ++i) {
@@ -134,37 +154,39 @@ __device__ __forceinline__ void fetch_tile(Staged& st, int k, const int32_t (&e)
         }
         const bool in_pool = (uint32_t)phys < (uint32_t)num_blocks;
         const bool ok = t < n && in_pool;
-        const int64_t off = (int64_t)(in_pool ? phys : 0) * blk_stride + row * kD + col * 8;
-        // unconditional loads (a row past the context or with an id outside
-        // the pool reads a row of some valid block and is zeroed when
-        // stored): a fixed number of loads per tile lets the waits count
-        // only the older tile's
-        st.k[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + off));
-        st.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + off));
+        // LDS row r = stage row, position col holds chunk col ^ (r & 15) of K
+        // and chunk col ^ 2(r & 3) of V
+        const int r = stage_token0(0, wave, i) + (lane >> 4);
+        const int64_t off = (int64_t)(in_pool ? phys : 0) * blk_stride + row * kD;
+        const int ck = col ^ (r & 15);
+        const int cv = col ^ (2 * (r & 3));
+        unsigned char* kdst = buf + stage_token0(0, wave, i) * kPitch;
+        unsigned char* vdst = buf + kTileBytes + stage_token0(0, wave, i) * kPitchV;
+        __builtin_amdgcn_global_load_lds((const void*)(kbase + off + ck * 8),
+                                         (__attribute__((address_space(3))) void*)kdst, 16, 0, kLoadPolicy);
+        __builtin_amdgcn_global_load_lds((const void*)(vbase + off + cv * 8),
+                                         (__attribute__((address_space(3))) void*)vdst, 16, 0, kLoadPolicy);
         st.ok[i] = ok;
     }
 }
 
-__device__ __forceinline__ void store_tile(const Staged& st, unsigned char* buf, unsigned char* flags, int wave,
-                                           int lane) {
+// After this thread's loads of the tile landed: zero its rows that are not
+// valid (past the context or outside the pool) and write the flags.
+__device__ __forceinline__ void finish_tile(const Staged& st, unsigned char* buf, unsigned char* flags, int wave,
+                                            int lane) {
     const int col = lane & 15;
     bool all_ok = true;
 #pragma unroll
     for (int i = 0; i < kStageRows; ++i) all_ok = all_ok && st.ok[i];
-    if (__all(all_ok)) {                                   // no row to zero (uniform)
-#pragma unroll
-        for (int i = 0; i < kStageRows; ++i) {
-            const int row = stage_token0(0, wave, i) + (lane >> 4);
-            *reinterpret_cast<u32x4*>(buf + row * kPitch + col * 16) = st.k[i];
-            *reinterpret_cast<u32x4*>(buf + kTileBytes + row * kPitchV + col * 16) = st.v[i];
-        }
-    } else {
+    if (!__all(all_ok)) {
 #pragma unroll
         for (int i = 0; i < kStageRows; ++i) {
             const int row = stage_token0(0, wave, i) + (lane >> 4);
             const u32x4 z = {0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(buf + row * kPitch + col * 16) = st.ok[i] ? st.k[i] : z;
-            *reinterpret_cast<u32x4*>(buf + kTileBytes + row * kPitchV + col * 16) = st.ok[i] ? st.v[i] : z;
+            if (!st.ok[i]) {
+                *reinterpret_cast<u32x4*>(buf + row * kPitch + col * 16) = z;
+                *reinterpret_cast<u32x4*>(buf + kTileBytes + row * kPitchV + col * 16) = z;
+            }
         }
     }
 #pragma unroll
@@ -230,7 +252,7 @@ __device__ __forceinline__ void consume_lds_tile(Softmax (&st)[kNT], const unsig
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const half8_t_ a = __builtin_bit_cast(half8_t_, *reinterpret_cast<const u32x4*>(
-                                                               kb + (16 * h + n) * kPitch + 64 * c + 16 * j));
+                                                               kb + (16 * h + n) * kPitch + 16 * ((4 * c + j) ^ n)));
 #pragma unroll
             for (int t = 0; t < kNT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[t][c], acc[t], 0, 0, 0);
         }
@@ -307,27 +329,51 @@ __device__ __forceinline__ void consume_lds_tile(Softmax (&st)[kNT], const unsig
     typedef short v4s_ __attribute__((ext_vector_type(4)));
     const int e4 = (lane & 15) >> 2;
     const int q4 = lane & 3;
+    static_assert(NS == 1, "one 32-token PV slab per tile");
+    // transpose reads issued in inline asm (with their wait inside the same
+    // block): the builtin carries no memory operand, so the compiler would
+    // wait for every load into LDS still in flight before it
+    const unsigned char* lo = vb + (4 * j + e4) * kPitchV + 8 * q4;
+    uint32_t a[4];
 #pragma unroll
-    for (int u = 0; u < NS; ++u) {
-        const unsigned char* lo = vb + (32 * u + 4 * j + e4) * kPitchV + 8 * q4;
-        const unsigned char* hi = lo + 16 * kPitchV;
+    for (int c = 0; c < 4; ++c)
+        a[c] = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)(lo + 32 * (c ^ e4));
+    v4s_ r[16];
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16\n\t"
+        "ds_read_b64_tr_b16 %1, %16 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %2, %17\n\t"
+        "ds_read_b64_tr_b16 %3, %17 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %4, %18\n\t"
+        "ds_read_b64_tr_b16 %5, %18 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %6, %19\n\t"
+        "ds_read_b64_tr_b16 %7, %19 offset:4096\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:128\n\t"
+        "ds_read_b64_tr_b16 %9, %16 offset:4224\n\t"
+        "ds_read_b64_tr_b16 %10, %17 offset:128\n\t"
+        "ds_read_b64_tr_b16 %11, %17 offset:4224\n\t"
+        "ds_read_b64_tr_b16 %12, %18 offset:128\n\t"
+        "ds_read_b64_tr_b16 %13, %18 offset:4224\n\t"
+        "ds_read_b64_tr_b16 %14, %19 offset:128\n\t"
+        "ds_read_b64_tr_b16 %15, %19 offset:4224\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+          "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]),
+          "=&v"(r[14]), "=&v"(r[15])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+        : "memory");
 #pragma unroll
-        for (int c = 0; c < kDTiles; ++c) {
-            const v4s_ b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4s_*)(lo + 32 * c));
-            const v4s_ b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) v4s_*)(hi + 32 * c));
-            const half4_t h0 = __builtin_bit_cast(half4_t, b0);
-            const half4_t h1 = __builtin_bit_cast(half4_t, b1);
-            const half8_t_ b = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+    for (int c = 0; c < kDTiles; ++c) {
+        const half4_t h0 = __builtin_bit_cast(half4_t, r[2 * c]);
+        const half4_t h1 = __builtin_bit_cast(half4_t, r[2 * c + 1]);
+        const half8_t_ b = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
 #pragma unroll
-            for (int t = 0; t < kNT; ++t)
-                st[t].o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p[t][u], b, st[t].o[c], 0, 0, 0);
-        }
+        for (int t = 0; t < kNT; ++t)
+            st[t].o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p[t][0], b, st[t].o[c], 0, 0, 0);
     }
 }
 
-template <int B>
+template <int B, bool kStream>
 __global__ void __launch_bounds__(kThreads)
 prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, int32_t num_tokens,
                     const _Float16* __restrict__ k_cache, const _Float16* __restrict__ v_cache,
@@ -336,8 +382,14 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
                     int32_t num_blocks, float scale_log2, int32_t max_query_len, int64_t len_cap,
                     float* __restrict__ ws_ml, float* __restrict__ ws_acc, int32_t tiles_per_part,
                     int32_t num_parts) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2][kTileBytes + kTileBytesV];
-    __shared__ __attribute__((aligned(4))) unsigned char lds_flags[2][kKvTile];
+    // three stage buffers as distinct objects, so that the compiler can
+    // tell the buffer a step reads from the ones whose loads are in flight
+    __shared__ __attribute__((aligned(16))) unsigned char ldsA[kBufBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char ldsB[kBufBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char ldsC[kBufBytes];
+    __shared__ __attribute__((aligned(4))) unsigned char flA[kKvTile];
+    __shared__ __attribute__((aligned(4))) unsigned char flB[kKvTile];
+    __shared__ __attribute__((aligned(4))) unsigned char flC[kKvTile];
     const int kvh = blockIdx.x;
     const int s = blockIdx.y;
     // grid z = (row tile, context part), parts fastest; last row tile first
@@ -426,25 +478,33 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
         for (int c = 0; c < kDTiles; ++c) st[t].o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Pipeline: tile k is consumed from LDS while tile k+1 waits in
-    // registers and tile k+2 is being fetched -- each fetch has two tile
-    // periods to land; the table entries of tile k+3 are read meanwhile.
-    // Register sets R0/R1 alternate; LDS buffers too.  Every step issues
-    // the same loads (tiles past the last one read clamped rows that are
-    // never used), so the waits before a store count only the older tile.
-    Staged R0, R1;
+    // Pipeline: tile k is consumed from its LDS buffer while tile k+1 lands
+    // in the next and tile k+2 is being fetched into the third -- each
+    // fetch has two tile periods to land; the table entries of tile k+3 are
+    // read meanwhile.  Tiles kb, kb+1, kb+2, ... use buffers A, B, C, A, ...
+    // (the loop is unrolled by three, so every step names its buffers at
+    // compile time).  Every step issues the same 4 loads per thread (tiles
+    // past the last one read clamped rows that are never used), so waiting
+    // for all but the newest 4 is waiting for tile k+1.  The waits are
+    // explicit and the barriers bare: a fence at the barrier would wait for
+    // every load in flight, the newest tile's too.
+    Staged SA, SB, SC;
     int32_t e[kStageRows] = {};
     const int kb = k_begin;
     if constexpr (B >= 4) table_entries<B>(e, kb, wave, n, trow);
-    fetch_tile<B>(R0, kb, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
+    fetch_tile<B, kStream>(SA, ldsA, kb, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
     if constexpr (B >= 4) table_entries<B>(e, kb + 1, wave, n, trow);
-    fetch_tile<B>(R1, kb + 1, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
+    fetch_tile<B, kStream>(SB, ldsB, kb + 1, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
     if constexpr (B >= 4) table_entries<B>(e, kb + 2, wave, n, trow);
-    store_tile(R0, lds[kb & 1], lds_flags[kb & 1], wave, lane);
-    __syncthreads();
-    auto step = [&](int k, Staged& fetch_into, const Staged& next) {
-        const int cur = k & 1;
-        fetch_tile<B>(fetch_into, k + 2, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
+    PA_WAIT_VM(2 * kStageRows);
+    finish_tile(SA, ldsA, flA, wave, lane);
+    PA_WAIT_LGKM0();
+    __builtin_amdgcn_s_barrier();
+    // step k: fetch tile k+2 into `fb`, consume tile k from `cb`, then wait
+    // for tile k+1 (in `nb`) and finish it
+    auto step = [&](int k, unsigned char* cb, unsigned char* cf, unsigned char* nb, unsigned char* nf,
+                    const Staged& ns, unsigned char* fb, Staged& fs) {
+        fetch_tile<B, kStream>(fs, fb, k + 2, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
         if constexpr (B >= 4) table_entries<B>(e, k + 3, wave, n, trow);
         if (k < my_end) {
             // uniform: tile below the wave's first row and wholly valid
@@ -453,19 +513,25 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
                 bool all_ok = true;          // the flags of tokens 16h + 4*jg .. +3, for every h
 #pragma unroll
                 for (int h = 0; h < kKvTile / 16; ++h)
-                    all_ok = all_ok && *reinterpret_cast<const uint32_t*>(lds_flags[cur] + 16 * h + 4 * jg) ==
-                                           0x01010101u;
+                    all_ok = all_ok && *reinterpret_cast<const uint32_t*>(cf + 16 * h + 4 * jg) == 0x01010101u;
                 interior = __all(all_ok);
             }
-            consume_lds_tile(st, lds[cur], lds_flags[cur], k * kKvTile, interior, qb, c_log2, lane, rw);
+            consume_lds_tile(st, cb, cf, k * kKvTile, interior, qb, c_log2, lane, rw);
         }
-        store_tile(next, lds[cur ^ 1], lds_flags[cur ^ 1], wave, lane);
-        __syncthreads();
+        PA_WAIT_VM(2 * kStageRows);
+        finish_tile(ns, nb, nf, wave, lane);
+        PA_WAIT_LGKM0();
+        __builtin_amdgcn_s_barrier();
     };
-    for (int k = kb; k < k_end; k += 2) {   // an odd count runs one idle step at the end
-        step(k, R0, R1);                    // R0 (tile k, now in LDS) refills with k+2; R1 holds k+1
-        step(k + 1, R1, R0);
+    for (int k = kb;;) {
+        step(k, ldsA, flA, ldsB, flB, SB, ldsC, SC);
+        if (++k >= k_end) break;
+        step(k, ldsB, flB, ldsC, flC, SC, ldsA, SA);
+        if (++k >= k_end) break;
+        step(k, ldsC, flC, ldsA, flA, SA, ldsB, SB);
+        if (++k >= k_end) break;
     }
+    PA_WAIT_VM(0);                          // no load into LDS outstanding at exit
 
     if (num_parts > 1) {
         // unnormalised partial state of every row for the merge kernel:
@@ -559,16 +625,17 @@ using PrefillFn = void (*)(_Float16*, const _Float16*, int32_t, const _Float16*,
                            int32_t, const int32_t*, const int32_t*, int32_t, int32_t, int32_t, float, int32_t,
                            int64_t, float*, float*, int32_t, int32_t);
 
+template <bool kStream>
 PrefillFn pick(int32_t b) {
     switch (b) {
-        case 1: return prefill_mfma_kernel<1>;
-        case 2: return prefill_mfma_kernel<2>;
-        case 4: return prefill_mfma_kernel<4>;
-        case 8: return prefill_mfma_kernel<8>;
-        case 16: return prefill_mfma_kernel<16>;
-        case 32: return prefill_mfma_kernel<32>;
-        case 64: return prefill_mfma_kernel<64>;
-        case 128: return prefill_mfma_kernel<128>;
+        case 1: return prefill_mfma_kernel<1, kStream>;
+        case 2: return prefill_mfma_kernel<2, kStream>;
+        case 4: return prefill_mfma_kernel<4, kStream>;
+        case 8: return prefill_mfma_kernel<8, kStream>;
+        case 16: return prefill_mfma_kernel<16, kStream>;
+        case 32: return prefill_mfma_kernel<32, kStream>;
+        case 64: return prefill_mfma_kernel<64, kStream>;
+        case 128: return prefill_mfma_kernel<128, kStream>;
         default: return nullptr;
     }
 }
@@ -624,7 +691,7 @@ SplitPlan split_plan(int32_t num_tokens, int32_t num_seqs, int32_t num_heads, in
 extern "C" size_t pa_prefill_workspace_size(int32_t num_tokens, int32_t num_seqs, int32_t num_heads,
                                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                             int32_t max_blocks_per_seq, int32_t max_query_len) {
-    if (head_dim != kD || !pick(block_size) || num_tokens < 0 || num_seqs < 0 || num_heads <= 0 ||
+    if (head_dim != kD || !pick<false>(block_size) || num_tokens < 0 || num_seqs < 0 || num_heads <= 0 ||
         num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || max_blocks_per_seq < 0 || max_query_len < 0)
         return (size_t)-1;
     return split_plan(num_tokens, num_seqs, num_heads, num_kv_heads, (int64_t)max_blocks_per_seq * block_size,
@@ -640,7 +707,7 @@ extern "C" int pa_prefill(void* out, const void* q, int32_t num_tokens, const vo
                           void* stream) {
     if (dtype != PA_DTYPE_F16) return pa::fail(PA_ERR_UNSUPPORTED, "pa_prefill: dtype %d", dtype);
     if (head_dim != kD) return pa::fail(PA_ERR_UNSUPPORTED, "pa_prefill: head_dim %d (only %d)", head_dim, kD);
-    if (!pick(block_size)) return pa::fail(PA_ERR_UNSUPPORTED, "pa_prefill: block_size %d", block_size);
+    if (!pick<false>(block_size)) return pa::fail(PA_ERR_UNSUPPORTED, "pa_prefill: block_size %d", block_size);
     if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
         num_blocks <= 0 || max_blocks_per_seq < 0 || max_query_len < 0)
         return pa::fail(PA_ERR_INVALID, "pa_prefill: bad sizes (S=%d H=%d Hkv=%d NB=%d W=%d max_q=%d)", num_seqs,
@@ -671,7 +738,12 @@ extern "C" int pa_prefill(void* out, const void* q, int32_t num_tokens, const vo
     float* ws_acc = P.num_parts > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + P.ml_bytes) : nullptr;
     const float scale_log2 = (float)((double)scale * kLog2e);
     auto st = static_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(pick(block_size),
+    // one row tile per (KV head, sequence): each K/V tile is read once, so
+    // stream it past the caches (measured on 4 x 8192 cached + 32 new: 106
+    // against 125 us); several row tiles re-read it (prompts: 233 against 245
+    // us with nontemporal loads)
+    const bool stream_kv = row_tiles == 1;
+    hipLaunchKernelGGL(stream_kv ? pick<true>(block_size) : pick<false>(block_size),
                        dim3((unsigned)num_kv_heads, (unsigned)num_seqs, (unsigned)(row_tiles * P.num_parts)),
                        dim3(kThreads), 0, st, static_cast<_Float16*>(out), static_cast<const _Float16*>(q), num_tokens,
                        static_cast<const _Float16*>(k_cache), static_cast<const _Float16*>(v_cache), block_tables,
