@@ -20,15 +20,14 @@
 //    CU.  Grid x = KV head (fastest, for XCD balance), y = sequence, z = row
 //    tile, issued last row tile first so the longest causal ranges start
 //    earliest.
-//  * K/V tiles of 32 tokens are staged through LDS once per workgroup and
+//  * K/V tiles of 64 tokens are staged through LDS once per workgroup and
 //    read by all 4 waves.  The loads go from HBM straight into LDS
 //    (global_load_lds_dwordx4: a wave instruction writes 1 KiB, 4 token rows
-//    of 256 bytes, 16 bytes per lane), two tiles ahead, into the third of
-//    three buffers -- no registers hold a tile in flight and no LDS store
-//    instructions run.  Each thread issues 4 such loads per tile (2 rows of
-//    K, 2 of V) and every step issues them (tiles past the last read
-//    clamped rows), so an explicit wait for all but the newest 4 is a wait
-//    for the next tile; one barrier per tile.  A wave's 4 rows of one load
+//    of 256 bytes, 16 bytes per lane), one tile ahead, into the other of two
+//    buffers (32 KiB each) -- no registers hold a tile in flight and no LDS
+//    store instructions run.  Each thread issues 8 such loads per tile (4
+//    rows of K, 4 of V), waited for explicitly before the step's barrier;
+//    one barrier per tile.  A wave's 4 rows of one load
 //    share a table entry (blocks of 4 or more tokens), read a tile ahead
 //    with a scalar load.  The DMA writes lane i's 16 bytes at byte 16i, so
 //    bank conflicts are avoided by choosing what each lane loads: position
@@ -40,7 +39,7 @@
 //    l, one 16-byte LDS read of K per two MFMAs; Q^T operands stay in
 //    registers.  S^T lands with each lane holding 8 scores of one row
 //    (tokens 4j..4j+3 and 16+4j..16+4j+3 of the tile) -- exactly that lane's
-//    A operand of P for the 32-token PV product, so the online softmax (base
+//    A operand of P for a 32-token PV product, so the online softmax (base
 //    2) runs in place and P goes to the matrix core as fp16; the row sum
 //    adds the same rounded weights.  Row max and sum cross the 4 lanes of a
 //    row with v_permlane32_swap / v_permlane16_swap.  Tiles wholly before a
@@ -74,7 +73,7 @@ constexpr double kLog2e = 1.4426950408889634073599246810019;
 // One K/V tile in LDS: kKvTile token rows of K and of V, 256 bytes each with
 // their 16-byte chunks permuted per row (see fetch_tile), plus a flag per
 // token (inside the context and the pool) in an array of its own.
-constexpr int kKvTile = 32;
+constexpr int kKvTile = 64;
 constexpr int kPitch = kD * 2;                // K rows (16-byte chunks XOR-swizzled by row & 15)
 constexpr int kPitchV = kD * 2;               // V rows (chunks swizzled by 2 * (row & 3))
 constexpr int kTileBytes = kKvTile * kPitch;
@@ -120,7 +119,7 @@ __device__ __forceinline__ void table_entries(int32_t (&e)[kStageRows], int k, i
     }
 }
 
-// Fetch tile k (tokens 32k .. 32k+31) from HBM into the LDS buffer `buf`;
+// Fetch tile k (tokens 64k .. 64k+63) from HBM into the LDS buffer `buf`;
 // `e` holds its table entries when B >= 4 (read a step earlier), else every
 // thread looks up its own row.  Rows past the context or with an id outside
 // the pool read a row of some valid block (a fixed number of loads per
@@ -227,9 +226,10 @@ __device__ __forceinline__ float row_sum4(float x) {
 // v_mfma_f32_16x16x32_f16.  Every operand read from LDS feeds kNT products.
 //   QK, per 16-token half h: S^T[token][row] = sum_d K[token][d] Q[row][d];
 //     MFMA c takes d = 32c + 8*(l/16) + 0..7 in lane l (one 16-byte LDS read).
-//   PV: k = 32 tokens; lane (n, j) supplies P[row n][tokens 4j..4j+3 and
-//     16+4j..16+4j+3] -- exactly the scores it holds -- and V rows of the
-//     same tokens at column 16c + n for d-tile c (LDS transpose reads).
+//   PV, per 32-token slab u: k = 32 tokens; lane (n, j) supplies P[row
+//     n][tokens 32u + 4j..4j+3 and 32u + 16+4j..16+4j+3] -- exactly the
+//     scores it holds -- and V rows of the same tokens at column 16c + n for
+//     d-tile c (LDS transpose reads).
 // `interior` (uniform): every token of the tile is valid and at or before
 // the first row's position, so no score is masked.  The exponent of a
 // weight is one FMA of the raw score: c = scale * log2(e) > 0, so the raw
@@ -329,7 +329,6 @@ __device__ __forceinline__ void consume_lds_tile(Softmax (&st)[kNT], const unsig
     typedef short v4s_ __attribute__((ext_vector_type(4)));
     const int e4 = (lane & 15) >> 2;
     const int q4 = lane & 3;
-    static_assert(NS == 1, "one 32-token PV slab per tile");
     // transpose reads issued in inline asm (with their wait inside the same
     // block): the builtin carries no memory operand, so the compiler would
     // wait for every load into LDS still in flight before it
@@ -338,39 +337,47 @@ __device__ __forceinline__ void consume_lds_tile(Softmax (&st)[kNT], const unsig
 #pragma unroll
     for (int c = 0; c < 4; ++c)
         a[c] = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)(lo + 32 * (c ^ e4));
-    v4s_ r[16];
-    asm volatile(
-        "ds_read_b64_tr_b16 %0, %16\n\t"
-        "ds_read_b64_tr_b16 %1, %16 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %2, %17\n\t"
-        "ds_read_b64_tr_b16 %3, %17 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %4, %18\n\t"
-        "ds_read_b64_tr_b16 %5, %18 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %6, %19\n\t"
-        "ds_read_b64_tr_b16 %7, %19 offset:4096\n\t"
-        "ds_read_b64_tr_b16 %8, %16 offset:128\n\t"
-        "ds_read_b64_tr_b16 %9, %16 offset:4224\n\t"
-        "ds_read_b64_tr_b16 %10, %17 offset:128\n\t"
-        "ds_read_b64_tr_b16 %11, %17 offset:4224\n\t"
-        "ds_read_b64_tr_b16 %12, %18 offset:128\n\t"
-        "ds_read_b64_tr_b16 %13, %18 offset:4224\n\t"
-        "ds_read_b64_tr_b16 %14, %19 offset:128\n\t"
-        "ds_read_b64_tr_b16 %15, %19 offset:4224\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
-          "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]),
-          "=&v"(r[14]), "=&v"(r[15])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
-        : "memory");
+#define PF_TR16(O0, O1, O2, O3)                                                                              \
+    asm volatile(                                                                                            \
+        "ds_read_b64_tr_b16 %0, %16 offset:" #O0 "\n\t"                                                     \
+        "ds_read_b64_tr_b16 %1, %16 offset:" #O1 "\n\t"                                                     \
+        "ds_read_b64_tr_b16 %2, %17 offset:" #O0 "\n\t"                                                     \
+        "ds_read_b64_tr_b16 %3, %17 offset:" #O1 "\n\t"                                                     \
+        "ds_read_b64_tr_b16 %4, %18 offset:" #O0 "\n\t"                                                     \
+        "ds_read_b64_tr_b16 %5, %18 offset:" #O1 "\n\t"                                                     \
+        "ds_read_b64_tr_b16 %6, %19 offset:" #O0 "\n\t"                                                     \
+        "ds_read_b64_tr_b16 %7, %19 offset:" #O1 "\n\t"                                                     \
+        "ds_read_b64_tr_b16 %8, %16 offset:" #O2 "\n\t"                                                     \
+        "ds_read_b64_tr_b16 %9, %16 offset:" #O3 "\n\t"                                                     \
+        "ds_read_b64_tr_b16 %10, %17 offset:" #O2 "\n\t"                                                    \
+        "ds_read_b64_tr_b16 %11, %17 offset:" #O3 "\n\t"                                                    \
+        "ds_read_b64_tr_b16 %12, %18 offset:" #O2 "\n\t"                                                    \
+        "ds_read_b64_tr_b16 %13, %18 offset:" #O3 "\n\t"                                                    \
+        "ds_read_b64_tr_b16 %14, %19 offset:" #O2 "\n\t"                                                    \
+        "ds_read_b64_tr_b16 %15, %19 offset:" #O3 "\n\t"                                                    \
+        "s_waitcnt lgkmcnt(0)"                                                                               \
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),        \
+          "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]),    \
+          "=&v"(r[14]), "=&v"(r[15])                                                                         \
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])                                                         \
+        : "memory")
+    static_assert(NS == 2, "two 32-token PV slabs per tile");
 #pragma unroll
-    for (int c = 0; c < kDTiles; ++c) {
-        const half4_t h0 = __builtin_bit_cast(half4_t, r[2 * c]);
-        const half4_t h1 = __builtin_bit_cast(half4_t, r[2 * c + 1]);
-        const half8_t_ b = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+    for (int u = 0; u < NS; ++u) {
+        v4s_ r[16];
+        if (u == 0) PF_TR16(0, 4096, 128, 4224);
+        else PF_TR16(8192, 12288, 8320, 12416);
 #pragma unroll
-        for (int t = 0; t < kNT; ++t)
-            st[t].o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p[t][0], b, st[t].o[c], 0, 0, 0);
+        for (int c = 0; c < kDTiles; ++c) {
+            const half4_t h0 = __builtin_bit_cast(half4_t, r[2 * c]);
+            const half4_t h1 = __builtin_bit_cast(half4_t, r[2 * c + 1]);
+            const half8_t_ b = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+#pragma unroll
+            for (int t = 0; t < kNT; ++t)
+                st[t].o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p[t][u], b, st[t].o[c], 0, 0, 0);
+        }
     }
+#undef PF_TR16
 }
 
 template <int B, bool kStream>
@@ -382,14 +389,12 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
                     int32_t num_blocks, float scale_log2, int32_t max_query_len, int64_t len_cap,
                     float* __restrict__ ws_ml, float* __restrict__ ws_acc, int32_t tiles_per_part,
                     int32_t num_parts) {
-    // three stage buffers as distinct objects, so that the compiler can
-    // tell the buffer a step reads from the ones whose loads are in flight
+    // two stage buffers as distinct objects, so that the compiler can tell
+    // the buffer a step reads from the one whose loads are in flight
     __shared__ __attribute__((aligned(16))) unsigned char ldsA[kBufBytes];
     __shared__ __attribute__((aligned(16))) unsigned char ldsB[kBufBytes];
-    __shared__ __attribute__((aligned(16))) unsigned char ldsC[kBufBytes];
     __shared__ __attribute__((aligned(4))) unsigned char flA[kKvTile];
     __shared__ __attribute__((aligned(4))) unsigned char flB[kKvTile];
-    __shared__ __attribute__((aligned(4))) unsigned char flC[kKvTile];
     const int kvh = blockIdx.x;
     const int s = blockIdx.y;
     // grid z = (row tile, context part), parts fastest; last row tile first
@@ -478,34 +483,31 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
         for (int c = 0; c < kDTiles; ++c) st[t].o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // Pipeline: tile k is consumed from its LDS buffer while tile k+1 lands
-    // in the next and tile k+2 is being fetched into the third -- each
-    // fetch has two tile periods to land; the table entries of tile k+3 are
-    // read meanwhile.  Tiles kb, kb+1, kb+2, ... use buffers A, B, C, A, ...
-    // (the loop is unrolled by three, so every step names its buffers at
-    // compile time).  Every step issues the same 4 loads per thread (tiles
-    // past the last one read clamped rows that are never used), so waiting
-    // for all but the newest 4 is waiting for tile k+1.  The waits are
-    // explicit and the barriers bare: a fence at the barrier would wait for
-    // every load in flight, the newest tile's too.
-    Staged SA, SB, SC;
+    // Pipeline: tile k is consumed from its LDS buffer while tile k+1 is
+    // being fetched into the other -- each fetch has one tile period (64
+    // tokens of products) to land; the table entries of tile k+2 are read
+    // meanwhile.  Tiles kb, kb+1, ... use buffers A, B, A, ... (the loop is
+    // unrolled by two, so every step names its buffers at compile time).
+    // The waits are explicit and the barriers bare: the compiler, left to
+    // itself, would wait for the loads in flight before every LDS read it
+    // cannot tell apart from the buffer being filled.  Three 32-token
+    // buffers (tile k+2 in flight while waiting for k+1) were slower on
+    // every prompt workload (8192-token prompts 641 against 721 TFLOP/s)
+    // and faster only on short chunks over long caches (4 x 8192 cached +
+    // 32 new: 106 against 110 us).
+    Staged SA, SB;
     int32_t e[kStageRows] = {};
     const int kb = k_begin;
     if constexpr (B >= 4) table_entries<B>(e, kb, wave, n, trow);
     fetch_tile<B, kStream>(SA, ldsA, kb, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
     if constexpr (B >= 4) table_entries<B>(e, kb + 1, wave, n, trow);
-    fetch_tile<B, kStream>(SB, ldsB, kb + 1, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
-    if constexpr (B >= 4) table_entries<B>(e, kb + 2, wave, n, trow);
-    PA_WAIT_VM(2 * kStageRows);
+    PA_WAIT_VM(0);
     finish_tile(SA, ldsA, flA, wave, lane);
     PA_WAIT_LGKM0();
     __builtin_amdgcn_s_barrier();
-    // step k: fetch tile k+2 into `fb`, consume tile k from `cb`, then wait
-    // for tile k+1 (in `nb`) and finish it
-    auto step = [&](int k, unsigned char* cb, unsigned char* cf, unsigned char* nb, unsigned char* nf,
-                    const Staged& ns, unsigned char* fb, Staged& fs) {
-        fetch_tile<B, kStream>(fs, fb, k + 2, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
-        if constexpr (B >= 4) table_entries<B>(e, k + 3, wave, n, trow);
+    auto step = [&](int k, unsigned char* cb, unsigned char* cf, unsigned char* nb, unsigned char* nf, Staged& ns) {
+        fetch_tile<B, kStream>(ns, nb, k + 1, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
+        if constexpr (B >= 4) table_entries<B>(e, k + 2, wave, n, trow);
         if (k < my_end) {
             // uniform: tile below the wave's first row and wholly valid
             bool interior = k * kKvTile + kKvTile - 1 <= first_pos;
@@ -518,17 +520,15 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
             }
             consume_lds_tile(st, cb, cf, k * kKvTile, interior, qb, c_log2, lane, rw);
         }
-        PA_WAIT_VM(2 * kStageRows);
+        PA_WAIT_VM(0);
         finish_tile(ns, nb, nf, wave, lane);
         PA_WAIT_LGKM0();
         __builtin_amdgcn_s_barrier();
     };
     for (int k = kb;;) {
-        step(k, ldsA, flA, ldsB, flB, SB, ldsC, SC);
+        step(k, ldsA, flA, ldsB, flB, SB);
         if (++k >= k_end) break;
-        step(k, ldsB, flB, ldsC, flC, SC, ldsA, SA);
-        if (++k >= k_end) break;
-        step(k, ldsC, flC, ldsA, flA, SA, ldsB, SB);
+        step(k, ldsB, flB, ldsA, flA, SA);
         if (++k >= k_end) break;
     }
     PA_WAIT_VM(0);                          // no load into LDS outstanding at exit
@@ -647,11 +647,11 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Context split.  Workgroups per part: one per (KV head, sequence, row
 // tile).  When they fill at most half the resident slots (2 per CU, 512),
 // the context is cut into floor(512 / workgroups) parts of at least 4 tiles
-// (128 tokens): one full round of workgroups, each leaving the partial
+// (256 tokens): one full round of workgroups, each leaving the partial
 // (m, l, O) of its rows for a merge kernel.  (A second, partial round costs
-// more than it brings: on 4 x 8192 cached + 32 new, 512 workgroups run in
-// 113 us, 768 in 149, 1024 in 147, 2048 in 203.)  The bound on the context
-// is max_blocks_per_seq * block_size (host-known).
+// more than it brings: on 4 x 8192 cached + 32 new, with 32-token tiles,
+// 512 workgroups ran in 113 us, 768 in 149, 1024 in 147, 2048 in 203.)  The
+// bound on the context is max_blocks_per_seq * block_size (host-known).
 struct SplitPlan {
     int32_t row_tiles;
     int32_t num_parts;
