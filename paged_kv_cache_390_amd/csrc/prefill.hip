@@ -17,9 +17,10 @@
 //    groups of 16 -- the N side of its MFMA tiles -- so that every K or V
 //    operand read from LDS feeds two products.  A 256-thread workgroup is 4
 //    such waves (128 rows) of one (KV head, sequence); 2 workgroups share a
-//    CU.  Grid x = KV head (fastest, for XCD balance), y = sequence, z = row
-//    tile, issued last row tile first so the longest causal ranges start
-//    earliest.
+//    CU.  The grid is one-dimensional and XCD-grouped: all row tiles of a
+//    (KV head, sequence) pair run together on one XCD, last row tile first
+//    (the longest causal range starts earliest), so that the K/V tiles they
+//    all walk are read from HBM once and then served by that XCD's L2.
 //  * K/V tiles of 64 tokens are staged through LDS once per workgroup and
 //    read by all 4 waves.  The loads go from HBM straight into LDS
 //    (global_load_lds_dwordx4: a wave instruction writes 1 KiB, 4 token rows
@@ -388,18 +389,38 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
                     const int32_t* __restrict__ query_start, int32_t num_heads, int32_t num_kv_heads,
                     int32_t num_blocks, float scale_log2, int32_t max_query_len, int64_t len_cap,
                     float* __restrict__ ws_ml, float* __restrict__ ws_acc, int32_t tiles_per_part,
-                    int32_t num_parts) {
+                    int32_t num_parts, int32_t num_seqs, int32_t row_tiles, int32_t xcd_grouped) {
     // two stage buffers as distinct objects, so that the compiler can tell
     // the buffer a step reads from the one whose loads are in flight
     __shared__ __attribute__((aligned(16))) unsigned char ldsA[kBufBytes];
     __shared__ __attribute__((aligned(16))) unsigned char ldsB[kBufBytes];
     __shared__ __attribute__((aligned(4))) unsigned char flA[kKvTile];
     __shared__ __attribute__((aligned(4))) unsigned char flB[kKvTile];
-    const int kvh = blockIdx.x;
-    const int s = blockIdx.y;
-    // grid z = (row tile, context part), parts fastest; last row tile first
-    const int rtile = (int)(gridDim.z / num_parts) - 1 - (int)blockIdx.z / num_parts;
-    const int part = (int)blockIdx.z % num_parts;
+    // One-dimensional grid over (KV head, sequence) pairs x row tiles x
+    // context parts.  Workgroups are dealt to the 8 XCDs round-robin in
+    // linear order; with xcd_grouped (pairs a multiple of 8) workgroup L
+    // runs item L / 8 of XCD L % 8, whose items are the row tiles and parts
+    // of its pairs (pair q on XCD q % 8), pair by pair: the row tiles of a
+    // pair, which all walk the same K/V tiles, run together on one XCD and
+    // share its L2.  Otherwise the pair is fastest (KV head first).  Either
+    // way the last row tile of a pair comes first (the longest causal range
+    // starts earliest) and parts are fastest within a row tile.
+    const int64_t L = blockIdx.x;
+    const int64_t pairs = (int64_t)num_kv_heads * num_seqs;
+    const int64_t rp_n = (int64_t)row_tiles * num_parts;
+    int64_t pair, rp;
+    if (xcd_grouped) {
+        const int64_t w = L >> 3;
+        pair = (L & 7) + 8 * (w / rp_n);
+        rp = w % rp_n;
+    } else {
+        pair = L % pairs;
+        rp = L / pairs;
+    }
+    const int kvh = (int)(pair % num_kv_heads);
+    const int s = (int)(pair / num_kv_heads);
+    const int rtile = row_tiles - 1 - (int)(rp / num_parts);
+    const int part = (int)(rp % num_parts);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = num_heads / num_kv_heads;
@@ -623,7 +644,7 @@ prefill_merge_kernel(_Float16* __restrict__ out, const float* __restrict__ ws_ml
 
 using PrefillFn = void (*)(_Float16*, const _Float16*, int32_t, const _Float16*, const _Float16*, const int32_t*,
                            int32_t, const int32_t*, const int32_t*, int32_t, int32_t, int32_t, float, int32_t,
-                           int64_t, float*, float*, int32_t, int32_t);
+                           int64_t, float*, float*, int32_t, int32_t, int32_t, int32_t, int32_t);
 
 template <bool kStream>
 PrefillFn pick(int32_t b) {
@@ -743,12 +764,15 @@ extern "C" int pa_prefill(void* out, const void* q, int32_t num_tokens, const vo
     // against 125 us); several row tiles re-read it (prompts: 233 against 245
     // us with nontemporal loads)
     const bool stream_kv = row_tiles == 1;
-    hipLaunchKernelGGL(stream_kv ? pick<true>(block_size) : pick<false>(block_size),
-                       dim3((unsigned)num_kv_heads, (unsigned)num_seqs, (unsigned)(row_tiles * P.num_parts)),
+    const int64_t pairs = (int64_t)num_kv_heads * num_seqs;
+    const int64_t grid = pairs * row_tiles * P.num_parts;
+    if (grid > 0x7fffffff) return pa::fail(PA_ERR_INVALID, "pa_prefill: %lld workgroups (limit 2^31 - 1)", (long long)grid);
+    hipLaunchKernelGGL(stream_kv ? pick<true>(block_size) : pick<false>(block_size), dim3((unsigned)grid),
                        dim3(kThreads), 0, st, static_cast<_Float16*>(out), static_cast<const _Float16*>(q), num_tokens,
                        static_cast<const _Float16*>(k_cache), static_cast<const _Float16*>(v_cache), block_tables,
                        max_blocks_per_seq, context_lens, query_start, num_heads, num_kv_heads, num_blocks, scale_log2,
-                       max_query_len, len_cap, ws_ml, ws_acc, P.tiles_per_part, P.num_parts);
+                       max_query_len, len_cap, ws_ml, ws_acc, P.tiles_per_part, P.num_parts, num_seqs,
+                       (int32_t)row_tiles, (int32_t)(pairs % 8 == 0));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "pa_prefill: %s", hipGetErrorString(e));
     if (P.num_parts > 1) {
