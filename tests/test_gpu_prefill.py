@@ -36,9 +36,12 @@ LENS = [1, 2, 15, 16, 17, 33, 64, 100, 129, 300]
 
 
 @pytest.mark.parametrize("B", [1, 4, 8, 16, 32, 128])
-@pytest.mark.parametrize("H,Hkv", [(2, 2), (8, 2), (6, 3)])
+@pytest.mark.parametrize("H,Hkv", [(2, 2), (8, 2), (6, 3), (4, 4), (8, 4)])
 @pytest.mark.parametrize("chunk", ["full", "chunked", "decode"])
 def test_prefill_matches_oracle(B, H, Hkv, chunk):
+    """10 sequences: with 2 or 3 KV heads the (KV head, sequence) pairs are
+    not a multiple of 8 and the grid takes the pair fastest; with 4 they are
+    (40) and the grid is XCD-grouped."""
     dev = device()
     case = workloads.random_case(900 + B + 10 * H + Hkv, LENS, H, Hkv, 128, B)
     kc, vc, tables, lens = _oracle_cache(case)
@@ -142,7 +145,7 @@ def test_prefill_rising_scores_move_the_running_maximum():
     assert_attention_close(out, ref, "rising scores")
 
 
-@pytest.mark.parametrize("H,Hkv", [(8, 2), (4, 4)])
+@pytest.mark.parametrize("H,Hkv", [(8, 2), (4, 4), (16, 8)])
 def test_prefill_split_context(H, Hkv):
     """Short chunks over long contexts with few sequences: the context is
     split into parts merged by a second kernel.  Against the oracle, against
