@@ -529,7 +529,9 @@ def prefill_bench(args, dev):
     clip(N(500, 150), 16, 2048) (the prompt mix of the block-size
     experiment on the 5688vip.com page), Llama-2-7B heads (32 x 128), B = 16,
     --layers layers resident (default here 4).  Each timed call is one
-    layer's pa_prefill over every prompt (the K/V already scattered).
+    layer's pa_prefill over every prompt (the K/V already scattered); then
+    the whole prompt path per layer -- K/V write and attention -- as
+    pa_reshape_and_cache + pa_prefill and as one pa_prefill_append.
     Algorithmic flops = sum over heads and new tokens of 4 * D * (causal
     positions seen); against the dense fp16 matrix-core peak."""
     import numpy as np
@@ -551,15 +553,18 @@ def prefill_bench(args, dev):
     qs = np.concatenate([[0], np.cumsum(lens_l)]).astype(np.int32)
     g = torch.Generator(device=dev)
     g.manual_seed(args.seed)
-    kcs, vcs = [], []
+    kcs, vcs, keys, vals = [], [], [], []
+    d_slots = torch.from_numpy(slots).to(dev)
     for _ in range(L):
         kc = torch.empty((NB, Hkv, B, D), dtype=torch.float16, device=dev)
         vc = torch.empty_like(kc)
         key = torch.randn((T, Hkv, D), generator=g, device=dev, dtype=torch.float16)
         val = torch.randn((T, Hkv, D), generator=g, device=dev, dtype=torch.float16)
-        pa.pa_reshape_and_cache(key, val, torch.from_numpy(slots).to(dev), kc, vc)
+        pa.pa_reshape_and_cache(key, val, d_slots, kc, vc)
         kcs.append(kc)
         vcs.append(vc)
+        keys.append(key)
+        vals.append(val)
     q = torch.randn((T, H, D), generator=g, device=dev, dtype=torch.float16)
     out = torch.empty_like(q)
     d_t, d_l, d_q = (torch.from_numpy(x).to(dev) for x in (tables, lens, qs))
@@ -586,9 +591,39 @@ def prefill_bench(args, dev):
     log(f"[bench] prefill: {S} prompts, {T} tokens (max {mq}), {L} layers; {us:.1f} us per layer = "
         f"{tflops:.1f} TFLOP/s ({100 * tflops / MFMA_F16_PEAK_TFLOPS:.1f}% of dense fp16 MFMA peak), "
         f"{T / us * 1e6:.0f} prompt tokens/s per layer")
+
+    # ---- the whole prompt path per layer: writing the prompts' K/V and the
+    # attention, as two calls (pa_reshape_and_cache, pa_prefill) or one
+    # (pa_prefill_append), in interleaved rounds of passes over the layers
+    def two_calls(l):
+        pa.pa_reshape_and_cache(keys[l], vals[l], d_slots, kcs[l], vcs[l])
+        call(l)
+
+    def fused(l):
+        pa.pa_prefill_append(out, q, keys[l], vals[l], kcs[l], vcs[l], d_t, d_l, d_q, 1 / np.sqrt(D),
+                             max_query_len=mq)
+
+    path_us = {"two_calls": [], "fused": []}
+    for _ in range(max(args.steps // 2, 2)):
+        for name, fn in (("two_calls", two_calls), ("fused", fused)):
+            for l in range(L):
+                fn(l)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for l in range(L):
+                fn(l)
+            b.record()
+            torch.cuda.synchronize()
+            path_us[name].append(a.elapsed_time(b) * 1e3 / L)
+    two_us = float(np.median(path_us["two_calls"]))
+    fused_us = float(np.median(path_us["fused"]))
+    log(f"[bench] prompt path per layer (K/V write + attention): pa_reshape_and_cache + pa_prefill {two_us:.1f} us, "
+        f"pa_prefill_append {fused_us:.1f} us ({T / fused_us * 1e6:.0f} prompt tokens/s per layer)")
     print(json.dumps({"metric": "paged prefill TFLOP/s", "value": round(tflops, 2), "unit": "TFLOP/s",
                       "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
                       "us_per_layer": round(us, 2), "tokens_per_s_per_layer": round(T / us * 1e6, 1),
+                      "prompt_path_us_per_layer": {"reshape_and_cache+prefill": round(two_us, 2),
+                                                   "prefill_append": round(fused_us, 2)},
                       "dtype": "f16",
                       "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                                    "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),

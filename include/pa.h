@@ -244,6 +244,39 @@ int pa_prefill(void *out, const void *q, int32_t num_tokens,
                float scale, int32_t max_query_len, void *workspace,
                size_t workspace_bytes, int32_t dtype, void *stream);
 
+/* ------------------------------------------------------------------------
+ * pa_reshape_and_cache of the new tokens followed by pa_prefill, in one
+ * call (the prompt path of a request, [lpnh-1824136] 3.2 second step: the
+ * prompt's K/V are stored into the blocks while its attention runs).
+ *
+ *   key, value     device, fp16; new token row i (the row of q holding it)
+ *                  and KV head h at element i * kv_token_stride + h *
+ *                  head_dim (head_dim contiguous); 16-byte aligned
+ *   kv_token_stride elements between consecutive token rows, a multiple of
+ *                  8 and >= num_kv_heads * head_dim
+ *   k_cache, v_cache  as for pa_prefill, and written: new token i of
+ *                  sequence s (position p = n_s - m_s + i) goes to block
+ *                  block_tables[s][p / block_size], row p % block_size, bit
+ *                  for bit.  A table entry outside [0, num_blocks) writes
+ *                  nothing and the token takes no part in any softmax.
+ * Every other argument, the output and the error behaviour are those of
+ * pa_prefill.  The cache is read for positions < n_s - m_s only; the new
+ * tokens' K/V come from key / value, so the result does not depend on their
+ * slots' contents before the call.  A sequence that pa_prefill skips or
+ * answers with NaN writes nothing.  The blocks written must not be shared
+ * with another sequence of the call (the block manager gives a sequence
+ * its own blocks for new tokens).
+ * ------------------------------------------------------------------------ */
+int pa_prefill_append(void *out, const void *q, int32_t num_tokens,
+                      const void *key, const void *value,
+                      int64_t kv_token_stride, void *k_cache, void *v_cache,
+                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *context_lens, const int32_t *query_start,
+                      int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                      float scale, int32_t max_query_len, void *workspace,
+                      size_t workspace_bytes, int32_t dtype, void *stream);
+
 /* Bytes of workspace pa_prefill uses for these sizes: 0 when the batch
  * fills the GPU without splitting the context, else (2 + head_dim) x 4 bytes
  * per (token, head, context part), in two 256-byte aligned regions.  The

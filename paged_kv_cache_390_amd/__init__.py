@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         "pa_prefill": ([P, P, i32, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, f32, i32, P, sz, i32, P],
                        ctypes.c_int),
         "pa_decode_order": ([P, P, i32, i32, P], ctypes.c_int),
+        "pa_prefill_append": ([P, P, i32, P, P, i64, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, f32, i32, P, sz,
+                               i32, P], ctypes.c_int),
         "pa_prefill_workspace_size": ([i32, i32, i32, i32, i32, i32, i32, i32], sz),
         "pa_decode_workspace_size": ([i32, i32, i32, i32, i32, i32, i32], sz),
         "pa_decode_default_partition": ([i32, i32, i32, i32, i32, i32], i32),
@@ -305,14 +307,8 @@ def pa_prefill_workspace_size(num_tokens: int, num_seqs: int, num_heads: int, nu
     return n
 
 
-def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float,
-               max_query_len: Optional[int] = None, workspace=None, split: bool = True) -> None:
-    """Causal attention of the packed new tokens q[T, H, D] over the paged
-    cache: sequence s's rows query_start[s] .. query_start[s+1]-1 are its
-    last m tokens (K/V already cached), row i at position context_lens[s] -
-    m + i.  max_query_len defaults to T.  workspace (uint8 device tensor)
-    is allocated when the batch is small enough for the context to be split
-    and none is given; split=False passes none (no split)."""
+def _prefill_args(out, q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len, workspace,
+                  split):
     torch = _torch()
     _dev_tensor(k_cache, "k_cache", torch.float16, 4)
     _dev_tensor(v_cache, "v_cache", torch.float16, 4)
@@ -340,10 +336,46 @@ def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start
                 workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
             _dev_tensor(workspace, "workspace", torch.uint8, 1)
             ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    return T, S, H, Hkv, D, B, NB, int(max_query_len), ws_ptr, ws_bytes
+
+
+def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float,
+               max_query_len: Optional[int] = None, workspace=None, split: bool = True) -> None:
+    """Causal attention of the packed new tokens q[T, H, D] over the paged
+    cache: sequence s's rows query_start[s] .. query_start[s+1]-1 are its
+    last m tokens (K/V already cached), row i at position context_lens[s] -
+    m + i.  max_query_len defaults to T.  workspace (uint8 device tensor)
+    is allocated when the batch is small enough for the context to be split
+    and none is given; split=False passes none (no split)."""
+    T, S, H, Hkv, D, B, NB, mq, ws_ptr, ws_bytes = _prefill_args(
+        out, q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len, workspace, split)
     _check(lib().pa_prefill(out.data_ptr(), q.data_ptr(), T, k_cache.data_ptr(), v_cache.data_ptr(),
                             block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
-                            query_start.data_ptr(), S, H, Hkv, D, B, NB, float(scale), int(max_query_len),
+                            query_start.data_ptr(), S, H, Hkv, D, B, NB, float(scale), mq,
                             ws_ptr, ws_bytes, PA_DTYPE_F16, _stream(q.device)), "pa_prefill")
+
+
+def pa_prefill_append(out, q, key, value, k_cache, v_cache, block_tables, context_lens, query_start, scale: float,
+                      max_query_len: Optional[int] = None, workspace=None, split: bool = True) -> None:
+    """pa_reshape_and_cache of the new tokens followed by pa_prefill, in one
+    call: key/value [T, Hkv, D] (fp16, head_dim contiguous, any 16-byte
+    aligned token stride) hold the K/V of the token in the same row of q; each
+    is written into the cache at its position's slot of block_tables and
+    attended to with the cached ones."""
+    torch = _torch()
+    T, S, H, Hkv, D, B, NB, mq, ws_ptr, ws_bytes = _prefill_args(
+        out, q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len, workspace, split)
+    _dev_tensor(key, "key", torch.float16, 3, contiguous=False)
+    _dev_tensor(value, "value", torch.float16, 3, contiguous=False)
+    if tuple(key.shape) != (T, Hkv, D) or tuple(value.shape) != (T, Hkv, D):
+        raise ValueError(f"key/value must be [{T}, {Hkv}, {D}]")
+    if key.stride() != value.stride() or key.stride(2) != 1 or key.stride(1) != D:
+        raise ValueError("key and value need equal strides with contiguous [Hkv, D] rows")
+    _check(lib().pa_prefill_append(out.data_ptr(), q.data_ptr(), T, key.data_ptr(), value.data_ptr(), key.stride(0),
+                                   k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+                                   block_tables.shape[1], context_lens.data_ptr(), query_start.data_ptr(), S, H, Hkv,
+                                   D, B, NB, float(scale), mq, ws_ptr, ws_bytes, PA_DTYPE_F16, _stream(q.device)),
+           "pa_prefill_append")
 
 
 def pa_copy_blocks(k_caches: Sequence, v_caches: Sequence, src_dst_pairs) -> None:

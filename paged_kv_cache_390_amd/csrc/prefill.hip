@@ -94,6 +94,19 @@ static_assert(kStageRows >= 1 && kKvTile * 16 == kStageRows * kThreads, "tile ro
 
 struct Staged {
     bool ok[kStageRows];
+    int32_t wphys[kStageRows];   // append mode: the block this thread writes the row into, or -1
+};
+
+// Append mode: the m new tokens of the sequence (positions base_pos ..
+// n - 1) are read from the step's key / value tensors, not from the cache,
+// and the workgroup holding a token's first query row writes it into the
+// cache.  `k` / `v` point at the sequence's first new token, KV head kvh.
+struct AppendSrc {
+    const _Float16* k;
+    const _Float16* v;
+    int64_t stride;      // elements between consecutive tokens
+    int base_pos;        // position of the first new token
+    int w_lo, w_hi;      // positions this workgroup writes: [w_lo, w_hi)
 };
 
 // s_waitcnt immediates (GFX9 encoding: vmcnt bits 3:0 and 15:14, expcnt
@@ -125,11 +138,11 @@ __device__ __forceinline__ void table_entries(int32_t (&e)[kStageRows], int k, i
 // thread looks up its own row.  Rows past the context or with an id outside
 // the pool read a row of some valid block (a fixed number of loads per
 // tile) and are zeroed by finish_tile.
-template <int B, bool kStream>
+template <int B, bool kStream, bool kAppend>
 __device__ __forceinline__ void fetch_tile(Staged& st, unsigned char* buf, int k, const int32_t (&e)[kStageRows], int wave, int lane,
                                            int n, const int32_t* __restrict__ trow,
                                            const _Float16* __restrict__ kbase, const _Float16* __restrict__ vbase,
-                                           int64_t blk_stride, int32_t num_blocks) {
+                                           int64_t blk_stride, int32_t num_blocks, const AppendSrc& ap) {
     // kStream: every K/V byte is read by one workgroup only (all query rows
     // of a sequence fit one row tile), so the loads are nontemporal (the nt
     // bit of the cache policy); otherwise later row tiles of the sequence
@@ -162,10 +175,21 @@ __device__ __forceinline__ void fetch_tile(Staged& st, unsigned char* buf, int k
         const int cv = col ^ (2 * (r & 3));
         unsigned char* kdst = buf + stage_token0(0, wave, i) * kPitch;
         unsigned char* vdst = buf + kTileBytes + stage_token0(0, wave, i) * kPitchV;
-        __builtin_amdgcn_global_load_lds((const void*)(kbase + off + ck * 8),
-                                         (__attribute__((address_space(3))) void*)kdst, 16, 0, kLoadPolicy);
-        __builtin_amdgcn_global_load_lds((const void*)(vbase + off + cv * 8),
-                                         (__attribute__((address_space(3))) void*)vdst, 16, 0, kLoadPolicy);
+        const _Float16* ksrc = kbase + off + ck * 8;
+        const _Float16* vsrc = vbase + off + cv * 8;
+        if constexpr (kAppend) {
+            const bool fresh = t >= ap.base_pos && t < n;   // a new token: from key / value
+            if (fresh) {
+                const int64_t tok = (int64_t)(t - ap.base_pos) * ap.stride;
+                ksrc = ap.k + tok + ck * 8;
+                vsrc = ap.v + tok + cv * 8;
+            }
+            st.wphys[i] = fresh && in_pool && t >= ap.w_lo && t < ap.w_hi ? phys : -1;
+        }
+        __builtin_amdgcn_global_load_lds((const void*)ksrc, (__attribute__((address_space(3))) void*)kdst, 16, 0,
+                                         kLoadPolicy);
+        __builtin_amdgcn_global_load_lds((const void*)vsrc, (__attribute__((address_space(3))) void*)vdst, 16, 0,
+                                         kLoadPolicy);
         st.ok[i] = ok;
     }
 }
@@ -192,6 +216,28 @@ __device__ __forceinline__ void finish_tile(const Staged& st, unsigned char* buf
 #pragma unroll
     for (int i = 0; i < kStageRows; ++i)
         if (col == 0) flags[stage_token0(0, wave, i) + (lane >> 4)] = st.ok[i];
+}
+
+// Append mode, while tile k is in LDS: the rows this thread loaded that are
+// new tokens owned by the workgroup go from LDS into the cache, 16 bytes of
+// K and of V each (LDS position col of row r holds chunk col ^ (r & 15) of
+// K and col ^ 2(r & 3) of V).  No workgroup reads these rows from the cache.
+template <int B>
+__device__ __forceinline__ void write_own_rows(const Staged& st, const unsigned char* buf, int k, int wave, int lane,
+                                               _Float16* __restrict__ kw, _Float16* __restrict__ vw,
+                                               int64_t blk_stride) {
+    const int col = lane & 15;
+#pragma unroll
+    for (int i = 0; i < kStageRows; ++i) {
+        if (st.wphys[i] < 0) continue;
+        const int r = stage_token0(0, wave, i) + (lane >> 4);
+        const int t = k * kKvTile + r;
+        const int64_t dst = (int64_t)st.wphys[i] * blk_stride + (int64_t)(t % B) * kD;
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(buf + r * kPitch + col * 16);
+        const u32x4 vv = *reinterpret_cast<const u32x4*>(buf + kTileBytes + r * kPitchV + col * 16);
+        *reinterpret_cast<u32x4*>(kw + dst + (col ^ (r & 15)) * 8) = kv;
+        *reinterpret_cast<u32x4*>(vw + dst + (col ^ (2 * (r & 3))) * 8) = vv;
+    }
 }
 
 // Runtime flags of one of the wave's 16-row groups, for this lane's row.
@@ -381,7 +427,7 @@ __device__ __forceinline__ void consume_lds_tile(Softmax (&st)[kNT], const unsig
 #undef PF_TR16
 }
 
-template <int B, bool kStream>
+template <int B, bool kStream, bool kAppend>
 __global__ void __launch_bounds__(kThreads)
 prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, int32_t num_tokens,
                     const _Float16* __restrict__ k_cache, const _Float16* __restrict__ v_cache,
@@ -389,7 +435,9 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
                     const int32_t* __restrict__ query_start, int32_t num_heads, int32_t num_kv_heads,
                     int32_t num_blocks, float scale_log2, int32_t max_query_len, int64_t len_cap,
                     float* __restrict__ ws_ml, float* __restrict__ ws_acc, int32_t tiles_per_part,
-                    int32_t num_parts, int32_t num_seqs, int32_t row_tiles, int32_t xcd_grouped) {
+                    int32_t num_parts, int32_t num_seqs, int32_t row_tiles, int32_t xcd_grouped,
+                    const _Float16* __restrict__ new_k, const _Float16* __restrict__ new_v, int64_t new_stride,
+                    _Float16* __restrict__ k_write, _Float16* __restrict__ v_write) {
     // two stage buffers as distinct objects, so that the compiler can tell
     // the buffer a step reads from the one whose loads are in flight
     __shared__ __attribute__((aligned(16))) unsigned char ldsA[kBufBytes];
@@ -516,18 +564,36 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
     // every prompt workload (8192-token prompts 641 against 721 TFLOP/s)
     // and faster only on short chunks over long caches (4 x 8192 cached +
     // 32 new: 106 against 110 us).
+    AppendSrc ap{};
+    _Float16* kw = nullptr;
+    _Float16* vw = nullptr;
+    if constexpr (kAppend) {
+        // the sequence's new tokens (rows q0 .. of key / value); this
+        // workgroup writes those whose first query row r = i * g is one of
+        // its rows [grow0, grow0 + kRowsPerGroup)
+        ap.k = new_k + (int64_t)q0 * new_stride + (int64_t)kvh * kD;
+        ap.v = new_v + (int64_t)q0 * new_stride + (int64_t)kvh * kD;
+        ap.stride = new_stride;
+        ap.base_pos = base_pos;
+        ap.w_lo = base_pos + (grow0 + g - 1) / g;
+        ap.w_hi = base_pos + (grow0 + kRowsPerGroup + g - 1) / g;
+        kw = k_write + (int64_t)kvh * slab;
+        vw = v_write + (int64_t)kvh * slab;
+    }
     Staged SA, SB;
     int32_t e[kStageRows] = {};
     const int kb = k_begin;
     if constexpr (B >= 4) table_entries<B>(e, kb, wave, n, trow);
-    fetch_tile<B, kStream>(SA, ldsA, kb, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
+    fetch_tile<B, kStream, kAppend>(SA, ldsA, kb, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks, ap);
     if constexpr (B >= 4) table_entries<B>(e, kb + 1, wave, n, trow);
     PA_WAIT_VM(0);
     finish_tile(SA, ldsA, flA, wave, lane);
     PA_WAIT_LGKM0();
     __builtin_amdgcn_s_barrier();
-    auto step = [&](int k, unsigned char* cb, unsigned char* cf, unsigned char* nb, unsigned char* nf, Staged& ns) {
-        fetch_tile<B, kStream>(ns, nb, k + 1, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks);
+    auto step = [&](int k, unsigned char* cb, unsigned char* cf, const Staged& cs, unsigned char* nb,
+                    unsigned char* nf, Staged& ns) {
+        fetch_tile<B, kStream, kAppend>(ns, nb, k + 1, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks,
+                                        ap);
         if constexpr (B >= 4) table_entries<B>(e, k + 2, wave, n, trow);
         if (k < my_end) {
             // uniform: tile below the wave's first row and wholly valid
@@ -542,14 +608,19 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
             consume_lds_tile(st, cb, cf, k * kKvTile, interior, qb, c_log2, lane, rw);
         }
         PA_WAIT_VM(0);
+        // append mode: the new tokens of tile k this workgroup owns go to the
+        // cache now, after the wait, so that the stores complete under the
+        // next step's products instead of stalling this step's wait; the LDS
+        // reads finish before the barrier, ahead of the next fetch into `cb`
+        if constexpr (kAppend) write_own_rows<B>(cs, cb, k, wave, lane, kw, vw, blk_stride);
         finish_tile(ns, nb, nf, wave, lane);
         PA_WAIT_LGKM0();
         __builtin_amdgcn_s_barrier();
     };
     for (int k = kb;;) {
-        step(k, ldsA, flA, ldsB, flB, SB);
+        step(k, ldsA, flA, SA, ldsB, flB, SB);
         if (++k >= k_end) break;
-        step(k, ldsB, flB, ldsA, flA, SA);
+        step(k, ldsB, flB, SB, ldsA, flA, SA);
         if (++k >= k_end) break;
     }
     PA_WAIT_VM(0);                          // no load into LDS outstanding at exit
@@ -644,19 +715,20 @@ prefill_merge_kernel(_Float16* __restrict__ out, const float* __restrict__ ws_ml
 
 using PrefillFn = void (*)(_Float16*, const _Float16*, int32_t, const _Float16*, const _Float16*, const int32_t*,
                            int32_t, const int32_t*, const int32_t*, int32_t, int32_t, int32_t, float, int32_t,
-                           int64_t, float*, float*, int32_t, int32_t, int32_t, int32_t, int32_t);
+                           int64_t, float*, float*, int32_t, int32_t, int32_t, int32_t, int32_t, const _Float16*,
+                           const _Float16*, int64_t, _Float16*, _Float16*);
 
-template <bool kStream>
+template <bool kStream, bool kAppend>
 PrefillFn pick(int32_t b) {
     switch (b) {
-        case 1: return prefill_mfma_kernel<1, kStream>;
-        case 2: return prefill_mfma_kernel<2, kStream>;
-        case 4: return prefill_mfma_kernel<4, kStream>;
-        case 8: return prefill_mfma_kernel<8, kStream>;
-        case 16: return prefill_mfma_kernel<16, kStream>;
-        case 32: return prefill_mfma_kernel<32, kStream>;
-        case 64: return prefill_mfma_kernel<64, kStream>;
-        case 128: return prefill_mfma_kernel<128, kStream>;
+        case 1: return prefill_mfma_kernel<1, kStream, kAppend>;
+        case 2: return prefill_mfma_kernel<2, kStream, kAppend>;
+        case 4: return prefill_mfma_kernel<4, kStream, kAppend>;
+        case 8: return prefill_mfma_kernel<8, kStream, kAppend>;
+        case 16: return prefill_mfma_kernel<16, kStream, kAppend>;
+        case 32: return prefill_mfma_kernel<32, kStream, kAppend>;
+        case 64: return prefill_mfma_kernel<64, kStream, kAppend>;
+        case 128: return prefill_mfma_kernel<128, kStream, kAppend>;
         default: return nullptr;
     }
 }
@@ -712,7 +784,7 @@ SplitPlan split_plan(int32_t num_tokens, int32_t num_seqs, int32_t num_heads, in
 extern "C" size_t pa_prefill_workspace_size(int32_t num_tokens, int32_t num_seqs, int32_t num_heads,
                                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                             int32_t max_blocks_per_seq, int32_t max_query_len) {
-    if (head_dim != kD || !pick<false>(block_size) || num_tokens < 0 || num_seqs < 0 || num_heads <= 0 ||
+    if (head_dim != kD || !pick<false, false>(block_size) || num_tokens < 0 || num_seqs < 0 || num_heads <= 0 ||
         num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || max_blocks_per_seq < 0 || max_query_len < 0)
         return (size_t)-1;
     return split_plan(num_tokens, num_seqs, num_heads, num_kv_heads, (int64_t)max_blocks_per_seq * block_size,
@@ -720,34 +792,52 @@ extern "C" size_t pa_prefill_workspace_size(int32_t num_tokens, int32_t num_seqs
         .total;
 }
 
-extern "C" int pa_prefill(void* out, const void* q, int32_t num_tokens, const void* k_cache, const void* v_cache,
-                          const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
-                          const int32_t* query_start, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                          int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
-                          int32_t max_query_len, void* workspace, size_t workspace_bytes, int32_t dtype,
-                          void* stream) {
-    if (dtype != PA_DTYPE_F16) return pa::fail(PA_ERR_UNSUPPORTED, "pa_prefill: dtype %d", dtype);
-    if (head_dim != kD) return pa::fail(PA_ERR_UNSUPPORTED, "pa_prefill: head_dim %d (only %d)", head_dim, kD);
-    if (!pick<false>(block_size)) return pa::fail(PA_ERR_UNSUPPORTED, "pa_prefill: block_size %d", block_size);
+namespace {
+
+// The new tokens' K/V when pa_prefill_append folds their write into the
+// call (null otherwise).
+struct PrefillAppend {
+    const _Float16* key;
+    const _Float16* value;
+    int64_t stride;
+};
+
+int prefill_impl(const char* fn, void* out, const void* q, int32_t num_tokens, const void* k_cache,
+                 const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                 const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs, int32_t num_heads,
+                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                 int32_t max_query_len, void* workspace, size_t workspace_bytes, int32_t dtype, void* stream,
+                 const PrefillAppend* app) {
+    if (dtype != PA_DTYPE_F16) return pa::fail(PA_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
+    if (head_dim != kD) return pa::fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (only %d)", fn, head_dim, kD);
+    if (!pick<false, false>(block_size)) return pa::fail(PA_ERR_UNSUPPORTED, "%s: block_size %d", fn, block_size);
     if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
         num_blocks <= 0 || max_blocks_per_seq < 0 || max_query_len < 0)
-        return pa::fail(PA_ERR_INVALID, "pa_prefill: bad sizes (S=%d H=%d Hkv=%d NB=%d W=%d max_q=%d)", num_seqs,
+        return pa::fail(PA_ERR_INVALID, "%s: bad sizes (S=%d H=%d Hkv=%d NB=%d W=%d max_q=%d)", fn, num_seqs,
                         num_heads, num_kv_heads, num_blocks, max_blocks_per_seq, max_query_len);
     if (num_seqs > 65535 || num_kv_heads > 65535 || num_heads > 65535)
-        return pa::fail(PA_ERR_INVALID, "pa_prefill: num_seqs and the head counts must be <= 65535");
-    if (!std::isfinite(scale)) return pa::fail(PA_ERR_INVALID, "pa_prefill: scale is not finite");
+        return pa::fail(PA_ERR_INVALID, "%s: num_seqs and the head counts must be <= 65535", fn);
+    if (!std::isfinite(scale)) return pa::fail(PA_ERR_INVALID, "%s: scale is not finite", fn);
     if (num_seqs == 0 || max_query_len == 0 || num_tokens == 0) return PA_OK;
     if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
-        return pa::fail(PA_ERR_INVALID, "pa_prefill: null pointer");
+        return pa::fail(PA_ERR_INVALID, "%s: null pointer", fn);
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
-        return pa::fail(PA_ERR_INVALID, "pa_prefill: out, q and caches must be 16-byte aligned");
+        return pa::fail(PA_ERR_INVALID, "%s: out, q and caches must be 16-byte aligned", fn);
     if (workspace && !aligned16(workspace))
-        return pa::fail(PA_ERR_INVALID, "pa_prefill: workspace must be 16-byte aligned");
+        return pa::fail(PA_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
+    if (app) {
+        if (!app->key || !app->value) return pa::fail(PA_ERR_INVALID, "%s: null key or value", fn);
+        if (!aligned16(app->key) || !aligned16(app->value) || app->stride % 8 != 0)
+            return pa::fail(PA_ERR_INVALID, "%s: key, value and kv_token_stride must be 16-byte aligned", fn);
+        if (app->stride < (int64_t)num_kv_heads * head_dim)
+            return pa::fail(PA_ERR_INVALID, "%s: kv_token_stride %lld < num_kv_heads * head_dim", fn,
+                            (long long)app->stride);
+    }
     const int64_t g = num_heads / num_kv_heads;
     const int64_t row_tiles = ((int64_t)max_query_len * g + kRowsPerGroup - 1) / kRowsPerGroup;
     if (row_tiles > 65535)
-        return pa::fail(PA_ERR_INVALID, "pa_prefill: max_query_len %d x %lld heads needs %lld row tiles (limit 65535)",
-                        max_query_len, (long long)g, (long long)row_tiles);
+        return pa::fail(PA_ERR_INVALID, "%s: max_query_len %d x %lld heads needs %lld row tiles (limit 65535)",
+                        fn, max_query_len, (long long)g, (long long)row_tiles);
     const int64_t len_cap = (int64_t)max_blocks_per_seq * block_size;
     SplitPlan P = split_plan(num_tokens, num_seqs, num_heads, num_kv_heads, len_cap, max_query_len);
     if (P.num_parts > 1 && (!workspace || workspace_bytes < P.total)) {
@@ -766,15 +856,24 @@ extern "C" int pa_prefill(void* out, const void* q, int32_t num_tokens, const vo
     const bool stream_kv = row_tiles == 1;
     const int64_t pairs = (int64_t)num_kv_heads * num_seqs;
     const int64_t grid = pairs * row_tiles * P.num_parts;
-    if (grid > 0x7fffffff) return pa::fail(PA_ERR_INVALID, "pa_prefill: %lld workgroups (limit 2^31 - 1)", (long long)grid);
-    hipLaunchKernelGGL(stream_kv ? pick<true>(block_size) : pick<false>(block_size), dim3((unsigned)grid),
+    if (grid > 0x7fffffff) return pa::fail(PA_ERR_INVALID, "%s: %lld workgroups (limit 2^31 - 1)", fn,
+                                              (long long)grid);
+    const PrefillFn fn_main = app ? (stream_kv ? pick<true, true>(block_size) : pick<false, true>(block_size))
+                                  : (stream_kv ? pick<true, false>(block_size) : pick<false, false>(block_size));
+    // the cache pointers double as write pointers in append mode: the kernel
+    // writes only the new tokens' rows, which no workgroup reads from the
+    // cache
+    hipLaunchKernelGGL(fn_main, dim3((unsigned)grid),
                        dim3(kThreads), 0, st, static_cast<_Float16*>(out), static_cast<const _Float16*>(q), num_tokens,
                        static_cast<const _Float16*>(k_cache), static_cast<const _Float16*>(v_cache), block_tables,
                        max_blocks_per_seq, context_lens, query_start, num_heads, num_kv_heads, num_blocks, scale_log2,
                        max_query_len, len_cap, ws_ml, ws_acc, P.tiles_per_part, P.num_parts, num_seqs,
-                       (int32_t)row_tiles, (int32_t)(pairs % 8 == 0));
+                       (int32_t)row_tiles, (int32_t)(pairs % 8 == 0), app ? app->key : nullptr,
+                       app ? app->value : nullptr, app ? app->stride : (int64_t)0,
+                       app ? static_cast<_Float16*>(const_cast<void*>(k_cache)) : nullptr,
+                       app ? static_cast<_Float16*>(const_cast<void*>(v_cache)) : nullptr);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "pa_prefill: %s", hipGetErrorString(e));
+    if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
     if (P.num_parts > 1) {
         hipLaunchKernelGGL(prefill_merge_kernel,
                            dim3((unsigned)num_heads, (unsigned)num_seqs,
@@ -783,7 +882,32 @@ extern "C" int pa_prefill(void* out, const void* q, int32_t num_tokens, const vo
                            num_tokens, context_lens, query_start, num_heads, num_kv_heads, max_query_len, len_cap,
                            P.tiles_per_part, P.num_parts);
         e = hipGetLastError();
-        if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "pa_prefill: %s", hipGetErrorString(e));
+        if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
     }
     return PA_OK;
+}
+
+}  // namespace
+
+extern "C" int pa_prefill(void* out, const void* q, int32_t num_tokens, const void* k_cache, const void* v_cache,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                          const int32_t* query_start, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                          int32_t max_query_len, void* workspace, size_t workspace_bytes, int32_t dtype,
+                          void* stream) {
+    return prefill_impl("pa_prefill", out, q, num_tokens, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                        context_lens, query_start, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                        scale, max_query_len, workspace, workspace_bytes, dtype, stream, nullptr);
+}
+
+extern "C" int pa_prefill_append(void* out, const void* q, int32_t num_tokens, const void* key, const void* value,
+                                 int64_t kv_token_stride, void* k_cache, void* v_cache, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* query_start,
+                                 int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks, float scale, int32_t max_query_len,
+                                 void* workspace, size_t workspace_bytes, int32_t dtype, void* stream) {
+    const PrefillAppend app{static_cast<const _Float16*>(key), static_cast<const _Float16*>(value), kv_token_stride};
+    return prefill_impl("pa_prefill_append", out, q, num_tokens, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                        context_lens, query_start, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                        scale, max_query_len, workspace, workspace_bytes, dtype, stream, &app);
 }

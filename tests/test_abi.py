@@ -199,6 +199,34 @@ def test_prefill_with_nothing_to_do_is_a_no_op():
     assert L.pa_prefill(*_prefill_args(T=0, out=None)) == pa.PA_OK
 
 
+def _prefill_append_args(key=16, value=16, stride=256, **kw):
+    a = _prefill_args(**kw)
+    # pa_prefill_append: out, q, T, key, value, kv_token_stride, k_cache, v_cache, then as pa_prefill
+    return a[:3] + (key, value, stride) + a[3:]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=1), pa.PA_ERR_UNSUPPORTED),
+    (dict(D=64), pa.PA_ERR_UNSUPPORTED),
+    (dict(B=12), pa.PA_ERR_UNSUPPORTED),
+    (dict(H=3, Hkv=2), pa.PA_ERR_INVALID),
+    (dict(qs=None), pa.PA_ERR_INVALID),
+    (dict(key=None), pa.PA_ERR_INVALID),
+    (dict(value=8), pa.PA_ERR_INVALID),             # misaligned
+    (dict(stride=260), pa.PA_ERR_INVALID),          # not a multiple of 8 elements
+    (dict(stride=128), pa.PA_ERR_INVALID),          # below num_kv_heads * head_dim
+])
+def test_prefill_append_rejects_bad_arguments_before_launch(kw, code):
+    assert pa.lib().pa_prefill_append(*_prefill_append_args(**kw)) == code
+    assert pa.last_error()
+
+
+def test_prefill_append_with_nothing_to_do_is_a_no_op():
+    L = pa.lib()
+    assert L.pa_prefill_append(*_prefill_append_args(S=0, out=None)) == pa.PA_OK
+    assert L.pa_prefill_append(*_prefill_append_args(T=0, out=None, key=None)) == pa.PA_OK
+
+
 def test_prefill_workspace_size():
     """Zero when the batch fills the GPU unsplit; otherwise (2 + D) x 4 bytes
     per (token, head, context part), two 256-byte aligned regions."""

@@ -12,6 +12,7 @@ import oracle
 import paged_kv_cache_390_amd as pa
 import workloads
 from gpu_common import assert_attention_close, bits, device, say
+from oracle.block_manager import BlockManagerModel
 from test_gpu_decode import _oracle_cache
 
 pytestmark = pytest.mark.gpu
@@ -243,3 +244,127 @@ def test_prompt_prefill_at_the_llama_shape():
     say(f"llama prompts: {lens_l}, T={T}")
     ref = oracle.prefill(q.cpu().numpy(), kc.cpu().numpy(), vc.cpu().numpy(), tables, lens, qs, 1 / np.sqrt(D))
     assert_attention_close(out, ref, "llama prompts")
+
+
+def _append_case(case, ms):
+    """The cache before a pa_prefill_append call (positions < n - m written by
+    the oracle's scatter, NaN everywhere else, the new tokens' slots
+    included), the cache the oracle's scatter of every position gives, and
+    the new tokens' K/V packed in query order [T, Hkv, D]."""
+    m_model = BlockManagerModel(case.num_blocks, case.block_size)
+    for s, (n, t) in enumerate(zip(case.lens, case.tables)):
+        m_model.set_table(s, t, n)
+    starts = np.concatenate([[0], np.cumsum(case.lens)]).astype(np.int64)
+    old = [(s, p) for s, n in enumerate(case.lens) for p in range(n - ms[s])]
+    new = [(s, p) for s, n in enumerate(case.lens) for p in range(n - ms[s], n)]
+    kc0, vc0, tables, lens = _oracle_cache(case)
+    kc0[...] = np.float16(np.nan)
+    vc0[...] = np.float16(np.nan)
+    kc1, vc1 = kc0.copy(), vc0.copy()
+    rows_old = np.array([starts[s] + p for s, p in old], np.int64)
+    rows_new = np.array([starts[s] + p for s, p in new], np.int64)
+    if len(old):
+        oracle.reshape_and_cache(np.ascontiguousarray(case.k_tokens[rows_old]),
+                                 np.ascontiguousarray(case.v_tokens[rows_old]),
+                                 np.array([m_model.slot(s, p) for s, p in old], np.int64), kc0, vc0)
+    kc1[...], vc1[...] = kc0, vc0
+    key = np.ascontiguousarray(case.k_tokens[rows_new])
+    value = np.ascontiguousarray(case.v_tokens[rows_new])
+    if len(new):
+        oracle.reshape_and_cache(key, value, np.array([m_model.slot(s, p) for s, p in new], np.int64), kc1, vc1)
+    return kc0, vc0, kc1, vc1, key, value, tables, lens
+
+
+def _gpu_prefill_append(dev, q, key, value, kc0, vc0, tables, lens, qs, scale, pad=0, split=True):
+    T, Hkv, D = key.shape
+    if pad:
+        # key and value as views into wider rows (a fused QKV-like buffer)
+        wide = torch.zeros((T, 2, Hkv * D + pad), dtype=torch.float16, device=dev)
+        wide[:, 0, :Hkv * D] = torch.from_numpy(key).to(dev).reshape(T, Hkv * D)
+        wide[:, 1, :Hkv * D] = torch.from_numpy(value).to(dev).reshape(T, Hkv * D)
+        k_t = wide[:, 0].narrow(1, 0, Hkv * D).unflatten(1, (Hkv, D))
+        v_t = wide[:, 1].narrow(1, 0, Hkv * D).unflatten(1, (Hkv, D))
+    else:
+        k_t, v_t = torch.from_numpy(key).to(dev), torch.from_numpy(value).to(dev)
+    kc, vc = torch.from_numpy(kc0).to(dev), torch.from_numpy(vc0).to(dev)
+    out = torch.full(q.shape, float("nan"), dtype=torch.float16, device=dev)
+    pa.pa_prefill_append(out, torch.from_numpy(q).to(dev), k_t, v_t, kc, vc, torch.from_numpy(tables).to(dev),
+                         torch.from_numpy(lens).to(dev), torch.from_numpy(qs).to(dev), scale, split=split)
+    torch.cuda.synchronize()
+    return out, kc, vc
+
+
+@pytest.mark.parametrize("B", [1, 4, 16, 128])
+@pytest.mark.parametrize("H,Hkv", [(2, 2), (6, 3), (4, 4), (8, 4)])
+@pytest.mark.parametrize("chunk", ["full", "chunked", "decode"])
+def test_prefill_append_matches_oracle(B, H, Hkv, chunk):
+    """pa_prefill_append against the oracle's scatter of the new tokens
+    followed by its prefill: the caches bit for bit (every new token written
+    once, by the workgroup holding its first query row -- with 3 query heads
+    per KV head a token's rows can straddle two row tiles), the output within
+    tolerance.  The new tokens' slots hold NaN before the call, so any read of
+    them from the cache would show."""
+    dev = device()
+    case = workloads.random_case(700 + B + 10 * H + Hkv, LENS, H, Hkv, 128, B)
+    if chunk == "full":
+        ms = list(LENS)
+    elif chunk == "chunked":
+        ms = [max(1, n // 3) for n in LENS]
+    else:
+        ms = [1] * len(LENS)
+    kc0, vc0, kc1, vc1, key, value, tables, lens = _append_case(case, ms)
+    q, qs = _queries(B + H + 5, ms, H, 128)
+    say(f"prefill_append B={B} H={H}/{Hkv} {chunk}: rows {int(qs[-1])}")
+    out, kc, vc = _gpu_prefill_append(dev, q, key, value, kc0, vc0, tables, lens, qs, case.scale,
+                                      pad=24 if B == 16 else 0)
+    assert np.array_equal(bits(kc), kc1.view(np.uint16)), "K cache differs from the oracle's scatter"
+    assert np.array_equal(bits(vc), vc1.view(np.uint16)), "V cache differs from the oracle's scatter"
+    ref = oracle.prefill(q, kc1, vc1, tables, lens, qs, case.scale)
+    assert_attention_close(out, ref, f"prefill_append B={B} H={H}/{Hkv} {chunk}")
+    # the same rows through the two-call path on the written cache
+    two = _gpu_prefill(dev, q, kc1, vc1, tables, lens, qs, case.scale)
+    assert_attention_close(two, ref, "two calls")
+
+
+@pytest.mark.parametrize("H,Hkv", [(8, 2), (16, 8)])
+def test_prefill_append_split_context(H, Hkv):
+    """Short chunks over long contexts, context split into parts: each new
+    token is written by the part whose tiles hold it; with and without a
+    workspace."""
+    dev = device()
+    lens_l = [3000, 2500, 1777]
+    ms = [8, 40, 1]
+    case = workloads.random_case(191 + H, lens_l, H, Hkv, 128, 16)
+    kc0, vc0, kc1, vc1, key, value, tables, lens = _append_case(case, ms)
+    q, qs = _queries(191, ms, H, 128)
+    ref = oracle.prefill(q, kc1, vc1, tables, lens, qs, case.scale)
+    for split in (True, False):
+        out, kc, vc = _gpu_prefill_append(dev, q, key, value, kc0, vc0, tables, lens, qs, case.scale, split=split)
+        assert np.array_equal(bits(kc), kc1.view(np.uint16)) and np.array_equal(bits(vc), vc1.view(np.uint16))
+        assert_attention_close(out, ref, f"append split={split} H={H}/{Hkv}")
+
+
+def test_prefill_append_skips_ids_outside_the_pool():
+    """A new token whose table entry lies outside the pool is neither written
+    nor attended to (as for a cached token behind such an entry); the other
+    tokens are written and the rest of the batch is unaffected."""
+    dev = device()
+    case = workloads.random_case(77, [40, 33], 4, 2, 128, 16)
+    ms = [40, 20]
+    kc0, vc0, kc1, vc1, key, value, tables, lens = _append_case(case, ms)
+    bad = tables.copy()
+    bad[1, 2] = case.num_blocks + 5                          # block of position 32, sequence 1's last new token
+    q, qs = _queries(77, ms, 4, 128)
+    out, kc, vc = _gpu_prefill_append(dev, q, key, value, kc0, vc0, bad, lens, qs, case.scale)
+    # expected cache: the oracle's, with the block of the bad entry left as before the call
+    blk = tables[1, 2]
+    kc_exp, vc_exp = kc1.copy(), vc1.copy()
+    kc_exp[blk], vc_exp[blk] = kc0[blk], vc0[blk]
+    assert np.array_equal(bits(kc), kc_exp.view(np.uint16)) and np.array_equal(bits(vc), vc_exp.view(np.uint16))
+    # sequence 0 is untouched by the bad entry; sequence 1's rows match pa_prefill over the written cache with the
+    # same bad table (the pool-id mask is the same in both calls)
+    ref0 = oracle.prefill(np.ascontiguousarray(q[:40]), kc1, vc1, np.ascontiguousarray(tables[:1]),
+                          np.ascontiguousarray(lens[:1]), np.array([0, 40], np.int32), case.scale)
+    assert_attention_close(out[:40], ref0, "sequence 0")
+    two = _gpu_prefill(dev, q, kc_exp, vc_exp, bad, lens, qs, case.scale)
+    assert_attention_close(out[40:], two[40:].float().cpu().numpy(), "sequence 1 against pa_prefill")
