@@ -1,5 +1,6 @@
-"""A decode step captured in a HIP graph (torch.cuda.graph over the C ABI's
-calls on the capture stream) replays the same results as eager launches:
+"""A decode step (and a prefill with its K/V write) captured in a HIP graph
+(torch.cuda.graph over the C ABI's calls on the capture stream) replays the
+same results as eager launches:
 the calls allocate nothing, synchronise with nothing and record no memset.
 
 Each replay starts from the cache as it was before the step (history only,
@@ -102,3 +103,66 @@ def test_decode_step_replays_in_a_hip_graph(H, Hkv, P):
             assert np.array_equal(bits(outs[l]), eager_out[l]), f"replay {rep} layer {l}: output differs"
             assert np.array_equal(bits(kcs[l]), kc_full.view(np.uint16)), f"replay {rep} layer {l}: K cache"
             assert np.array_equal(bits(vcs[l]), vc_full.view(np.uint16)), f"replay {rep} layer {l}: V cache"
+
+
+@pytest.mark.parametrize("split", [False, True])
+def test_prefill_append_replays_in_a_hip_graph(split):
+    """Chunks of new tokens over cached contexts (pa_prefill_append: the
+    chunks' K/V written and attended in one call), captured and replayed with
+    eager work between replays; with a caller workspace the context is split
+    and the merge kernel is captured too.  Every replay reproduces the eager
+    output and cache writes bit for bit."""
+    from test_gpu_prefill import _append_case, _queries
+    dev = device()
+    lens_l = [3000, 2500, 1777] if split else [40, 300, 129, 777]
+    ms = [8, 40, 1] if split else [40, 100, 17, 300]
+    H, Hkv, D, B = 8, 2, 128, 16
+    case = workloads.random_case(620 + len(lens_l), lens_l, H, Hkv, D, B)
+    kc_h, vc_h, kc_full, vc_full, key_h, val_h, tables, lens = _append_case(case, ms)
+    q_h, qs = _queries(620, ms, H, D)
+    T = int(qs[-1])
+    say(f"graph prefill_append split={split} rows={T}")
+    kc0, vc0 = torch.from_numpy(kc_h).to(dev), torch.from_numpy(vc_h).to(dev)
+    kc, vc = kc0.clone(), vc0.clone()
+    q, key, val = (torch.from_numpy(x).to(dev) for x in (q_h, key_h, val_h))
+    d_t, d_l, d_q = (torch.from_numpy(x).to(dev) for x in (tables, lens, qs))
+    need = pa.pa_prefill_workspace_size(T, len(lens_l), H, Hkv, D, B, tables.shape[1], max(ms))
+    assert need > 0 or not split                               # the split batch needs a workspace
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, H, D), dtype=torch.float16, device=dev)
+
+    def call():
+        pa.pa_prefill_append(out, q, key, val, kc, vc, d_t, d_l, d_q, case.scale, max_query_len=max(ms),
+                             workspace=ws if split else None, split=split)
+
+    def reset():
+        kc.copy_(kc0)
+        vc.copy_(vc0)
+        out.fill_(float("nan"))
+
+    call()                                                   # eager
+    torch.cuda.synchronize()
+    eager_out = bits(out).copy()
+    assert np.array_equal(bits(kc), kc_full.view(np.uint16)) and np.array_equal(bits(vc), vc_full.view(np.uint16))
+    ref = oracle.prefill(q_h, kc_full, vc_full, tables, lens, qs, case.scale)
+    assert_attention_close(out, ref, "eager")
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        reset()
+        call()                                               # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        reset()                                              # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(out), eager_out), f"replay {rep}: output differs"
+        assert np.array_equal(bits(kc), kc_full.view(np.uint16)), f"replay {rep}: K cache"
+        assert np.array_equal(bits(vc), vc_full.view(np.uint16)), f"replay {rep}: V cache"
