@@ -119,9 +119,11 @@ def kernel_source_hash(workload: str) -> str:
 
 
 def traffic_from_profiles(workload: str):
-    """HBM bytes per decode call from the committed PMC summary of this
-    workload, if it was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"decode_{workload}_pmc.json")
+    """HBM bytes per call of the workload's timed kernel (the decode call, or
+    pa_prefill) from the committed PMC summary, if it was taken on the
+    current kernel sources; else None."""
+    name = "prefill_pmc.json" if workload == "prefill" else f"decode_{workload}_pmc.json"
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     try:
@@ -130,7 +132,7 @@ def traffic_from_profiles(workload: str):
         return None
     if d.get("kernel_source_sha256_16") != kernel_source_hash(workload):
         return None
-    return d.get("hbm_bytes_per_decode_call")
+    return d.get("hbm_bytes_per_call", d.get("hbm_bytes_per_decode_call"))
 
 
 def main():
@@ -627,7 +629,7 @@ def prefill_bench(args, dev):
                       "dtype": "f16",
                       "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                                    "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                                   "traffic": None},
+                                   "traffic": traffic_from_profiles("prefill")},
                       "config": {"workload": "prefill", "prompts": S, "tokens": T, "max_prompt": mq,
                                  "num_heads": H, "num_kv_heads": Hkv, "head_dim": D, "block_size": B,
                                  "layers_resident": L}}), flush=True)
