@@ -54,10 +54,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="llama7b", choices=["llama7b", "gqa", "long", "copy", "swap", "prefix", "prefill", "prefill-long", "chunked",
-                            "sweep", "sampling"],
+    p.add_argument("--workload", default="llama7b", choices=["llama7b", "gqa", "long", "copy", "scatter", "swap", "prefix", "prefill",
+                            "prefill-long", "chunked", "sweep", "sampling"],
                    help="llama7b: the Llama-2-7B decode batch (default); gqa: 64 query heads over 8 KV "
-                        "heads (matrix-core kernel); long: 16 x 4096 tokens; copy: block-copy calibration; "
+                        "heads (matrix-core kernel); long: 16 x 4096 tokens; copy: block-copy calibration; scatter: the slot-mapped K/V write; "
                         "swap: block swaps between HBM and pinned host memory; prefix: 100 requests "
                         "sharing a 1000-token system prompt; prefill: causal attention of 32 prompts "
                         "(mean 500 tokens) over the paged cache; prefill-long: full causal prompts of 1k-8k "
@@ -158,6 +158,8 @@ def main():
 
     if args.workload == "copy":
         return copy_bench(args, dev)
+    if args.workload == "scatter":
+        return scatter_bench(args, dev)
     if args.workload == "swap":
         return swap_bench(args, dev)
     if args.workload == "prefix":
@@ -395,6 +397,60 @@ def copy_bench(args, dev):
                                    "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
                       "config": {"workload": "copy-blocks", "pairs": npairs, "block_bytes": block_bytes}}),
           flush=True)
+
+
+def scatter_bench(args, dev):
+    """pa_reshape_and_cache on its own: the prompts of the prefill workload
+    (32 prompts, 15,360 tokens, lengths clip(N(500, 150), 16, 2048)) written
+    into their slots at the Llama-2-7B head shape (32 x 128, fp16, B = 16),
+    slots from the product block manager; then one decode step's write (64
+    tokens, the Llama decode batch's size), which is bound by launch latency.
+    Every byte of K and V is read once and written once."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_390_amd as pa
+    import workloads
+
+    Hkv, D, B = 32, 128, args.block_size
+    sw = workloads.block_size_sweep(seed=args.seed, num_seqs=32, gen_max=1)
+    lens_l = [int(n) - 1 for n in sw.lens]
+    T = int(sum(lens_l))
+    NB = sum(-(-n // B) for n in lens_l) + 8
+    bm = pa.BlockManager(NB, B)
+    slots = np.concatenate([bm.add_sequence(s, n) for s, n in enumerate(lens_l)])
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed)
+    kc = torch.zeros((NB, Hkv, B, D), dtype=torch.float16, device=dev)
+    vc = torch.zeros_like(kc)
+    key = torch.randn((T, Hkv, D), generator=g, device=dev, dtype=torch.float16)
+    val = torch.randn((T, Hkv, D), generator=g, device=dev, dtype=torch.float16)
+    d_slots = torch.from_numpy(slots).to(dev)
+    results = []
+    for name, t in (("prompts", T), ("decode-step", 64)):
+        k_t, v_t, s_t = key[:t], val[:t], d_slots[:t]
+        for _ in range(max(args.warmup, 3)):
+            pa.pa_reshape_and_cache(k_t, v_t, s_t, kc, vc)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for a, b in ev:
+            a.record()
+            pa.pa_reshape_and_cache(k_t, v_t, s_t, kc, vc)
+            b.record()
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+        moved = 2 * t * Hkv * D * 2                   # K and V bytes, each read once and written once
+        gbs = 2 * moved / us / 1e3
+        log(f"[bench] scatter {name}: {t} tokens x {Hkv} x {D}, {us:.1f} us per call = {gbs:.0f} GB/s (read+write)")
+        results.append({"write": name, "tokens": t, "us": round(us, 2), "GB_s": round(gbs, 2)})
+    best = results[0]
+    print(json.dumps({"metric": "slot-mapped KV write GB/s (read+write)", "value": best["GB_s"], "unit": "GB/s",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+                      "dtype": "f16", "writes": results,
+                      "roofline": {"bound": "hbm", "achieved": best["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": round(best["GB_s"] / HBM_PEAK_GBS, 4), "traffic": None},
+                      "config": {"workload": "reshape-and-cache", "tokens": T, "num_kv_heads": Hkv, "head_dim": D,
+                                 "block_size": B}}), flush=True)
 
 
 def swap_bench(args, dev):

@@ -57,8 +57,13 @@ scatter_kv_kernel(const uint16_t* __restrict__ key, const uint16_t* __restrict__
     const int64_t src = t * token_stride + (int64_t)h * head_dim + (int64_t)c * VEC;
     const int64_t dst = ((blk * num_kv_heads + h) * block_size + row) * head_dim + (int64_t)c * VEC;
     if constexpr (VEC == 8) {
-        *reinterpret_cast<uint4*>(k_cache + dst) = *reinterpret_cast<const uint4*>(key + src);
-        *reinterpret_cast<uint4*>(v_cache + dst) = *reinterpret_cast<const uint4*>(value + src);
+        // nontemporal both ways: each byte is moved once (15360 prompt tokens
+        // at 32 x 128 heads: 96 instead of 102 us)
+        typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
+        const u32x4_nt kv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(key + src));
+        const u32x4_nt vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(value + src));
+        __builtin_nontemporal_store(kv, reinterpret_cast<u32x4_nt*>(k_cache + dst));
+        __builtin_nontemporal_store(vv, reinterpret_cast<u32x4_nt*>(v_cache + dst));
     } else {
         k_cache[dst] = key[src];
         v_cache[dst] = value[src];
