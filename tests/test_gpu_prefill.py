@@ -216,7 +216,8 @@ def test_prompt_prefill_at_the_llama_shape():
     """8 prompts of the block-size-sweep length mix (normal around 500
     tokens) at 32 x 128 heads, B = 16: the product block manager admits
     them, the product scatter writes their K/V, pa_prefill attends; every
-    row against the oracle."""
+    row against the oracle; then pa_prefill_append on a NaN cache writes the
+    same caches and the same outputs bit for bit."""
     dev = device()
     rng = np.random.default_rng(12)
     lens_l = [int(x) for x in np.clip(np.rint(rng.normal(500, 150, size=8)), 16, 2048)]
@@ -244,6 +245,17 @@ def test_prompt_prefill_at_the_llama_shape():
     say(f"llama prompts: {lens_l}, T={T}")
     ref = oracle.prefill(q.cpu().numpy(), kc.cpu().numpy(), vc.cpu().numpy(), tables, lens, qs, 1 / np.sqrt(D))
     assert_attention_close(out, ref, "llama prompts")
+    # the same prompts through pa_prefill_append on a cache holding only NaN:
+    # the caches it writes equal the scatter's bit for bit, and so do the outputs
+    # (both calls read the same K/V values, in the same order)
+    kc2 = torch.full_like(kc, float("nan"))
+    vc2 = torch.full_like(kc, float("nan"))
+    out2 = torch.empty_like(q)
+    pa.pa_prefill_append(out2, q, key, val, kc2, vc2, torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev),
+                         torch.from_numpy(qs).to(dev), 1 / np.sqrt(D), max_query_len=max(lens_l))
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(kc2), bits(kc)) and np.array_equal(bits(vc2), bits(vc)), "append: caches differ"
+    assert np.array_equal(bits(out2), bits(out)), "append: outputs differ from pa_prefill's"
 
 
 def _append_case(case, ms):
