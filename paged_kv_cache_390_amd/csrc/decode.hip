@@ -716,9 +716,11 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
     if (L.num_parts > 65535)
         return pa::fail(PA_ERR_INVALID, "%s: max_context_len %d needs %d partitions of %d (limit 65535)", fn,
                         max_context_len, L.num_parts, p);
-    const int64_t len_cap_tables = (int64_t)max_blocks_per_seq * block_size;
-    const int64_t len_cap_grid = (int64_t)L.num_parts * p;
-    const int64_t len_cap = len_cap_tables < len_cap_grid ? len_cap_tables : len_cap_grid;
+    // a row is computed only when its length fits the table, the grid and
+    // the caller's bound; any other row comes out as NaN
+    int64_t len_cap = (int64_t)max_blocks_per_seq * block_size;
+    if ((int64_t)L.num_parts * p < len_cap) len_cap = (int64_t)L.num_parts * p;
+    if ((int64_t)max_context_len < len_cap) len_cap = max_context_len;
 
     char* wsb = static_cast<char*>(workspace);
     int32_t* own_order = compute_order ? reinterpret_cast<int32_t*>(wsb) : nullptr;
@@ -796,3 +798,4 @@ extern "C" int pa_decode_append(void* out, const void* q, const void* key, const
                        context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
                        max_context_len, partition_size, workspace, workspace_bytes, seq_order, dtype, stream, &app);
 }
+

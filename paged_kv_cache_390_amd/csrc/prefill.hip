@@ -592,9 +592,13 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
     __builtin_amdgcn_s_barrier();
     auto step = [&](int k, unsigned char* cb, unsigned char* cf, const Staged& cs, unsigned char* nb,
                     unsigned char* nf, Staged& ns) {
-        fetch_tile<B, kStream, kAppend>(ns, nb, k + 1, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks,
-                                        ap);
-        if constexpr (B >= 4) table_entries<B>(e, k + 2, wave, n, trow);
+        // the last step of the walk fetches nothing: no step consumes tile k_end
+        const bool more = k + 1 < k_end;
+        if (more)
+            fetch_tile<B, kStream, kAppend>(ns, nb, k + 1, e, wave, lane, n, trow, kbase, vbase, blk_stride,
+                                            num_blocks, ap);
+        if constexpr (B >= 4)
+            if (k + 2 < k_end) table_entries<B>(e, k + 2, wave, n, trow);
         if (k < my_end) {
             // uniform: tile below the wave's first row and wholly valid
             bool interior = k * kKvTile + kKvTile - 1 <= first_pos;
@@ -613,7 +617,7 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
         // next step's products instead of stalling this step's wait; the LDS
         // reads finish before the barrier, ahead of the next fetch into `cb`
         if constexpr (kAppend) write_own_rows<B>(cs, cb, k, wave, lane, kw, vw, blk_stride);
-        finish_tile(ns, nb, nf, wave, lane);
+        if (more) finish_tile(ns, nb, nf, wave, lane);
         PA_WAIT_LGKM0();
         __builtin_amdgcn_s_barrier();
     };

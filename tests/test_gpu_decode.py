@@ -267,6 +267,21 @@ def test_rows_longer_than_the_bound_are_nan_and_others_unaffected():
     assert_attention_close(out, ref, "bounded")
 
 
+@pytest.mark.parametrize("P,bound", [(0, 100), (256, 300), (128, 200)])
+def test_rows_past_a_bound_off_the_partition_grid_are_nan(P, bound):
+    """The bound need not be a whole number of partitions: a row longer
+    than max_context_len is NaN even where the partitions the grid covers
+    would reach it (n = 200 > 100 with the default partition)."""
+    dev = device()
+    case = workloads.random_case(13, [bound, bound + 1, 60, 2 * bound], 2, 2, 128, 16)
+    kc, vc, tables, lens = _oracle_cache(case)
+    out = _gpu_decode(dev, case.q, kc, vc, tables, lens, case.scale, partition_size=P, max_context_len=bound)
+    ref = oracle.decode(case.q, kc, vc, tables, lens, case.scale)
+    ref[1] = np.nan
+    ref[3] = np.nan
+    assert_attention_close(out, ref, f"bound {bound} P={P}")
+
+
 def test_table_entries_outside_the_pool_are_skipped():
     dev = device()
     case = workloads.random_case(12, [64, 80], 2, 2, 128, 16)
