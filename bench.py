@@ -35,6 +35,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -55,14 +56,16 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="llama7b", choices=["llama7b", "gqa", "long", "copy", "scatter", "swap", "prefix", "prefill",
-                            "prefill-long", "chunked", "sweep", "sampling"],
+                            "prefill-long", "chunked", "sweep", "sampling", "read", "tiny"],
                    help="llama7b: the Llama-2-7B decode batch (default); gqa: 64 query heads over 8 KV "
                         "heads (matrix-core kernel); long: 16 x 4096 tokens; copy: block-copy calibration; scatter: the slot-mapped K/V write; "
                         "swap: block swaps between HBM and pinned host memory; prefix: 100 requests "
                         "sharing a 1000-token system prompt; prefill: causal attention of 32 prompts "
                         "(mean 500 tokens) over the paged cache; prefill-long: full causal prompts of 1k-8k "
                         "tokens; sweep: decode of 256 sequences at "
-                        "block_size 8/16/32/64; sampling: 32 samples of one prompt with copy-on-write")
+                        "block_size 8/16/32/64; sampling: 32 samples of one prompt with copy-on-write; "
+                        "read: read-only streaming ceilings (contiguous, and the decode's block pattern); "
+                        "tiny: latency of the 4-sequence tiny case")
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--batch", type=int, default=0, help="sequences (0: 64 for llama7b, 256 for gqa)")
     p.add_argument("--block-size", type=int, default=16)
@@ -118,10 +121,10 @@ def kernel_source_hash(workload: str) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str):
-    """HBM bytes per call of the workload's timed kernel (the decode call, or
-    pa_prefill) from the committed PMC summary, if it was taken on the
-    current kernel sources; else None."""
+def pmc_summary(workload: str):
+    """The committed PMC summary of the workload's timed kernel (the decode
+    call, or pa_prefill), if it was taken on the current kernel sources;
+    else None."""
     name = "prefill_pmc.json" if workload == "prefill" else f"decode_{workload}_pmc.json"
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
@@ -132,7 +135,108 @@ def traffic_from_profiles(workload: str):
         return None
     if d.get("kernel_source_sha256_16") != kernel_source_hash(workload):
         return None
-    return d.get("hbm_bytes_per_call", d.get("hbm_bytes_per_decode_call"))
+    return d
+
+
+def traffic_from_profiles(workload: str):
+    """HBM bytes per call from the committed PMC summary (see pmc_summary)."""
+    d = pmc_summary(workload)
+    return None if d is None else d.get("hbm_bytes_per_call", d.get("hbm_bytes_per_decode_call"))
+
+
+def traffic_fields(workload: str) -> dict:
+    """roofline fields from the PMC summary: the measured HBM bytes per call
+    (`traffic`), the same run's algorithmic bytes per call and their ratio,
+    and the cached tokens of the profiled calls -- the counter run is a short
+    one whose batch has grown fewer steps than the timed one, so its bytes
+    are compared with its own algorithmic bytes, never with this line's."""
+    d = pmc_summary(workload)
+    if d is None:
+        return {"traffic": None}
+    out = {"traffic": d.get("hbm_bytes_per_call", d.get("hbm_bytes_per_decode_call"))}
+    alg = d.get("algorithmic_total_bytes_per_call")
+    if alg:
+        out["traffic_algorithmic_bytes"] = alg
+        out["traffic_ratio"] = round(out["traffic"] / alg, 4)
+    if d.get("cached_tokens_per_call"):
+        out["traffic_ctx_tokens"] = d["cached_tokens_per_call"]
+    return out
+
+
+def host_cpu() -> dict:
+    """The host the oracle runs on: logical CPUs, those this process may use,
+    the job's CPU share (OMP_NUM_THREADS) and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        aff = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        aff = None
+    return {"nproc": os.cpu_count(), "affinity_cpus": aff, "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
+            "cpu_model": model}
+
+
+def stats_of(xs, scale: float = 1e3, nd: int = 3) -> dict:
+    """median / mean / min / max of a list of seconds, times `scale` (ms by
+    default), and the sample count."""
+    import statistics
+    return {"median": round(statistics.median(xs) * scale, nd), "mean": round(sum(xs) / len(xs) * scale, nd),
+            "min": round(min(xs) * scale, nd), "max": round(max(xs) * scale, nd), "n": len(xs)}
+
+
+def tiny_latency(dev, reps: int = 100, oracle_reps: int = 200, with_oracle: bool = True) -> dict:
+    """The tiny case (4 sequences of 1/5/12/50 tokens, B = 4, 2 heads x 16,
+    sequence 2 on the page's table [7, 3, 1]): pa_decode latency, each call
+    bracketed by its own HIP events (launch included), and the oracle's
+    latency on the same inputs."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_390_amd as pa
+    import workloads
+
+    w = workloads.tiny(seed=0)
+    S, B = len(w.lens), w.block_size
+    bm = pa.BlockManager(w.num_blocks, B)
+    for s, (n, t) in enumerate(zip(w.lens, w.tables)):
+        bm.set_table(s, t, n)
+    width = max(len(t) for t in w.tables)
+    slots = np.concatenate([bm.get_slots(s, 0, n) for s, n in enumerate(w.lens)])
+    tables, lens = bm.get_tables(range(S), width)
+    kc = torch.zeros((w.num_blocks, w.num_kv_heads, B, w.head_dim), dtype=torch.float16, device=dev)
+    vc = torch.zeros_like(kc)
+    pa.pa_reshape_and_cache(torch.from_numpy(w.k_tokens).to(dev), torch.from_numpy(w.v_tokens).to(dev),
+                            torch.from_numpy(slots).to(dev), kc, vc)
+    q = torch.from_numpy(w.q).to(dev)
+    d_t, d_l = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
+    out = torch.empty_like(q)
+    for _ in range(10):
+        pa.pa_decode(out, q, kc, vc, d_t, d_l, w.scale, B)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        pa.pa_decode(out, q, kc, vc, d_t, d_l, w.scale, B)
+        b.record()
+    torch.cuda.synchronize()
+    res = {"workload": "tiny", "gpu_us": stats_of([a.elapsed_time(b) / 1e3 for a, b in ev], 1e6, 2)}
+    if with_oracle:
+        import oracle
+        kc_h, vc_h = kc.cpu().numpy(), vc.cpu().numpy()
+        ts = []
+        for _ in range(oracle_reps):
+            t0 = time.perf_counter()
+            oracle.decode(w.q, kc_h, vc_h, tables, lens, w.scale, nthreads=1)
+            ts.append(time.perf_counter() - t0)
+        res["oracle_us_1_thread"] = stats_of(ts, 1e6, 2)
+    return res
 
 
 def main():
@@ -174,6 +278,10 @@ def main():
         return sweep_bench(args, dev)
     if args.workload == "sampling":
         return sampling_bench(args, dev)
+    if args.workload == "read":
+        return read_bench(args, dev)
+    if args.workload == "tiny":
+        return tiny_bench(args, dev)
 
     L = args.layers
     B = args.block_size
@@ -308,25 +416,41 @@ def main():
 
     # ---- oracle on the host cores, same workload (layer 0, one decode)
     cpu = None
+    tiny = None
     if args.cpu_baseline:
         import oracle
         threads = oracle.default_threads()
         tables, lens = bm.get_tables(seqs, width)
         q_h = q.cpu().numpy()
         kc_h, vc_h = oracle_pool
-        reps, spent, kv_done = 0, 0.0, 0
-        while reps == 0 or spent < args.cpu_seconds:
+        layer_kv = int(lens.astype(np.int64).sum()) * kv_per_token
+        per_call, spent = [], 0.0
+        while len(per_call) < 3 or spent < args.cpu_seconds:
             c0 = time.perf_counter()
             oracle.decode(q_h, kc_h, vc_h, tables, lens, w.scale, nthreads=threads)
-            spent += time.perf_counter() - c0
-            kv_done += int(lens.astype(np.int64).sum()) * kv_per_token
-            reps += 1
-        cpu = {"value": round(kv_done / spent / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-               "sample": f"{reps} x one layer's decode of the same batch ({S} seqs x {H} heads, "
-                         f"{int(lens.sum())} cached tokens), fp64 C oracle, {spent:.1f} s"}
-        log(f"[bench] cpu oracle: {cpu['value']} GB/s on {threads} threads ({spent:.1f}s)")
+            per_call.append(time.perf_counter() - c0)
+            spent += per_call[-1]
+        c0 = time.perf_counter()
+        oracle.decode(q_h, kc_h, vc_h, tables, lens, w.scale, nthreads=1)
+        one = time.perf_counter() - c0
+        med = statistics.median(per_call)
+        cpu = {"value": round(layer_kv / med / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"{len(per_call)} x one layer's decode of the same batch ({S} seqs x {H} heads, "
+                         f"{int(lens.sum())} cached tokens, {layer_kv / 1e9:.3f} GB of K/V), fp64 C oracle on "
+                         f"{threads} threads, {spent:.1f} s; value from the median call",
+               "per_call_ms": stats_of(per_call),
+               "value_from_mean": round(layer_kv * len(per_call) / spent / 1e9, 4),
+               "single_thread": {"value": round(layer_kv / one / 1e9, 4), "unit": "GB/s",
+                                 "ms_per_call": round(one * 1e3, 1),
+                                 "sample": "one call of the same layer's decode on 1 thread"},
+               **host_cpu()}
+        log(f"[bench] cpu oracle: {cpu['value']} GB/s on {threads} threads (median of {len(per_call)} calls, "
+            f"{spent:.1f}s); 1 thread {cpu['single_thread']['value']} GB/s")
+        tiny = tiny_latency(dev)
+        log(f"[bench] tiny case: pa_decode {tiny['gpu_us']['median']} us (median, launch included), oracle "
+            f"{tiny['oracle_us_1_thread']['median']} us on 1 thread")
 
-    traffic = traffic_from_profiles(args.workload)
+    traffic = traffic_fields(args.workload)
     line = {
         "metric": "paged-decode achieved KV GB/s (% of HBM peak) + tokens/s per layer, bs=16",
         "value": round(value, 2),
@@ -343,7 +467,9 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s_per_layer": round(tokens_per_s_layer, 1),
         "decode_only": {"GB_s": round(achieved, 2), "pct_hbm_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
-                        "tokens_per_s_per_layer": round(S / dec_avg_s, 1), "us_per_call": round(dec_avg_s * 1e6, 2)},
+                        "tokens_per_s_per_layer": round(S / dec_avg_s, 1), "us_per_call": round(dec_avg_s * 1e6, 2),
+                        "us_per_call_by_sweep": stats_of([x / 1e3 for x in dec_ms], 1e6, 2),
+                        "GB_s_from_median_sweep": round(kv_per_launch / (statistics.median(dec_ms) / 1e3) / 1e9, 2)},
         "config": {"workload": wl_name, "batch": S, "block_size": B, "num_heads": H, "num_kv_heads": Hkv,
                    "head_dim": D, "context": ctx_desc, "layers_resident": L, "pool_blocks_per_layer": NB,
                    "partition_size": part or pa.pa_decode_default_partition(S, H, Hkv, D, B, width * B),
@@ -351,8 +477,11 @@ def main():
                             "written inside the decode call)" if args.fused else
                             "host append+tables, H2D, decode order, per layer reshape_and_cache + decode")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), **traffic,
+                     "kernel": "decode call (partition kernel + merge kernel when a context is split)",
+                     "algorithmic_bytes_per_call": kv_per_launch, "cached_tokens_per_call": ctx_last},
         "cpu_baseline": cpu,
+        "tiny_latency": tiny,
     }
     print(json.dumps(line), flush=True)
 
@@ -962,6 +1091,93 @@ def sampling_bench(args, dev):
                       "config": {"workload": "parallel-sampling", "samples": N, "prompt": w.prompt_len,
                                  "block_size": B, "num_heads": w.num_heads, "head_dim": w.head_dim,
                                  "fused": bool(args.fused)}}), flush=True)
+
+
+def read_bench(args, dev):
+    """Read-only streaming ceilings on this chip (include/pa_bench.h), timed
+    like the decode call: a plain contiguous read of a 4 GiB buffer, one MiB
+    per workgroup; and the Llama-2-7B decode batch's access pattern -- the K
+    and V slabs of every block of every (sequence, KV head), scattered by the
+    tables -- over --layers resident layers, with no arithmetic.  Beside them
+    pa_decode on the same batch and layers (default partition, longest-first
+    order computed once).  Each is timed with HIP events around --steps
+    sweeps; GB/s from the median sweep."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_390_amd as pa
+    import workloads
+
+    B, L = args.block_size, args.layers
+    w = workloads.llama7b_decode(seed=args.seed, num_seqs=args.batch or 64, block_size=B)
+    S, H, Hkv, D, NB = len(w.lens), w.num_heads, w.num_kv_heads, w.head_dim, w.num_blocks
+    pools = [w.pool(l, dev) for l in range(L)]
+    tables = torch.from_numpy(np.ascontiguousarray(w.perm_tables)).to(dev)
+    lens = torch.from_numpy(w.lens).to(dev)
+    width = tables.shape[1]
+    q, _, _ = w.new_tokens(0, dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(max(1, pa.pa_decode_workspace_size(S, H, Hkv, D, B, width * B, 0)), dtype=torch.uint8,
+                     device=dev)
+    order = pa.pa_decode_order(lens, width * B)
+    sink = torch.empty(S * Hkv, dtype=torch.int32, device=dev)
+    buf = torch.zeros(4 << 30, dtype=torch.uint8, device=dev)
+    bsink = torch.empty(max(1, buf.numel() >> 20), dtype=torch.int32, device=dev)
+    kv_tok = 2 * Hkv * D * 2
+    n = w.lens.astype(np.int64)
+    decode_bytes = int(n.sum()) * kv_tok
+    block_bytes = int((-(-n // B) * B).sum()) * kv_tok
+
+    def sweeps(call, per_sweep):
+        for _ in range(max(args.warmup, 3)):
+            for l in range(per_sweep):
+                call(l)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        ev[0].record()
+        for i in range(args.steps):
+            for l in range(per_sweep):
+                call(l)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) / 1e3 / per_sweep for i in range(args.steps)]
+
+    res = {}
+    t = sweeps(lambda l: pa.pa_bench_stream_read(buf, bsink), 1)
+    res["contiguous_read"] = {"bytes_per_call": buf.numel(), "us_per_call": stats_of(t, 1e6, 2),
+                              "GB_s": round(buf.numel() / statistics.median(t) / 1e9, 2)}
+    t = sweeps(lambda l: pa.pa_bench_block_read(pools[l][0], pools[l][1], tables, lens, sink), L)
+    res["block_pattern_read"] = {"bytes_per_call": block_bytes, "us_per_call": stats_of(t, 1e6, 2),
+                                 "GB_s": round(block_bytes / statistics.median(t) / 1e9, 2)}
+    t = sweeps(lambda l: pa.pa_decode(out, q, pools[l][0], pools[l][1], tables, lens, w.scale, B,
+                                      max_context_len=width * B, workspace=ws, seq_order=order), L)
+    res["decode"] = {"bytes_per_call": decode_bytes, "us_per_call": stats_of(t, 1e6, 2),
+                     "GB_s": round(decode_bytes / statistics.median(t) / 1e9, 2)}
+    for k, r in res.items():
+        log(f"[bench] {k}: {r['us_per_call']['median']} us per call (median) = {r['GB_s']} GB/s "
+            f"({100 * r['GB_s'] / HBM_PEAK_GBS:.1f}% of peak)")
+    print(json.dumps({"metric": "read-only streaming GB/s (same-chip ceiling for paged decode)",
+                      "value": res["block_pattern_read"]["GB_s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+                      "warmup": args.warmup, "higher_is_better": True, "dtype": "f16", "data": "synthetic",
+                      "reads": res,
+                      "decode_over_block_read": round(res["decode"]["GB_s"] / res["block_pattern_read"]["GB_s"], 4),
+                      "config": {"workload": "read-ceiling", "batch": S, "block_size": B, "num_kv_heads": Hkv,
+                                 "head_dim": D, "context": "U[1,2048]", "layers_resident": L}}), flush=True)
+
+
+def tiny_bench(args, dev):
+    """Latency of the tiny case (4 sequences of 1/5/12/50 tokens, block_size
+    4, 2 heads x 16; sequence 2 on the 5688vip.com page's table [7, 3, 1]):
+    pa_decode with each call between its own HIP events (launch included),
+    and the fp64 oracle on one thread on the same inputs."""
+    r = tiny_latency(dev, reps=max(args.steps, 20))
+    log(f"[bench] tiny: pa_decode {r['gpu_us']['median']} us median ({r['gpu_us']['min']}..{r['gpu_us']['max']}), "
+        f"oracle {r['oracle_us_1_thread']['median']} us")
+    print(json.dumps({"metric": "paged-decode latency, tiny case", "value": r["gpu_us"]["median"], "unit": "us",
+                      "n_gpus": 1, "steps": r["gpu_us"]["n"], "higher_is_better": False, "dtype": "f16",
+                      "data": "synthetic", **r,
+                      "config": {"workload": "tiny", "lens": [1, 5, 12, 50], "block_size": 4, "num_heads": 2,
+                                 "head_dim": 16}}), flush=True)
 
 
 if __name__ == "__main__":

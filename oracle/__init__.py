@@ -57,8 +57,18 @@ def lib() -> ctypes.CDLL:
 
 
 def default_threads() -> int:
-    n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+    """Threads the oracle uses: the CPUs this process may run on, capped by
+    OMP_NUM_THREADS when it is set (the machine's CPU share for one job),
+    else by 16."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "") or 16)
+    except ValueError:
+        cap = 16
+    return max(1, min(n, cap))
 
 
 def _ptr(a: np.ndarray) -> int:

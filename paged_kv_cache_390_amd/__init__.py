@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
         "pa_decode_default_partition": ([i32, i32, i32, i32, i32, i32], i32),
         "pa_copy_blocks": ([P, P, i32, P, i32, i32, i64, i32, P], ctypes.c_int),
         "pa_swap_blocks": ([P, P, i32, P, i32, i32, i32, i64, i32, i32, P], ctypes.c_int),
+        "pa_bench_stream_read_groups": ([sz], i64),
+        "pa_bench_stream_read": ([P, sz, P, P], ctypes.c_int),
+        "pa_bench_block_read": ([P, P, P, i32, P, i32, i32, i32, i32, i32, P, P], ctypes.c_int),
         "pa_bm_create": ([i32, i32], P),
         "pa_bm_create_with_host": ([i32, i32, i32], P),
         "pa_bm_swap_out": ([P, P, i32, P, i32, P], ctypes.c_int),
@@ -445,6 +448,51 @@ def pa_swap_blocks(dev_caches: Sequence, host_caches: Sequence, pairs, direction
 # ---------------------------------------------------------------------------
 # host block manager
 # ---------------------------------------------------------------------------
+def pa_bench_stream_read(buf, sink=None):
+    """Measurement aid (include/pa_bench.h): read every byte of the
+    contiguous device tensor `buf` once; returns the sink tensor (one uint32
+    word per MiB, as int32)."""
+    torch = _torch()
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    groups = lib().pa_bench_stream_read_groups(nbytes)
+    if sink is None:
+        sink = torch.empty(max(groups, 1), dtype=torch.int32, device=buf.device)
+    _dev_tensor(sink, "sink", torch.int32, 1)
+    if sink.numel() < groups:
+        raise ValueError(f"sink needs {groups} words")
+    _check(lib().pa_bench_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), _stream(buf.device)),
+           "pa_bench_stream_read")
+    return sink
+
+
+def pa_bench_block_read(k_cache, v_cache, block_tables, context_lens, sink=None):
+    """Measurement aid (include/pa_bench.h): the decode access pattern --
+    the K and V slabs of every block of every (sequence, KV head) -- with
+    no arithmetic; returns the sink tensor (one word per pair)."""
+    torch = _torch()
+    _dev_tensor(k_cache, "k_cache", torch.float16, 4)
+    _dev_tensor(v_cache, "v_cache", torch.float16, 4)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    NB, Hkv, B, D = k_cache.shape
+    _dev_tensor(block_tables, "block_tables", torch.int32, 2)
+    _dev_tensor(context_lens, "context_lens", torch.int32, 1)
+    S, W = block_tables.shape
+    if context_lens.shape[0] != S:
+        raise ValueError("context_lens must have one entry per sequence")
+    if sink is None:
+        sink = torch.empty(max(S * Hkv, 1), dtype=torch.int32, device=k_cache.device)
+    _dev_tensor(sink, "sink", torch.int32, 1)
+    if sink.numel() < S * Hkv:
+        raise ValueError(f"sink needs {S * Hkv} words")
+    _check(lib().pa_bench_block_read(k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), W,
+                                     context_lens.data_ptr(), S, Hkv, D, B, NB, sink.data_ptr(),
+                                     _stream(k_cache.device)), "pa_bench_block_read")
+    return sink
+
+
 def _i64(a) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(a, dtype=np.int64))
 

@@ -1,4 +1,4 @@
-"""The C-ABI library loads and exports every function include/pa.h declares;
+"""The C-ABI library loads and exports every function include/*.h declares;
 argument errors are reported before any device work (no GPU needed)."""
 import ctypes
 import os
@@ -12,10 +12,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared():
-    text = open(os.path.join(ROOT, "include", "pa.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)
-    return sorted(set(names))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if not h.endswith(".h"):
+            continue
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_three_calls():
