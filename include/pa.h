@@ -192,6 +192,34 @@ int pa_decode_append(void *out, const void *q, const void *key,
                      size_t workspace_bytes, const int32_t *seq_order,
                      int32_t dtype, void *stream);
 
+/* ------------------------------------------------------------------------
+ * pa_decode without a caller workspace, for callers that cannot allocate
+ * device memory (code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid allocation).  The library keeps the workspace in a
+ * device array of PA_NOALLOC_SCRATCH_BYTES bytes per GPU, reserved when the
+ * library's code is loaded on that GPU and held until the process ends; the
+ * call itself allocates nothing.
+ *
+ * Arguments, results and error behaviour are those of pa_decode with
+ * workspace = that array.  PA_ERR_INVALID, before anything is enqueued, when
+ * the sizes need more workspace than the array holds
+ * (pa_decode_workspace_size() > PA_NOALLOC_SCRATCH_BYTES).  Every call on
+ * one GPU shares its array: calls that may overlap on a GPU (different
+ * streams without ordering between them, or several host threads) race and
+ * must be serialised by the caller.  Nothing in the array needs to be
+ * cleared between calls.
+ * ------------------------------------------------------------------------ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int pa_decode_noalloc(void *out, const void *q, const void *k_cache,
+                      const void *v_cache, const int32_t *block_tables,
+                      int32_t max_blocks_per_seq, const int32_t *context_lens,
+                      int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                      float scale, int32_t max_context_len,
+                      int32_t partition_size, const int32_t *seq_order,
+                      int32_t dtype, void *stream);
+
 /* Longest-first dispatch order for pa_decode: seq_order (device, int32
  * [num_seqs], written) becomes a permutation of 0 .. num_seqs - 1 with the
  * sequences sorted by context_lens into 1024 classes of

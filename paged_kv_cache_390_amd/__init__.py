@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         "pa_prefill": ([P, P, i32, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, f32, i32, P, sz, i32, P],
                        ctypes.c_int),
         "pa_decode_order": ([P, P, i32, i32, P], ctypes.c_int),
+        "pa_decode_noalloc": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P, i32, P],
+                              ctypes.c_int),
         "pa_prefill_append": ([P, P, i32, P, P, i64, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, f32, i32, P, sz,
                                i32, P], ctypes.c_int),
         "pa_prefill_workspace_size": ([i32, i32, i32, i32, i32, i32, i32, i32], sz),
@@ -257,6 +259,45 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float
                            block_tables.data_ptr(), W, context_lens.data_ptr(), S, H, Hkv, D, B, NB,
                            float(scale), mcl, int(partition_size), ws_ptr, ws_bytes,
                            order_ptr, PA_DTYPE_F16, _stream(q.device)), "pa_decode")
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                      block_size: Optional[int] = None, max_context_len: Optional[int] = None,
+                      partition_size: int = 0, seq_order=None) -> None:
+    """pa_decode with the workspace held by the library (one fixed-size
+    device array per GPU): allocates nothing, for callers that cannot.
+    Raises PAError (PA_ERR_INVALID) when the sizes need more workspace than
+    that array holds.  Calls that may overlap on one GPU share the array and
+    must be serialised by the caller."""
+    torch = _torch()
+    _dev_tensor(k_cache, "k_cache", torch.float16, 4)
+    _dev_tensor(v_cache, "v_cache", torch.float16, 4)
+    NB, Hkv, B, D = k_cache.shape
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    if block_size is not None and block_size != B:
+        raise ValueError(f"block_size {block_size} != cache block dimension {B}")
+    _dev_tensor(q, "q", torch.float16, 3)
+    _dev_tensor(out, "out", torch.float16, 3)
+    S, H, Dq = q.shape
+    if Dq != D or tuple(out.shape) != (S, H, D):
+        raise ValueError("q/out must be [S, H, head_dim]")
+    _dev_tensor(block_tables, "block_tables", torch.int32, 2)
+    _dev_tensor(context_lens, "context_lens", torch.int32, 1)
+    if block_tables.shape[0] != S or context_lens.shape[0] != S:
+        raise ValueError("block_tables/context_lens must have one row per sequence")
+    W = block_tables.shape[1]
+    mcl = W * B if max_context_len is None else int(max_context_len)
+    order_ptr = None
+    if seq_order is not None:
+        _dev_tensor(seq_order, "seq_order", torch.int32, 1)
+        if seq_order.shape[0] != S:
+            raise ValueError("seq_order must have one entry per sequence")
+        order_ptr = seq_order.data_ptr()
+    _check(lib().pa_decode_noalloc(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                   block_tables.data_ptr(), W, context_lens.data_ptr(), S, H, Hkv, D, B, NB,
+                                   float(scale), mcl, int(partition_size), order_ptr, PA_DTYPE_F16,
+                                   _stream(q.device)), "pa_decode_noalloc")
 
 
 def pa_decode_append(out, q, key, value, k_cache, v_cache, block_tables, context_lens, scale: float,

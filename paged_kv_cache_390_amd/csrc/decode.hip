@@ -53,6 +53,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "decode_internal.h"
 #include "pa.h"
@@ -799,3 +800,71 @@ extern "C" int pa_decode_append(void* out, const void* q, const void* key, const
                        max_context_len, partition_size, workspace, workspace_bytes, seq_order, dtype, stream, &app);
 }
 
+// ---------------------------------------------------------------------------
+// pa_decode_noalloc: pa_decode with its workspace held by the library, for
+// callers that cannot allocate device memory.  The workspace lives in a
+// file-scope device array (one copy per GPU, kept until the process ends);
+// its device address is looked up once per device with that device current
+// and kept, and only that address is ever handed to kernels.  Nothing in it
+// has to start at zero: the order kernel writes every entry it later reads,
+// and the partition kernel writes every partial state before the merge
+// kernel reads it.
+namespace {
+
+constexpr size_t kScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(const char* fn, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return pa::fail(PA_ERR_HIP, "%s: device %d out of range", fn, dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return pa::fail(PA_ERR_HIP, "%s: hipGetSymbolAddress: %s", fn, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 float scale, int32_t max_context_len, int32_t partition_size,
+                                 const int32_t* seq_order, int32_t dtype, void* stream) {
+    const char* fn = "pa_decode_noalloc";
+    // the same argument checks and workspace layout as pa_decode; sizes
+    // that pa_decode would refuse are refused by decode_impl below
+    if (!bad_geometry(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, partition_size) &&
+        supported_block_size(block_size) && num_seqs > 0) {
+        const int32_t p = partition_size ? partition_size
+                                         : default_partition(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                             block_size, max_context_len);
+        const size_t need = workspace_layout(num_seqs, num_heads, head_dim, max_context_len, p).total;
+        if (need > kScratchBytes)
+            return pa::fail(PA_ERR_INVALID,
+                            "%s: these sizes need %zu bytes of workspace, above the library's %zu-byte scratch; "
+                            "call pa_decode with a workspace instead (or a longer partition_size)",
+                            fn, need, kScratchBytes);
+    }
+    void* ws = nullptr;
+    if (num_seqs > 0) {
+        const int rc = scratch_address(fn, &ws);
+        if (rc != PA_OK) return rc;
+    }
+    return decode_impl(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                       num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, max_context_len,
+                       partition_size, ws, ws ? kScratchBytes : 0, seq_order, dtype, stream, nullptr);
+}

@@ -1,0 +1,110 @@
+"""pa_decode_noalloc -- pa_decode with its workspace held by the library, for
+callers that cannot allocate -- called through the C ABI against pa_decode
+given a caller workspace: bit-identical outputs (same kernels, same
+partitions), also within tolerance of the oracle.  Two calls in a row, the
+second with a smaller batch, for the vector kernel and the matrix-core
+(grouped-query) kernel, with split contexts so that the library's array
+holds partial states and the dispatch order."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_390_amd as pa
+import workloads
+from gpu_common import assert_attention_close, bits, device, poisoned_cache, say
+from oracle.block_manager import BlockManagerModel
+
+SCRATCH_BYTES = 64 << 20          # PA_NOALLOC_SCRATCH_BYTES in include/pa.h
+
+
+def _c_call():
+    f = pa.lib().pa_decode_noalloc
+    P, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    f.argtypes = [P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P, i32, P]
+    f.restype = ctypes.c_int
+    return f
+
+
+def _oracle_cache(case):
+    m = BlockManagerModel(case.num_blocks, case.block_size)
+    for s, (n, t) in enumerate(zip(case.lens, case.tables)):
+        m.set_table(s, t, n)
+    slots = np.array([m.slot(s, p) for s, n in enumerate(case.lens) for p in range(n)], dtype=np.int64)
+    kc = poisoned_cache(case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim)
+    vc = kc.copy()
+    oracle.reshape_and_cache(case.k_tokens, case.v_tokens, slots, kc, vc)
+    width = max(1, max(len(t) for t in case.tables))
+    rows, lens = m.tables(range(len(case.lens)), width)
+    return kc, vc, np.array(rows, dtype=np.int32), np.array(lens, dtype=np.int32)
+
+
+def _run(dev, case, P):
+    kc_h, vc_h, tables_h, lens_h = _oracle_cache(case)
+    S, H, D = case.q.shape
+    NB, Hkv, B, _ = kc_h.shape
+    W = tables_h.shape[1]
+    mcl = W * B
+    q = torch.from_numpy(case.q).to(dev)
+    kc, vc = torch.from_numpy(kc_h).to(dev), torch.from_numpy(vc_h).to(dev)
+    tables, lens = torch.from_numpy(tables_h).to(dev), torch.from_numpy(lens_h).to(dev)
+    need = pa.pa_decode_workspace_size(S, H, Hkv, D, B, mcl, P)
+    assert 0 < need <= SCRATCH_BYTES
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    want = torch.full((S, H, D), float("nan"), dtype=torch.float16, device=dev)
+    pa.pa_decode(want, q, kc, vc, tables, lens, case.scale, B, max_context_len=mcl, partition_size=P, workspace=ws)
+    got = torch.full((S, H, D), float("nan"), dtype=torch.float16, device=dev)
+    rc = _c_call()(got.data_ptr(), q.data_ptr(), kc.data_ptr(), vc.data_ptr(), tables.data_ptr(), W,
+                   lens.data_ptr(), S, H, Hkv, D, B, NB, case.scale, mcl, P, None, pa.PA_DTYPE_F16,
+                   torch.cuda.current_stream(dev).cuda_stream)
+    assert rc == pa.PA_OK, pa.last_error()
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(got), bits(want)), "pa_decode_noalloc differs from pa_decode"
+    ref = oracle.decode(case.q, kc_h, vc_h, tables_h, lens_h, case.scale)
+    assert_attention_close(got, ref, f"noalloc S={S} H={H}/{Hkv} P={P}")
+    return need
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("H,Hkv", [(8, 8), (16, 2)])
+def test_noalloc_matches_pa_decode_twice_second_smaller(H, Hkv):
+    dev = device()
+    rng = np.random.default_rng(H * 100 + Hkv)
+    big = workloads.random_case(40 + H, rng.integers(1, 1500, size=40).tolist(), H, Hkv, 128, 16)
+    small = workloads.random_case(41 + H, [1, 300, 700, 17, 1024], H, Hkv, 128, 16)
+    n1 = _run(dev, big, 256)
+    n2 = _run(dev, small, 256)
+    say(f"  workspace used: {n1} then {n2} bytes of {SCRATCH_BYTES}")
+    assert n2 < n1
+
+
+@pytest.mark.gpu
+def test_noalloc_binding_and_order_given():
+    """The Python binding (no workspace argument) and a caller's dispatch
+    order: same bits as pa_decode."""
+    dev = device()
+    case = workloads.random_case(77, [5, 900, 2000, 64, 1], 4, 4, 64, 8)
+    kc_h, vc_h, tables_h, lens_h = _oracle_cache(case)
+    q = torch.from_numpy(case.q).to(dev)
+    kc, vc = torch.from_numpy(kc_h).to(dev), torch.from_numpy(vc_h).to(dev)
+    tables, lens = torch.from_numpy(tables_h).to(dev), torch.from_numpy(lens_h).to(dev)
+    mcl = tables.shape[1] * 8
+    order = pa.pa_decode_order(lens, mcl)
+    want = torch.empty_like(q)
+    pa.pa_decode(want, q, kc, vc, tables, lens, case.scale, 8, partition_size=128, seq_order=order)
+    got = torch.empty_like(q)
+    pa.pa_decode_noalloc(got, q, kc, vc, tables, lens, case.scale, 8, partition_size=128, seq_order=order)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(got), bits(want))
+
+
+def test_noalloc_refuses_sizes_beyond_its_array():
+    """Checked on the host before any device work (no GPU needed): a batch
+    whose partial states exceed the array is PA_ERR_INVALID with a message."""
+    f = _c_call()
+    rc = f(16, 16, 16, 16, 16, 4096, 16, 4096, 64, 64, 128, 16, 1 << 20, 0.1, 65536, 128, None,
+           pa.PA_DTYPE_F16, None)
+    assert rc == pa.PA_ERR_INVALID
+    assert "scratch" in pa.last_error()
