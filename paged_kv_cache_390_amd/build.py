@@ -17,7 +17,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpa.so")
 
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
-HIP_SOURCES = ["decode.hip", "decode_gqa.hip", "prefill.hip", "cache_ops.hip", "bench_read.hip"]
+HIP_SOURCES = ["decode.hip", "decode_gqa.hip", "prefill.hip", "cache_ops.hip", "bench_read.hip", "validate.hip"]
 CXX_SOURCES = ["block_manager.cpp", "status.cpp"]
 
 HIPCC_FLAGS = [

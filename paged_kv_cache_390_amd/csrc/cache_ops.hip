@@ -187,6 +187,8 @@ extern "C" int pa_reshape_and_cache(const void* key, const void* value, int64_t 
     const int32_t chunk_shift = __builtin_ctz((unsigned)(head_dim / vecw));   // head_dim / vecw: a power of two
     const int32_t block_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
     const int64_t pool_slots = (int64_t)num_blocks * block_size;
+    if (pa::validate_enabled())
+        if (int rc = pa::validate_slots("pa_reshape_and_cache", slot_mapping, num_tokens, pool_slots, stream)) return rc;
     auto st = static_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)num_tokens, (unsigned)groups);
     if (vec)
@@ -224,6 +226,10 @@ extern "C" int pa_copy_blocks(void* const* k_caches, void* const* v_caches, int3
         src.push_back(v_caches[l]);
         dst.push_back(v_caches[l]);
     }
+    if (pa::validate_enabled())
+        if (int rc = pa::validate_pairs("pa_copy_blocks", src_dst_pairs, num_pairs, num_blocks, num_blocks, true,
+                                        stream))
+            return rc;
     return launch_block_copies(src, dst, src_dst_pairs, num_pairs, num_blocks, num_blocks, block_elems, vec,
                                static_cast<hipStream_t>(stream), "pa_copy_blocks");
 }
@@ -258,6 +264,8 @@ extern "C" int pa_swap_blocks(void* const* dev_caches, void* const* host_caches,
     }
     const int64_t src_nb = direction == PA_SWAP_OUT ? dev_num_blocks : host_num_blocks;
     const int64_t dst_nb = direction == PA_SWAP_OUT ? host_num_blocks : dev_num_blocks;
+    if (pa::validate_enabled())
+        if (int rc = pa::validate_pairs("pa_swap_blocks", pairs, num_pairs, src_nb, dst_nb, false, stream)) return rc;
     return launch_block_copies(src, dst, pairs, num_pairs, src_nb, dst_nb, block_elems, vec,
                                static_cast<hipStream_t>(stream), "pa_swap_blocks");
 }

@@ -723,6 +723,11 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
     if ((int64_t)L.num_parts * p < len_cap) len_cap = (int64_t)L.num_parts * p;
     if ((int64_t)max_context_len < len_cap) len_cap = max_context_len;
 
+    if (pa::validate_enabled())
+        if (int rc = pa::validate_tables(fn, block_tables, max_blocks_per_seq, context_lens, num_seqs, block_size,
+                                         num_blocks, max_context_len, stream))
+            return rc;
+
     char* wsb = static_cast<char*>(workspace);
     int32_t* own_order = compute_order ? reinterpret_cast<int32_t*>(wsb) : nullptr;
     const int32_t* order = seq_order ? seq_order : own_order;

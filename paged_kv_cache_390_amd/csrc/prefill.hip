@@ -843,6 +843,13 @@ int prefill_impl(const char* fn, void* out, const void* q, int32_t num_tokens, c
         return pa::fail(PA_ERR_INVALID, "%s: max_query_len %d x %lld heads needs %lld row tiles (limit 65535)",
                         fn, max_query_len, (long long)g, (long long)row_tiles);
     const int64_t len_cap = (int64_t)max_blocks_per_seq * block_size;
+    if (pa::validate_enabled()) {
+        if (int rc = pa::validate_queries(fn, query_start, num_seqs, num_tokens, context_lens, max_query_len, stream))
+            return rc;
+        if (int rc = pa::validate_tables(fn, block_tables, max_blocks_per_seq, context_lens, num_seqs, block_size,
+                                         num_blocks, len_cap, stream))
+            return rc;
+    }
     SplitPlan P = split_plan(num_tokens, num_seqs, num_heads, num_kv_heads, len_cap, max_query_len);
     if (P.num_parts > 1 && (!workspace || workspace_bytes < P.total)) {
         // no room for the partial states: one part per row tile

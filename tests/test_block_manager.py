@@ -170,3 +170,64 @@ def test_get_tables_pads_and_checks_width():
     assert t[0].tolist() == [bm.table(3)[0], -1, -1, -1]
     with pytest.raises(pa.PAError):
         bm.get_tables([7], 2)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_cow_pairs_of_a_batch_meet_the_copy_rule(seed):
+    """pa_copy_blocks copies all pairs of one call at once, so within one
+    call destinations must be distinct and never also a source (a source may
+    repeat).  The pairs one batched append produces always meet that: a
+    destination is a block just taken off the free list, held by its writer
+    alone, and a source keeps a holder after the copy, so it is not freed
+    and cannot come back as a later destination (lpnh.cn/news/2758356 4.2,
+    third step).  Checked over random forests of forks sharing partly
+    filled tails, with every batch compared against the model."""
+    rng = np.random.default_rng(seed)
+    B = int(rng.choice([2, 4, 16]))
+    bm = pa.BlockManager(400, B)
+    m = BlockManagerModel(400, B)
+    seqs = []
+    nid = 0
+    total_pairs = 0
+    for _ in range(60):
+        r = rng.random()
+        if r < 0.25 or not seqs:
+            n = int(rng.integers(1, 5 * B))
+            try:
+                m.add_sequence(nid, n)
+            except OOM:
+                continue
+            bm.add_sequence(nid, n)
+            seqs.append(nid)
+            nid += 1
+        elif r < 0.6:
+            for _ in range(int(rng.integers(1, 4))):
+                p = int(rng.choice(seqs))
+                m.fork(p, nid)
+                bm.fork(p, nid)
+                seqs.append(nid)
+                nid += 1
+        else:
+            batch = [int(x) for x in rng.choice(seqs, size=min(len(seqs), int(rng.integers(1, 12))), replace=False)]
+            want = []
+            done = 0
+            for s in batch:
+                try:
+                    want.append(m.append_token(s))
+                    done += 1
+                except OOM:
+                    break
+            try:
+                slots, pairs = bm.append_tokens(batch)
+            except pa.OutOfBlocks:
+                assert done < len(batch)
+                _same_state(bm, m)
+                continue
+            assert slots.tolist() == [w[0] for w in want]
+            assert [tuple(p) for p in pairs.tolist()] == [w[1] for w in want if w[1]]
+            src, dst = pairs[:, 0].tolist(), pairs[:, 1].tolist()
+            assert len(set(dst)) == len(dst), "two pairs copy onto one block"
+            assert not set(dst) & set(src), "a destination is also a source"
+            total_pairs += len(pairs)
+        _same_state(bm, m)
+    assert total_pairs > 0
