@@ -69,6 +69,8 @@ def parse():
     p.add_argument("--layers", type=int, default=32)
     p.add_argument("--batch", type=int, default=0, help="sequences (0: 64 for llama7b, 256 for gqa)")
     p.add_argument("--block-size", type=int, default=16)
+    p.add_argument("--head-dim", type=int, default=128,
+                   help="gqa, prefill: head_dim of the batch (64/128/256)")
     p.add_argument("--partition", type=int, default=0, help="decode partition size (0 = library default)")
     p.add_argument("--fused", type=int, default=1,
                    help="decode workloads: 1 writes the new K/V inside the decode call (pa_decode_append), "
@@ -80,8 +82,9 @@ def parse():
     return p.parse_args()
 
 
-KERNEL_SOURCES = {"llama7b": ("decode.hip",), "gqa": ("decode.hip", "decode_gqa.hip", "mfma_tile.h"),
-                  "prefill": ("prefill.hip", "mfma_tile.h")}
+KERNEL_SOURCES = {"llama7b": ("decode.hip",), "gqa": ("decode.hip", "decode_gqa.hip"),
+                  "gqa_d64": ("decode.hip", "decode_gqa.hip"), "gqa_d256": ("decode.hip", "decode_gqa.hip"),
+                  "prefill": ("prefill.hip",)}
 
 
 def code_tokens(text: str) -> str:
@@ -291,8 +294,8 @@ def main():
         wl_name = "llama2-7b-decode"
         ctx_desc = "U[1,2048]"
     elif args.workload == "gqa":
-        w = workloads.gqa_decode(seed=args.seed, num_seqs=args.batch or 256, block_size=B)
-        wl_name = "gqa-64q-8kv-decode"
+        w = workloads.gqa_decode(seed=args.seed, num_seqs=args.batch or 256, block_size=B, head_dim=args.head_dim)
+        wl_name = "gqa-64q-8kv-decode" if args.head_dim == 128 else f"gqa-64q-8kv-d{args.head_dim}-decode"
         ctx_desc = "U[1,2048]"
     else:
         w = workloads.long_context(seed=args.seed, num_seqs=16, block_size=B,
@@ -375,8 +378,9 @@ def main():
                 decode_call(l)
         return ctx
 
+    all_ctx = 0                              # cached tokens over every decode call of the run
     for i in range(W):
-        step(i)
+        all_ctx += step(i) * L
     torch.cuda.synchronize()
 
     ctx_sum = 0
@@ -386,6 +390,7 @@ def main():
     for i in range(K):
         ctx_last = step(W + i)
         ctx_sum += ctx_last
+        all_ctx += ctx_last * L
     torch.cuda.synchronize()
     t1 = time.perf_counter()
 
@@ -406,6 +411,7 @@ def main():
         sweep_ev[i + 1].record(stream)
     torch.cuda.synchronize()
     dec_ms = [sweep_ev[i].elapsed_time(sweep_ev[i + 1]) / L for i in range(K)]
+    all_ctx += ctx_last * L * K
     dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
     kv_per_launch = ctx_last * kv_per_token
     achieved = kv_per_launch / dec_avg_s / 1e9
@@ -450,7 +456,8 @@ def main():
         log(f"[bench] tiny case: pa_decode {tiny['gpu_us']['median']} us (median, launch included), oracle "
             f"{tiny['oracle_us_1_thread']['median']} us on 1 thread")
 
-    traffic = traffic_fields(args.workload)
+    traffic = traffic_fields(args.workload if args.workload != "gqa" or args.head_dim == 128
+                             else f"gqa_d{args.head_dim}")
     line = {
         "metric": "paged-decode achieved KV GB/s (% of HBM peak) + tokens/s per layer, bs=16",
         "value": round(value, 2),
@@ -480,6 +487,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), **traffic,
                      "kernel": "decode call (partition kernel + merge kernel when a context is split)",
                      "algorithmic_bytes_per_call": kv_per_launch, "cached_tokens_per_call": ctx_last},
+        "decode_calls": {"count": (W + 2 * K) * L, "cached_tokens_total": all_ctx},
         "cpu_baseline": cpu,
         "tiny_latency": tiny,
     }
@@ -728,7 +736,7 @@ def prefill_bench(args, dev):
     import workloads
 
     L = args.layers if args.layers != 32 else 4
-    S, H, Hkv, D, B = 32, 32, 32, 128, args.block_size
+    S, H, Hkv, D, B = 32, 32, 32, args.head_dim, args.block_size
     sw = workloads.block_size_sweep(seed=args.seed, num_seqs=S, gen_max=1)
     lens_l = [int(n) - 1 for n in sw.lens]                 # the prompt part only
     T = int(sum(lens_l))
@@ -814,7 +822,7 @@ def prefill_bench(args, dev):
                       "dtype": "f16",
                       "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_F16_PEAK_TFLOPS,
                                    "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4),
-                                   "traffic": traffic_from_profiles("prefill")},
+                                   "traffic": traffic_from_profiles("prefill") if D == 128 else None},
                       "config": {"workload": "prefill", "prompts": S, "tokens": T, "max_prompt": mq,
                                  "num_heads": H, "num_kv_heads": Hkv, "head_dim": D, "block_size": B,
                                  "layers_resident": L}}), flush=True)
@@ -1098,10 +1106,13 @@ def read_bench(args, dev):
     like the decode call: a plain contiguous read of a 4 GiB buffer, one MiB
     per workgroup; and the Llama-2-7B decode batch's access pattern -- the K
     and V slabs of every block of every (sequence, KV head), scattered by the
-    tables -- over --layers resident layers, with no arithmetic.  Beside them
-    pa_decode on the same batch and layers (default partition, longest-first
-    order computed once).  Each is timed with HIP events around --steps
-    sweeps; GB/s from the median sweep."""
+    tables -- over --layers resident layers, with no arithmetic, on two
+    batches: every context at 2048 tokens (the pattern's own ceiling: equal
+    workgroups, all resident at once) and contexts U[1, 2048] (the headline
+    batch, in index order).  Beside each, pa_decode on the same batch and
+    layers (default partition, longest-first order computed once).  Each is
+    timed with HIP events around --steps sweeps; GB/s from the median
+    sweep."""
     import numpy as np
     import torch
 
@@ -1109,24 +1120,12 @@ def read_bench(args, dev):
     import workloads
 
     B, L = args.block_size, args.layers
-    w = workloads.llama7b_decode(seed=args.seed, num_seqs=args.batch or 64, block_size=B)
-    S, H, Hkv, D, NB = len(w.lens), w.num_heads, w.num_kv_heads, w.head_dim, w.num_blocks
-    pools = [w.pool(l, dev) for l in range(L)]
-    tables = torch.from_numpy(np.ascontiguousarray(w.perm_tables)).to(dev)
-    lens = torch.from_numpy(w.lens).to(dev)
-    width = tables.shape[1]
-    q, _, _ = w.new_tokens(0, dev)
-    out = torch.empty_like(q)
-    ws = torch.empty(max(1, pa.pa_decode_workspace_size(S, H, Hkv, D, B, width * B, 0)), dtype=torch.uint8,
-                     device=dev)
-    order = pa.pa_decode_order(lens, width * B)
-    sink = torch.empty(S * Hkv, dtype=torch.int32, device=dev)
-    buf = torch.zeros(4 << 30, dtype=torch.uint8, device=dev)
-    bsink = torch.empty(max(1, buf.numel() >> 20), dtype=torch.int32, device=dev)
+    S0 = args.batch or 64
+    mixed = workloads.llama7b_decode(seed=args.seed, num_seqs=S0, block_size=B)
+    uniform = workloads.llama7b_decode(seed=args.seed, num_seqs=S0, block_size=B, min_len=2048)
+    H, Hkv, D, NB = mixed.num_heads, mixed.num_kv_heads, mixed.head_dim, mixed.num_blocks
+    pools = [mixed.pool(l, dev) for l in range(L)]
     kv_tok = 2 * Hkv * D * 2
-    n = w.lens.astype(np.int64)
-    decode_bytes = int(n.sum()) * kv_tok
-    block_bytes = int((-(-n // B) * B).sum()) * kv_tok
 
     def sweeps(call, per_sweep):
         for _ in range(max(args.warmup, 3)):
@@ -1142,27 +1141,47 @@ def read_bench(args, dev):
         torch.cuda.synchronize()
         return [ev[i].elapsed_time(ev[i + 1]) / 1e3 / per_sweep for i in range(args.steps)]
 
+    def entry(nbytes, t):
+        return {"bytes_per_call": nbytes, "us_per_call": stats_of(t, 1e6, 2),
+                "GB_s": round(nbytes / statistics.median(t) / 1e9, 2)}
+
     res = {}
-    t = sweeps(lambda l: pa.pa_bench_stream_read(buf, bsink), 1)
-    res["contiguous_read"] = {"bytes_per_call": buf.numel(), "us_per_call": stats_of(t, 1e6, 2),
-                              "GB_s": round(buf.numel() / statistics.median(t) / 1e9, 2)}
-    t = sweeps(lambda l: pa.pa_bench_block_read(pools[l][0], pools[l][1], tables, lens, sink), L)
-    res["block_pattern_read"] = {"bytes_per_call": block_bytes, "us_per_call": stats_of(t, 1e6, 2),
-                                 "GB_s": round(block_bytes / statistics.median(t) / 1e9, 2)}
-    t = sweeps(lambda l: pa.pa_decode(out, q, pools[l][0], pools[l][1], tables, lens, w.scale, B,
-                                      max_context_len=width * B, workspace=ws, seq_order=order), L)
-    res["decode"] = {"bytes_per_call": decode_bytes, "us_per_call": stats_of(t, 1e6, 2),
-                     "GB_s": round(decode_bytes / statistics.median(t) / 1e9, 2)}
+    buf = torch.zeros(4 << 30, dtype=torch.uint8, device=dev)
+    bsink = torch.empty(max(1, buf.numel() >> 20), dtype=torch.int32, device=dev)
+    res["contiguous_read"] = entry(buf.numel(), sweeps(lambda l: pa.pa_bench_stream_read(buf, bsink), 1))
+    del buf
+    for name, w in (("uniform_2048", uniform), ("mixed_U1_2048", mixed)):
+        S = len(w.lens)
+        tables = torch.from_numpy(np.ascontiguousarray(w.perm_tables)).to(dev)
+        lens = torch.from_numpy(w.lens).to(dev)
+        width = tables.shape[1]
+        q, _, _ = w.new_tokens(0, dev)
+        out = torch.empty_like(q)
+        ws = torch.empty(max(1, pa.pa_decode_workspace_size(S, H, Hkv, D, B, width * B, 0)), dtype=torch.uint8,
+                         device=dev)
+        order = pa.pa_decode_order(lens, width * B)
+        sink = torch.empty(S * Hkv, dtype=torch.int32, device=dev)
+        n = w.lens.astype(np.int64)
+        res[f"block_pattern_read_{name}"] = entry(
+            int((-(-n // B) * B).sum()) * kv_tok,
+            sweeps(lambda l: pa.pa_bench_block_read(pools[l][0], pools[l][1], tables, lens, sink), L))
+        res[f"decode_{name}"] = entry(
+            int(n.sum()) * kv_tok,
+            sweeps(lambda l: pa.pa_decode(out, q, pools[l][0], pools[l][1], tables, lens, w.scale, B,
+                                          max_context_len=width * B, workspace=ws, seq_order=order), L))
     for k, r in res.items():
         log(f"[bench] {k}: {r['us_per_call']['median']} us per call (median) = {r['GB_s']} GB/s "
             f"({100 * r['GB_s'] / HBM_PEAK_GBS:.1f}% of peak)")
+    ceiling = res["block_pattern_read_uniform_2048"]["GB_s"]
     print(json.dumps({"metric": "read-only streaming GB/s (same-chip ceiling for paged decode)",
-                      "value": res["block_pattern_read"]["GB_s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+                      "value": ceiling, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
                       "warmup": args.warmup, "higher_is_better": True, "dtype": "f16", "data": "synthetic",
                       "reads": res,
-                      "decode_over_block_read": round(res["decode"]["GB_s"] / res["block_pattern_read"]["GB_s"], 4),
-                      "config": {"workload": "read-ceiling", "batch": S, "block_size": B, "num_kv_heads": Hkv,
-                                 "head_dim": D, "context": "U[1,2048]", "layers_resident": L}}), flush=True)
+                      "decode_over_block_read": {
+                          k: round(res[f"decode_{k}"]["GB_s"] / res[f"block_pattern_read_{k}"]["GB_s"], 4)
+                          for k in ("uniform_2048", "mixed_U1_2048")},
+                      "config": {"workload": "read-ceiling", "batch": S0, "block_size": B, "num_kv_heads": Hkv,
+                                 "head_dim": D, "layers_resident": L}}), flush=True)
 
 
 def tiny_bench(args, dev):

@@ -31,7 +31,7 @@
  *     kernels skip any that fall outside the pool, so a bad index is never
  *     dereferenced (see each call for what the output then holds).
  *   - dtype: PA_DTYPE_F16 is the only element type.
- *   - head_dim in {16, 32, 64, 128, 256} (pa_prefill: 128); the attention
+ *   - head_dim in {16, 32, 64, 128, 256} (pa_prefill: 64, 128, 256); the attention
  *     calls take block_size in {1, 2, 4, 8, 16, 32, 64, 128}
  *     (PA_ERR_UNSUPPORTED otherwise); pa_reshape_and_cache and the block
  *     copies take any block size.
@@ -111,10 +111,10 @@ int pa_reshape_and_cache(const void *key, const void *value,
  *                  the token just written.  n == 0 gives an all-zero row.
  *   num_heads      query heads; num_heads % num_kv_heads == 0 and query head
  *                  h reads KV head h / (num_heads / num_kv_heads).  When 2 to
- *                  16 query heads share a KV head and head_dim is 128, the
- *                  products run on the matrix cores (one workgroup reads each
- *                  K/V block once for the whole group); otherwise on the
- *                  vector ALUs, one workgroup per query head.
+ *                  16 query heads share a KV head and head_dim is 64, 128 or
+ *                  256, the products run on the matrix cores (one workgroup
+ *                  reads each K/V block once for the whole group); otherwise
+ *                  on the vector ALUs, one workgroup per query head.
  *   scale          multiplies q.k (1/sqrt(head_dim) in the usual model)
  *   max_context_len  host-known upper bound on every n; it sizes the grid so
  *                  that no device-to-host read is needed.  A row whose n
@@ -259,9 +259,9 @@ int pa_decode_order(int32_t *seq_order, const int32_t *context_lens,
  *                  second kernel; without it (NULL or smaller) the context
  *                  is not split.  Contents on entry are ignored; calls
  *                  sharing a workspace must be stream-ordered.
- * head_dim 128 only (PA_ERR_UNSUPPORTED otherwise); any num_heads multiple of
- * num_kv_heads.  Runs on the matrix cores (v_mfma_f32_16x16x32_f16, fp32
- * accumulation).
+ * head_dim 64, 128 or 256 (PA_ERR_UNSUPPORTED otherwise); any num_heads
+ * multiple of num_kv_heads.  Runs on the matrix cores
+ * (v_mfma_f32_16x16x32_f16, fp32 accumulation).
  * ------------------------------------------------------------------------ */
 int pa_prefill(void *out, const void *q, int32_t num_tokens,
                const void *k_cache, const void *v_cache,

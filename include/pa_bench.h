@@ -33,7 +33,10 @@ int pa_bench_stream_read(const void *buf, size_t bytes, uint32_t *sink,
 /* The decode access pattern without its arithmetic: for every sequence s
  * and KV head h, the K and V slabs (block_size x head_dim fp16) of blocks
  * block_tables[s][0 .. ceil(context_lens[s] / block_size) - 1], whole
- * blocks, in table order.  Arguments as for pa_decode; an id outside
+ * blocks, in table order, on the decode kernel's schedule (1 KiB wave
+ * loads, 4 K + 4 V loads per wave step, two steps in flight).  Arguments as
+ * for pa_decode; a slab (block_size * head_dim * 2 bytes) must be a power
+ * of two of at least 1 KiB; an id outside
  * [0, num_blocks) reads block 0.  `sink` receives num_seqs * num_kv_heads
  * words. */
 int pa_bench_block_read(const void *k_cache, const void *v_cache,

@@ -749,7 +749,7 @@ int decode_impl(const char* fn, void* out, const void* q, const void* k_cache, c
         pa::DecodeLaunch a{static_cast<_Float16*>(out), ws_ml, ws_acc, order, static_cast<const _Float16*>(q),
                            static_cast<const _Float16*>(k_cache), static_cast<const _Float16*>(v_cache),
                            block_tables, max_blocks_per_seq, context_lens, num_seqs, num_heads, num_kv_heads,
-                           num_blocks, block_size, scale_log2, p, L.num_parts, len_cap, st,
+                           num_blocks, block_size, head_dim, scale_log2, p, L.num_parts, len_cap, st,
                            app ? app->key : nullptr, app ? app->value : nullptr, app ? app->stride : 0};
         e = pa::launch_gqa_mfma(a);
     } else {

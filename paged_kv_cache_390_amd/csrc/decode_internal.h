@@ -28,6 +28,7 @@ struct DecodeLaunch {
     int32_t num_kv_heads;
     int32_t num_blocks;
     int32_t block_size;
+    int32_t head_dim;
     float scale_log2;
     int32_t part_size;
     int32_t num_parts;
@@ -41,7 +42,7 @@ struct DecodeLaunch {
     int64_t new_stride;
 };
 
-// Grouped-query decode on the matrix cores: head_dim 128, 2 <= group <= 16.
+// Grouped-query decode on the matrix cores: head_dim 64, 128 or 256, 2 <= group <= 16.
 bool gqa_mfma_supported(int32_t head_dim, int32_t block_size, int32_t group);
 hipError_t launch_gqa_mfma(const DecodeLaunch& a);
 

@@ -58,43 +58,94 @@
 #include <cmath>
 #include <cstdint>
 
-#include "mfma_tile.h"
 #include "pa.h"
 #include "pa_internal.h"
 
 namespace {
 
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kNT = 2;                     // 16-row groups per wave (the N side of its MFMA tiles)
-constexpr int kRowsPerWave = 16 * kNT;
-constexpr int kRowsPerGroup = kWaves * kRowsPerWave;
 constexpr double kLog2e = 1.4426950408889634073599246810019;
 
-// One K/V tile in LDS: kKvTile token rows of K and of V, 256 bytes each with
-// their 16-byte chunks permuted per row (see fetch_tile), plus a flag per
-// token (inside the context and the pool) in an array of its own.
-constexpr int kKvTile = 64;
-constexpr int kPitch = kD * 2;                // K rows (16-byte chunks XOR-swizzled by row & 15)
-constexpr int kPitchV = kD * 2;               // V rows (chunks swizzled by 2 * (row & 3))
-constexpr int kTileBytes = kKvTile * kPitch;
-constexpr int kTileBytesV = kKvTile * kPitchV;
-constexpr int kBufBytes = kTileBytes + kTileBytesV;
+// Geometry per head_dim D (64, 128 or 256).
+//  * A K/V tile in LDS: kKvTile token rows of K and of V, 2D bytes each with
+//    their 16-byte chunks permuted per row (see fetch_tile), plus a flag per
+//    token (inside the context and the pool) in an array of its own; two such
+//    buffers per workgroup (32 KiB each at D <= 128 with 64-token tiles; at
+//    D = 256, 32-token tiles keep a buffer at 32 KiB).
+//  * kNT 16-row groups per wave -- the N side of its MFMA tiles, each K or V
+//    operand read from LDS feeding kNT products; one at D = 256, whose O
+//    and Q^T alone would fill the registers of two.
+//  * One thread's share of a K/V tile in flight: kStageRows token rows whose
+//    16 bytes at LDS position l % kChunks it loads.  Thread (wave w, lane l)
+//    stages rows kRowsPerLoad*w + l/kChunks + 4*kRowsPerLoad*i, i <
+//    kStageRows: a wave's rows for one i are kRowsPerLoad consecutive
+//    tokens starting at a multiple of kRowsPerLoad, so with blocks of at
+//    least kRowsPerLoad tokens they share one table entry, read with a
+//    scalar load.
+template <int D>
+struct PGeo {
+    static constexpr int kChunks = D / 8;                      // 16-byte chunks per row
+    static constexpr int kKvTile = D >= 256 ? 32 : 64;         // tokens per LDS tile
+    static constexpr int kNT = D >= 256 ? 1 : 2;
+    static constexpr int kRowsPerWave = 16 * kNT;
+    static constexpr int kRowsPerGroup = kWaves * kRowsPerWave;
+    static constexpr int kPitch = D * 2;                       // K rows (chunks XOR-swizzled by row & kSwzK)
+    static constexpr int kPitchV = D * 2;                      // V rows (chunks swizzled by 2 * (row & 3))
+    static constexpr int kTileBytes = kKvTile * kPitch;
+    static constexpr int kTileBytesV = kKvTile * kPitchV;
+    static constexpr int kBufBytes = kTileBytes + kTileBytesV;
+    static constexpr int kRowsPerLoad = 64 / kChunks;          // rows one wave load stages
+    static constexpr int kStageRows = kKvTile * kChunks / kThreads;
+    static constexpr int kSwzK = kChunks < 16 ? kChunks - 1 : 15;
+    static constexpr int kQk = D / 32;                         // QK MFMAs (k = 32) per 16 tokens
+    static constexpr int kDTiles = D / 16;                     // PV d-tiles (16 output columns each)
+    static_assert(kStageRows >= 1 && kKvTile * kChunks == kStageRows * kThreads, "tile rows must split evenly");
+    static_assert(kKvTile % 32 == 0 && kDTiles % 4 == 0, "whole PV slabs and d-tile groups");
+};
+
+// The geometry of PGeo<D> under short names inside a kernel or helper.
+#define PF_GEO(D)                                                   \
+    using PG_ = PGeo<D>;                                            \
+    constexpr int kD = D;                                           \
+    constexpr int kChunks = PG_::kChunks;                           \
+    constexpr int kKvTile = PG_::kKvTile;                           \
+    constexpr int kNT = PG_::kNT;                                   \
+    constexpr int kRowsPerWave = PG_::kRowsPerWave;                 \
+    constexpr int kRowsPerGroup = PG_::kRowsPerGroup;               \
+    constexpr int kPitch = PG_::kPitch;                             \
+    constexpr int kPitchV = PG_::kPitchV;                           \
+    constexpr int kTileBytes = PG_::kTileBytes;                     \
+    constexpr int kBufBytes = PG_::kBufBytes;                       \
+    constexpr int kRowsPerLoad = PG_::kRowsPerLoad;                 \
+    constexpr int kStageRows = PG_::kStageRows;                     \
+    constexpr int kSwzK = PG_::kSwzK;                               \
+    constexpr int kQk = PG_::kQk;                                   \
+    constexpr int kDTiles = PG_::kDTiles;                           \
+    (void)kD; (void)kChunks; (void)kKvTile; (void)kNT; (void)kRowsPerWave; (void)kRowsPerGroup; (void)kPitch; \
+    (void)kPitchV; (void)kTileBytes; (void)kBufBytes; (void)kRowsPerLoad; (void)kStageRows; (void)kSwzK; \
+    (void)kQk; (void)kDTiles
 
 typedef _Float16 half8_t_ __attribute__((ext_vector_type(8)));
 
-// One thread's share of a K/V tile in flight: the validity of the
-// kStageRows token rows whose 16 bytes at LDS position l%16 it loads.
-// Thread (wave w, lane l) stages rows 4w + l/16 + (kThreads/16)*i, i <
-// kStageRows: a wave's rows for one i are 4 consecutive tokens starting at a
-// multiple of 4, so with blocks of 4 or more tokens they share one table
-// entry, read with a scalar load.
-constexpr int kStageRows = kKvTile * 16 / kThreads;
-static_assert(kStageRows >= 1 && kKvTile * 16 == kStageRows * kThreads, "tile rows must split evenly");
+// The online-softmax state of a lane for one 16-row group: the running max
+// and sum of its row and its share of the unnormalised output rows.
+template <int D>
+struct Softmax {
+    float m, l;                            // running max (base 2) and sum of row l % 16
+    float4_t o[D / 16];                    // O[row 4*(l/16) + i][d = 16c + l % 16] in o[c][i]
+};
 
+template <int D>
 struct Staged {
-    bool ok[kStageRows];
-    int32_t wphys[kStageRows];   // append mode: the block this thread writes the row into, or -1
+    bool ok[PGeo<D>::kStageRows];
+    int32_t wphys[PGeo<D>::kStageRows];   // append mode: the block this thread writes the row into, or -1
 };
 
 // Append mode: the m new tokens of the sequence (positions base_pos ..
@@ -116,30 +167,33 @@ struct AppendSrc {
 #define PA_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8))
 
 // First token of the wave's stage row i of tile k.
+template <int D>
 __device__ __forceinline__ int stage_token0(int k, int wave, int i) {
-    return k * kKvTile + 4 * wave + (kThreads / 16) * i;
+    constexpr int R = PGeo<D>::kRowsPerLoad;
+    return k * PGeo<D>::kKvTile + R * wave + (kWaves * R) * i;
 }
 
-// Table entries of the wave's stage rows of tile k (B >= 4: one per row,
-// uniform over the wave); tokens past the context read the last token's
-// entry and are masked.
-template <int B>
-__device__ __forceinline__ void table_entries(int32_t (&e)[kStageRows], int k, int wave, int n,
+// Table entries of the wave's stage rows of tile k (B >= kRowsPerLoad: one
+// per row, uniform over the wave); tokens past the context read the last
+// token's entry and are masked.
+template <int D, int B>
+__device__ __forceinline__ void table_entries(int32_t (&e)[PGeo<D>::kStageRows], int k, int wave, int n,
                                               const int32_t* __restrict__ trow) {
 #pragma unroll
-    for (int i = 0; i < kStageRows; ++i) {
-        const int t = stage_token0(k, wave, i);
+    for (int i = 0; i < PGeo<D>::kStageRows; ++i) {
+        const int t = stage_token0<D>(k, wave, i);
         e[i] = trow[(t < n ? t : n - 1) / B];
     }
 }
 
-// Fetch tile k (tokens 64k .. 64k+63) from HBM into the LDS buffer `buf`;
-// `e` holds its table entries when B >= 4 (read a step earlier), else every
-// thread looks up its own row.  Rows past the context or with an id outside
+// Fetch tile k (tokens kKvTile*k ..) from HBM into the LDS buffer `buf`;
+// `e` holds its table entries when B >= kRowsPerLoad (read a step earlier),
+// else every thread looks up its own row.  Rows past the context or with an id outside
 // the pool read a row of some valid block (a fixed number of loads per
 // tile) and are zeroed by finish_tile.
-template <int B, bool kStream, bool kAppend>
-__device__ __forceinline__ void fetch_tile(Staged& st, unsigned char* buf, int k, const int32_t (&e)[kStageRows], int wave, int lane,
+template <int D, int B, bool kStream, bool kAppend>
+__device__ __forceinline__ void fetch_tile(Staged<D>& st, unsigned char* buf, int k,
+                                           const int32_t (&e)[PGeo<D>::kStageRows], int wave, int lane,
                                            int n, const int32_t* __restrict__ trow,
                                            const _Float16* __restrict__ kbase, const _Float16* __restrict__ vbase,
                                            int64_t blk_stride, int32_t num_blocks, const AppendSrc& ap) {
@@ -148,18 +202,19 @@ __device__ __forceinline__ void fetch_tile(Staged& st, unsigned char* buf, int k
     // bit of the cache policy); otherwise later row tiles of the sequence
     // re-read the tile and the default policy keeps it for them
     constexpr int kLoadPolicy = kStream ? 2 : 0;
-    const int col = lane & 15;
+    PF_GEO(D);
+    const int col = lane % kChunks;
 #pragma unroll
     for (int i = 0; i < kStageRows; ++i) {
-        const int t0 = stage_token0(k, wave, i);           // uniform, a multiple of 4
-        const int t = t0 + (lane >> 4);
+        const int t0 = stage_token0<D>(k, wave, i);        // uniform, a multiple of kRowsPerLoad
+        const int t = t0 + lane / kChunks;
         int32_t phys;
         int row;                                           // row inside the block
-        if constexpr (B >= 4) {
-            // the wave's 4 rows share entry e[i] (of token min(t0, n-1)) and
-            // lie at t0 % B + 0..3 of a block -- inside it also past the context
+        if constexpr (B >= kRowsPerLoad) {
+            // the wave's rows share entry e[i] (of token min(t0, n-1)) and
+            // lie at t0 % B + 0.. of a block -- inside it also past the context
             phys = e[i];
-            row = t0 % B + (lane >> 4);
+            row = t0 % B + lane / kChunks;
         } else {
             const int tc = t < n ? t : n - 1;
             phys = trow[tc / B];
@@ -167,14 +222,14 @@ __device__ __forceinline__ void fetch_tile(Staged& st, unsigned char* buf, int k
         }
         const bool in_pool = (uint32_t)phys < (uint32_t)num_blocks;
         const bool ok = t < n && in_pool;
-        // LDS row r = stage row, position col holds chunk col ^ (r & 15) of K
-        // and chunk col ^ 2(r & 3) of V
-        const int r = stage_token0(0, wave, i) + (lane >> 4);
+        // LDS row r = stage row, position col holds chunk col ^ (r & kSwzK) of
+        // K and chunk col ^ 2(r & 3) of V
+        const int r = stage_token0<D>(0, wave, i) + lane / kChunks;
         const int64_t off = (int64_t)(in_pool ? phys : 0) * blk_stride + row * kD;
-        const int ck = col ^ (r & 15);
+        const int ck = col ^ (r & kSwzK);
         const int cv = col ^ (2 * (r & 3));
-        unsigned char* kdst = buf + stage_token0(0, wave, i) * kPitch;
-        unsigned char* vdst = buf + kTileBytes + stage_token0(0, wave, i) * kPitchV;
+        unsigned char* kdst = buf + stage_token0<D>(0, wave, i) * kPitch;
+        unsigned char* vdst = buf + kTileBytes + stage_token0<D>(0, wave, i) * kPitchV;
         const _Float16* ksrc = kbase + off + ck * 8;
         const _Float16* vsrc = vbase + off + cv * 8;
         if constexpr (kAppend) {
@@ -196,16 +251,18 @@ __device__ __forceinline__ void fetch_tile(Staged& st, unsigned char* buf, int k
 
 // After this thread's loads of the tile landed: zero its rows that are not
 // valid (past the context or outside the pool) and write the flags.
-__device__ __forceinline__ void finish_tile(const Staged& st, unsigned char* buf, unsigned char* flags, int wave,
+template <int D>
+__device__ __forceinline__ void finish_tile(const Staged<D>& st, unsigned char* buf, unsigned char* flags, int wave,
                                             int lane) {
-    const int col = lane & 15;
+    PF_GEO(D);
+    const int col = lane % kChunks;
     bool all_ok = true;
 #pragma unroll
     for (int i = 0; i < kStageRows; ++i) all_ok = all_ok && st.ok[i];
     if (!__all(all_ok)) {
 #pragma unroll
         for (int i = 0; i < kStageRows; ++i) {
-            const int row = stage_token0(0, wave, i) + (lane >> 4);
+            const int row = stage_token0<D>(0, wave, i) + lane / kChunks;
             const u32x4 z = {0u, 0u, 0u, 0u};
             if (!st.ok[i]) {
                 *reinterpret_cast<u32x4*>(buf + row * kPitch + col * 16) = z;
@@ -215,27 +272,29 @@ __device__ __forceinline__ void finish_tile(const Staged& st, unsigned char* buf
     }
 #pragma unroll
     for (int i = 0; i < kStageRows; ++i)
-        if (col == 0) flags[stage_token0(0, wave, i) + (lane >> 4)] = st.ok[i];
+        if (col == 0) flags[stage_token0<D>(0, wave, i) + lane / kChunks] = st.ok[i];
 }
 
 // Append mode, while tile k is in LDS: the rows this thread loaded that are
 // new tokens owned by the workgroup go from LDS into the cache, 16 bytes of
-// K and of V each (LDS position col of row r holds chunk col ^ (r & 15) of
-// K and col ^ 2(r & 3) of V).  No workgroup reads these rows from the cache.
-template <int B>
-__device__ __forceinline__ void write_own_rows(const Staged& st, const unsigned char* buf, int k, int wave, int lane,
-                                               _Float16* __restrict__ kw, _Float16* __restrict__ vw,
+// K and of V each (LDS position col of row r holds chunk col ^ (r & kSwzK)
+// of K and col ^ 2(r & 3) of V).  No workgroup reads these rows from the
+// cache.
+template <int D, int B>
+__device__ __forceinline__ void write_own_rows(const Staged<D>& st, const unsigned char* buf, int k, int wave,
+                                               int lane, _Float16* __restrict__ kw, _Float16* __restrict__ vw,
                                                int64_t blk_stride) {
-    const int col = lane & 15;
+    PF_GEO(D);
+    const int col = lane % kChunks;
 #pragma unroll
     for (int i = 0; i < kStageRows; ++i) {
         if (st.wphys[i] < 0) continue;
-        const int r = stage_token0(0, wave, i) + (lane >> 4);
+        const int r = stage_token0<D>(0, wave, i) + lane / kChunks;
         const int t = k * kKvTile + r;
         const int64_t dst = (int64_t)st.wphys[i] * blk_stride + (int64_t)(t % B) * kD;
         const u32x4 kv = *reinterpret_cast<const u32x4*>(buf + r * kPitch + col * 16);
         const u32x4 vv = *reinterpret_cast<const u32x4*>(buf + kTileBytes + r * kPitchV + col * 16);
-        *reinterpret_cast<u32x4*>(kw + dst + (col ^ (r & 15)) * 8) = kv;
+        *reinterpret_cast<u32x4*>(kw + dst + (col ^ (r & kSwzK)) * 8) = kv;
         *reinterpret_cast<u32x4*>(vw + dst + (col ^ (2 * (r & 3))) * 8) = vv;
     }
 }
@@ -269,6 +328,83 @@ __device__ __forceinline__ float row_sum4(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+typedef short v4s_ __attribute__((ext_vector_type(4)));
+
+// LDS transpose reads of kG (1 or 2) groups of 4 PV d-tiles: for group gg,
+// r[8gg + 2c] = the 8 bytes at a[c] + base + gg * kGroup and r[8gg + 2c +
+// 1] at the same + kHalf (the second half of the 32-token slab), base = u *
+// kSlab + grp * kGroup.  Issued in inline asm with their wait inside the
+// same block: the builtin carries no memory operand, so the compiler would
+// wait for every load into LDS still in flight before it.  The offsets are
+// immediates, hence one asm block per (slab, group) pair.
+template <int kG, int kSlab, int kHalf, int kGroup>
+__device__ __forceinline__ void tr_reads(v4s_ (&r)[8 * kG], const uint32_t (&a)[4], int u, int grp) {
+    static_assert(kSlab + 3 * kGroup + kHalf < 65536, "transpose-read offsets fit the 16-bit field");
+#define PF_TR8(BASE)                                                                                   \
+    asm volatile(                                                                                      \
+        "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"                                                     \
+        "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"                                                     \
+        "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"                                                     \
+        "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"                                                     \
+        "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"                                                    \
+        "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"                                                    \
+        "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"                                                    \
+        "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"                                                    \
+        "s_waitcnt lgkmcnt(0)"                                                                         \
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),  \
+          "=&v"(r[7])                                                                                  \
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(BASE), "i"((BASE) + kHalf)                 \
+        : "memory")
+#define PF_TR16(BASE)                                                                                  \
+    asm volatile(                                                                                      \
+        "ds_read_b64_tr_b16 %0, %16 offset:%20\n\t"                                                    \
+        "ds_read_b64_tr_b16 %1, %16 offset:%21\n\t"                                                    \
+        "ds_read_b64_tr_b16 %2, %17 offset:%20\n\t"                                                    \
+        "ds_read_b64_tr_b16 %3, %17 offset:%21\n\t"                                                    \
+        "ds_read_b64_tr_b16 %4, %18 offset:%20\n\t"                                                    \
+        "ds_read_b64_tr_b16 %5, %18 offset:%21\n\t"                                                    \
+        "ds_read_b64_tr_b16 %6, %19 offset:%20\n\t"                                                    \
+        "ds_read_b64_tr_b16 %7, %19 offset:%21\n\t"                                                    \
+        "ds_read_b64_tr_b16 %8, %16 offset:%22\n\t"                                                    \
+        "ds_read_b64_tr_b16 %9, %16 offset:%23\n\t"                                                    \
+        "ds_read_b64_tr_b16 %10, %17 offset:%22\n\t"                                                   \
+        "ds_read_b64_tr_b16 %11, %17 offset:%23\n\t"                                                   \
+        "ds_read_b64_tr_b16 %12, %18 offset:%22\n\t"                                                   \
+        "ds_read_b64_tr_b16 %13, %18 offset:%23\n\t"                                                   \
+        "ds_read_b64_tr_b16 %14, %19 offset:%22\n\t"                                                   \
+        "ds_read_b64_tr_b16 %15, %19 offset:%23\n\t"                                                   \
+        "s_waitcnt lgkmcnt(0)"                                                                         \
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),  \
+          "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]),             \
+          "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])                                                     \
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(BASE), "i"((BASE) + kHalf),                 \
+          "i"((BASE) + kGroup), "i"((BASE) + kGroup + kHalf)                                           \
+        : "memory")
+    if constexpr (kG == 1) {
+        switch (u * 8 + grp) {
+            case 0: PF_TR8(0); break;
+            case 1: PF_TR8(kGroup); break;
+            case 2: PF_TR8(2 * kGroup); break;
+            case 3: PF_TR8(3 * kGroup); break;
+            case 8: PF_TR8(kSlab); break;
+            case 9: PF_TR8(kSlab + kGroup); break;
+            case 10: PF_TR8(kSlab + 2 * kGroup); break;
+            case 11: PF_TR8(kSlab + 3 * kGroup); break;
+            default: break;
+        }
+    } else {
+        switch (u * 8 + grp) {
+            case 0: PF_TR16(0); break;
+            case 2: PF_TR16(2 * kGroup); break;
+            case 8: PF_TR16(kSlab); break;
+            case 10: PF_TR16(kSlab + 2 * kGroup); break;
+            default: break;
+        }
+    }
+#undef PF_TR8
+#undef PF_TR16
+}
+
 // Consume one LDS tile for the wave's kNT groups of 16 rows on
 // v_mfma_f32_16x16x32_f16.  Every operand read from LDS feeds kNT products.
 //   QK, per 16-token half h: S^T[token][row] = sum_d K[token][d] Q[row][d];
@@ -281,10 +417,12 @@ __device__ __forceinline__ float row_sum4(float x) {
 // the first row's position, so no score is masked.  The exponent of a
 // weight is one FMA of the raw score: c = scale * log2(e) > 0, so the raw
 // maximum times c is the maximum of the scaled scores, and -inf stays -inf.
-__device__ __forceinline__ void consume_lds_tile(Softmax (&st)[kNT], const unsigned char* buf,
+template <int D>
+__device__ __forceinline__ void consume_lds_tile(Softmax<D> (&st)[PGeo<D>::kNT], const unsigned char* buf,
                                                  const unsigned char* flags, int t0, bool interior,
-                                                 const half8_t_ (&qb)[kNT][4], float c_log2, int lane,
-                                                 const Rows (&rw)[kNT]) {
+                                                 const half8_t_ (&qb)[PGeo<D>::kNT][PGeo<D>::kQk], float c_log2,
+                                                 int lane, const Rows (&rw)[PGeo<D>::kNT]) {
+    PF_GEO(D);
     constexpr int NS = kKvTile / 32;            // 32-token sub-tiles (one PV MFMA k-slab each)
     const int n = lane & 15;
     const int j = lane >> 4;
@@ -297,9 +435,9 @@ __device__ __forceinline__ void consume_lds_tile(Softmax (&st)[kNT], const unsig
 #pragma unroll
         for (int t = 0; t < kNT; ++t) acc[t] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < kQk; ++c) {
             const half8_t_ a = __builtin_bit_cast(half8_t_, *reinterpret_cast<const u32x4*>(
-                                                               kb + (16 * h + n) * kPitch + 16 * ((4 * c + j) ^ n)));
+                kb + (16 * h + n) * kPitch + 16 * ((4 * c + j) ^ ((16 * h + n) & kSwzK))));
 #pragma unroll
             for (int t = 0; t < kNT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[t][c], acc[t], 0, 0, 0);
         }
@@ -371,63 +509,39 @@ __device__ __forceinline__ void consume_lds_tile(Softmax (&st)[kNT], const unsig
     // 4q] (tb = 4j for k 0..3 of the B operand, 16 + 4j for k 4..7: the
     // tokens whose weights the lane holds in P), so lane (n, j) receives
     // V[tb + e][16c + n]: the B operand of d-tile c, output column n of d-tile
-    // c being d = 16c + n.  V rows are 288 bytes apart so that the 4 rows x 4
-    // pieces of one lane group fall in 32 different banks.
-    typedef short v4s_ __attribute__((ext_vector_type(4)));
+    // c being d = 16c + n.  The 32-byte unit c of V row r sits at unit c ^ (r
+    // & 3) (the chunk swizzle of fetch_tile), so the 4 rows x 4 pieces of one
+    // lane group fall in distinct banks.  d-tiles come in groups of 4 (128
+    // bytes of a row); one asm block reads two token halves of one group.
     const int e4 = (lane & 15) >> 2;
     const int q4 = lane & 3;
-    // transpose reads issued in inline asm (with their wait inside the same
-    // block): the builtin carries no memory operand, so the compiler would
-    // wait for every load into LDS still in flight before it
     const unsigned char* lo = vb + (4 * j + e4) * kPitchV + 8 * q4;
     uint32_t a[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
         a[c] = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)(lo + 32 * (c ^ e4));
-#define PF_TR16(O0, O1, O2, O3)                                                                              \
-    asm volatile(                                                                                            \
-        "ds_read_b64_tr_b16 %0, %16 offset:" #O0 "\n\t"                                                     \
-        "ds_read_b64_tr_b16 %1, %16 offset:" #O1 "\n\t"                                                     \
-        "ds_read_b64_tr_b16 %2, %17 offset:" #O0 "\n\t"                                                     \
-        "ds_read_b64_tr_b16 %3, %17 offset:" #O1 "\n\t"                                                     \
-        "ds_read_b64_tr_b16 %4, %18 offset:" #O0 "\n\t"                                                     \
-        "ds_read_b64_tr_b16 %5, %18 offset:" #O1 "\n\t"                                                     \
-        "ds_read_b64_tr_b16 %6, %19 offset:" #O0 "\n\t"                                                     \
-        "ds_read_b64_tr_b16 %7, %19 offset:" #O1 "\n\t"                                                     \
-        "ds_read_b64_tr_b16 %8, %16 offset:" #O2 "\n\t"                                                     \
-        "ds_read_b64_tr_b16 %9, %16 offset:" #O3 "\n\t"                                                     \
-        "ds_read_b64_tr_b16 %10, %17 offset:" #O2 "\n\t"                                                    \
-        "ds_read_b64_tr_b16 %11, %17 offset:" #O3 "\n\t"                                                    \
-        "ds_read_b64_tr_b16 %12, %18 offset:" #O2 "\n\t"                                                    \
-        "ds_read_b64_tr_b16 %13, %18 offset:" #O3 "\n\t"                                                    \
-        "ds_read_b64_tr_b16 %14, %19 offset:" #O2 "\n\t"                                                    \
-        "ds_read_b64_tr_b16 %15, %19 offset:" #O3 "\n\t"                                                    \
-        "s_waitcnt lgkmcnt(0)"                                                                               \
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),        \
-          "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]), "=&v"(r[12]), "=&v"(r[13]),    \
-          "=&v"(r[14]), "=&v"(r[15])                                                                         \
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])                                                         \
-        : "memory")
-    static_assert(NS == 2, "two 32-token PV slabs per tile");
+    constexpr int kG = kDTiles >= 8 ? 2 : 1;   // d-tile groups per asm block
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
-        v4s_ r[16];
-        if (u == 0) PF_TR16(0, 4096, 128, 4224);
-        else PF_TR16(8192, 12288, 8320, 12416);
 #pragma unroll
-        for (int c = 0; c < kDTiles; ++c) {
-            const half4_t h0 = __builtin_bit_cast(half4_t, r[2 * c]);
-            const half4_t h1 = __builtin_bit_cast(half4_t, r[2 * c + 1]);
-            const half8_t_ b = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+        for (int grp = 0; grp < kDTiles / 4; grp += kG) {
+            v4s_ r[8 * kG];
+            tr_reads<kG, 32 * kPitchV, 16 * kPitchV, 128>(r, a, u, grp);
 #pragma unroll
-            for (int t = 0; t < kNT; ++t)
-                st[t].o[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(p[t][u], b, st[t].o[c], 0, 0, 0);
+            for (int c = 0; c < 4 * kG; ++c) {
+                const half4_t h0 = __builtin_bit_cast(half4_t, r[2 * c]);
+                const half4_t h1 = __builtin_bit_cast(half4_t, r[2 * c + 1]);
+                const half8_t_ b = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+#pragma unroll
+                for (int t = 0; t < kNT; ++t)
+                    st[t].o[4 * grp + c] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(p[t][u], b, st[t].o[4 * grp + c], 0, 0, 0);
+            }
         }
     }
-#undef PF_TR16
 }
 
-template <int B, bool kStream, bool kAppend>
+template <int D, int B, bool kStream, bool kAppend>
 __global__ void __launch_bounds__(kThreads)
 prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, int32_t num_tokens,
                     const _Float16* __restrict__ k_cache, const _Float16* __restrict__ v_cache,
@@ -438,6 +552,7 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
                     int32_t num_parts, int32_t num_seqs, int32_t row_tiles, int32_t xcd_grouped,
                     const _Float16* __restrict__ new_k, const _Float16* __restrict__ new_v, int64_t new_stride,
                     _Float16* __restrict__ k_write, _Float16* __restrict__ v_write) {
+    PF_GEO(D);
     // two stage buffers as distinct objects, so that the compiler can tell
     // the buffer a step reads from the one whose loads are in flight
     __shared__ __attribute__((aligned(16))) unsigned char ldsA[kBufBytes];
@@ -508,7 +623,7 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
     const bool neg = scale_log2 < 0.f;
     const float c_log2 = fmaxf(neg ? -scale_log2 : scale_log2, 1.17549435e-38f);
     Rows rw[kNT];
-    half8_t_ qb[kNT][4];
+    half8_t_ qb[kNT][kQk];
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
         rw[t].live = 16 * t + nrow < rows;
@@ -516,7 +631,7 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
         rw[t].pos = base_pos + r / g;
         const _Float16* qrow = q + (((int64_t)q0 + r / g) * num_heads + (int64_t)kvh * g + r % g) * kD;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < kQk; ++c) {
             const u32x4 z = {0u, 0u, 0u, 0u};
             const uint32_t flip = neg ? 0x80008000u : 0u;
             u32x4 v = rw[t].live ? *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * jg) : z;
@@ -543,7 +658,7 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
     const _Float16* vbase = v_cache + (int64_t)kvh * slab;
     const int64_t blk_stride = (int64_t)num_kv_heads * slab;
 
-    Softmax st[kNT];
+    Softmax<D> st[kNT];
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
         st[t].m = -INFINITY;
@@ -580,25 +695,26 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
         kw = k_write + (int64_t)kvh * slab;
         vw = v_write + (int64_t)kvh * slab;
     }
-    Staged SA, SB;
+    Staged<D> SA, SB;
     int32_t e[kStageRows] = {};
     const int kb = k_begin;
-    if constexpr (B >= 4) table_entries<B>(e, kb, wave, n, trow);
-    fetch_tile<B, kStream, kAppend>(SA, ldsA, kb, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks, ap);
-    if constexpr (B >= 4) table_entries<B>(e, kb + 1, wave, n, trow);
+    if constexpr (B >= kRowsPerLoad) table_entries<D, B>(e, kb, wave, n, trow);
+    fetch_tile<D, B, kStream, kAppend>(SA, ldsA, kb, e, wave, lane, n, trow, kbase, vbase, blk_stride, num_blocks,
+                                       ap);
+    if constexpr (B >= kRowsPerLoad) table_entries<D, B>(e, kb + 1, wave, n, trow);
     PA_WAIT_VM(0);
-    finish_tile(SA, ldsA, flA, wave, lane);
+    finish_tile<D>(SA, ldsA, flA, wave, lane);
     PA_WAIT_LGKM0();
     __builtin_amdgcn_s_barrier();
-    auto step = [&](int k, unsigned char* cb, unsigned char* cf, const Staged& cs, unsigned char* nb,
-                    unsigned char* nf, Staged& ns) {
+    auto step = [&](int k, unsigned char* cb, unsigned char* cf, const Staged<D>& cs, unsigned char* nb,
+                    unsigned char* nf, Staged<D>& ns) {
         // the last step of the walk fetches nothing: no step consumes tile k_end
         const bool more = k + 1 < k_end;
         if (more)
-            fetch_tile<B, kStream, kAppend>(ns, nb, k + 1, e, wave, lane, n, trow, kbase, vbase, blk_stride,
-                                            num_blocks, ap);
-        if constexpr (B >= 4)
-            if (k + 2 < k_end) table_entries<B>(e, k + 2, wave, n, trow);
+            fetch_tile<D, B, kStream, kAppend>(ns, nb, k + 1, e, wave, lane, n, trow, kbase, vbase, blk_stride,
+                                               num_blocks, ap);
+        if constexpr (B >= kRowsPerLoad)
+            if (k + 2 < k_end) table_entries<D, B>(e, k + 2, wave, n, trow);
         if (k < my_end) {
             // uniform: tile below the wave's first row and wholly valid
             bool interior = k * kKvTile + kKvTile - 1 <= first_pos;
@@ -609,15 +725,15 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
                     all_ok = all_ok && *reinterpret_cast<const uint32_t*>(cf + 16 * h + 4 * jg) == 0x01010101u;
                 interior = __all(all_ok);
             }
-            consume_lds_tile(st, cb, cf, k * kKvTile, interior, qb, c_log2, lane, rw);
+            consume_lds_tile<D>(st, cb, cf, k * kKvTile, interior, qb, c_log2, lane, rw);
         }
         PA_WAIT_VM(0);
         // append mode: the new tokens of tile k this workgroup owns go to the
         // cache now, after the wait, so that the stores complete under the
         // next step's products instead of stalling this step's wait; the LDS
         // reads finish before the barrier, ahead of the next fetch into `cb`
-        if constexpr (kAppend) write_own_rows<B>(cs, cb, k, wave, lane, kw, vw, blk_stride);
-        if (more) finish_tile(ns, nb, nf, wave, lane);
+        if constexpr (kAppend) write_own_rows<D, B>(cs, cb, k, wave, lane, kw, vw, blk_stride);
+        if (more) finish_tile<D>(ns, nb, nf, wave, lane);
         PA_WAIT_LGKM0();
         __builtin_amdgcn_s_barrier();
     };
@@ -673,15 +789,17 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
 
 // Merge of the context parts: output row (token i of sequence s, head h)
 // combines the (m, l, O) its row tile's parts left, weighted by exp2(m_p -
-// max m).  One 128-thread workgroup (one thread per column) per (head,
+// max m).  One workgroup of D threads (one thread per column) per (head,
 // sequence, 16 tokens).
 constexpr int kMergeTokens = 16;
 
-__global__ void __launch_bounds__(kD)
+template <int D>
+__global__ void __launch_bounds__(256)
 prefill_merge_kernel(_Float16* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
                      int32_t num_tokens, const int32_t* __restrict__ lens, const int32_t* __restrict__ query_start,
                      int32_t num_heads, int32_t num_kv_heads, int32_t max_query_len, int64_t len_cap,
                      int32_t tiles_per_part, int32_t num_parts) {
+    PF_GEO(D);
     const int h = blockIdx.x;
     const int s = blockIdx.y;
     const int d = threadIdx.x;
@@ -722,18 +840,54 @@ using PrefillFn = void (*)(_Float16*, const _Float16*, int32_t, const _Float16*,
                            int64_t, float*, float*, int32_t, int32_t, int32_t, int32_t, int32_t, const _Float16*,
                            const _Float16*, int64_t, _Float16*, _Float16*);
 
-template <bool kStream, bool kAppend>
+template <int D, bool kStream, bool kAppend>
 PrefillFn pick(int32_t b) {
     switch (b) {
-        case 1: return prefill_mfma_kernel<1, kStream, kAppend>;
-        case 2: return prefill_mfma_kernel<2, kStream, kAppend>;
-        case 4: return prefill_mfma_kernel<4, kStream, kAppend>;
-        case 8: return prefill_mfma_kernel<8, kStream, kAppend>;
-        case 16: return prefill_mfma_kernel<16, kStream, kAppend>;
-        case 32: return prefill_mfma_kernel<32, kStream, kAppend>;
-        case 64: return prefill_mfma_kernel<64, kStream, kAppend>;
-        case 128: return prefill_mfma_kernel<128, kStream, kAppend>;
+        case 1: return prefill_mfma_kernel<D, 1, kStream, kAppend>;
+        case 2: return prefill_mfma_kernel<D, 2, kStream, kAppend>;
+        case 4: return prefill_mfma_kernel<D, 4, kStream, kAppend>;
+        case 8: return prefill_mfma_kernel<D, 8, kStream, kAppend>;
+        case 16: return prefill_mfma_kernel<D, 16, kStream, kAppend>;
+        case 32: return prefill_mfma_kernel<D, 32, kStream, kAppend>;
+        case 64: return prefill_mfma_kernel<D, 64, kStream, kAppend>;
+        case 128: return prefill_mfma_kernel<D, 128, kStream, kAppend>;
         default: return nullptr;
+    }
+}
+
+template <bool kStream, bool kAppend>
+PrefillFn pick(int32_t d, int32_t b) {
+    switch (d) {
+        case 64: return pick<64, kStream, kAppend>(b);
+        case 128: return pick<128, kStream, kAppend>(b);
+        case 256: return pick<256, kStream, kAppend>(b);
+        default: return nullptr;
+    }
+}
+
+using MergeFn = void (*)(_Float16*, const float*, const float*, int32_t, const int32_t*, const int32_t*, int32_t,
+                         int32_t, int32_t, int64_t, int32_t, int32_t);
+
+MergeFn pick_merge(int32_t d) {
+    switch (d) {
+        case 64: return prefill_merge_kernel<64>;
+        case 128: return prefill_merge_kernel<128>;
+        case 256: return prefill_merge_kernel<256>;
+        default: return nullptr;
+    }
+}
+
+// Row tile and K/V tile of the kernel serving head_dim d.
+struct HostGeo {
+    int32_t rows_per_group;
+    int32_t kv_tile;
+};
+
+HostGeo host_geo(int32_t d) {
+    switch (d) {
+        case 64: return {PGeo<64>::kRowsPerGroup, PGeo<64>::kKvTile};
+        case 256: return {PGeo<256>::kRowsPerGroup, PGeo<256>::kKvTile};
+        default: return {PGeo<128>::kRowsPerGroup, PGeo<128>::kKvTile};
     }
 }
 
@@ -758,16 +912,20 @@ struct SplitPlan {
 };
 
 SplitPlan split_plan(int32_t num_tokens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                     int64_t len_cap, int32_t max_query_len) {
+                     int32_t head_dim, int64_t len_cap, int32_t max_query_len) {
     SplitPlan P{};
+    const HostGeo hg = host_geo(head_dim);
     const int64_t g = num_heads / num_kv_heads;
-    P.row_tiles = (int32_t)(((int64_t)max_query_len * g + kRowsPerGroup - 1) / kRowsPerGroup);
-    const int64_t max_tiles = len_cap / kKvTile + 1;
+    P.row_tiles = (int32_t)(((int64_t)max_query_len * g + hg.rows_per_group - 1) / hg.rows_per_group);
+    // contexts shorter than a few tiles are not worth splitting (parts of at
+    // least 256 tokens)
+    const int64_t max_tiles = len_cap / hg.kv_tile + 1;
+    const int64_t min_tiles_per_part = 256 / hg.kv_tile;
     const int64_t wgs = (int64_t)num_kv_heads * num_seqs * P.row_tiles;
     int64_t parts = 1;
-    if (wgs > 0 && 2 * wgs <= 512 && max_tiles >= 8) {
+    if (wgs > 0 && 2 * wgs <= 512 && max_tiles >= 2 * min_tiles_per_part) {
         parts = 512 / wgs;
-        if (parts > max_tiles / 4) parts = max_tiles / 4;
+        if (parts > max_tiles / min_tiles_per_part) parts = max_tiles / min_tiles_per_part;
         if (parts * P.row_tiles > 65535) parts = 65535 / P.row_tiles;
         if (parts < 1) parts = 1;
     }
@@ -779,7 +937,7 @@ SplitPlan split_plan(int32_t num_tokens, int32_t num_seqs, int32_t num_heads, in
     }
     const size_t rows = (size_t)num_tokens * num_heads * P.num_parts;
     P.ml_bytes = align_up(rows * 2 * sizeof(float), 256);
-    P.total = P.ml_bytes + align_up(rows * kD * sizeof(float), 256);
+    P.total = P.ml_bytes + align_up(rows * head_dim * sizeof(float), 256);
     return P;
 }
 
@@ -788,11 +946,11 @@ SplitPlan split_plan(int32_t num_tokens, int32_t num_seqs, int32_t num_heads, in
 extern "C" size_t pa_prefill_workspace_size(int32_t num_tokens, int32_t num_seqs, int32_t num_heads,
                                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                             int32_t max_blocks_per_seq, int32_t max_query_len) {
-    if (head_dim != kD || !pick<false, false>(block_size) || num_tokens < 0 || num_seqs < 0 || num_heads <= 0 ||
+    if (!pick<false, false>(head_dim, block_size) || num_tokens < 0 || num_seqs < 0 || num_heads <= 0 ||
         num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || max_blocks_per_seq < 0 || max_query_len < 0)
         return (size_t)-1;
-    return split_plan(num_tokens, num_seqs, num_heads, num_kv_heads, (int64_t)max_blocks_per_seq * block_size,
-                      max_query_len)
+    return split_plan(num_tokens, num_seqs, num_heads, num_kv_heads, head_dim,
+                      (int64_t)max_blocks_per_seq * block_size, max_query_len)
         .total;
 }
 
@@ -813,8 +971,10 @@ int prefill_impl(const char* fn, void* out, const void* q, int32_t num_tokens, c
                  int32_t max_query_len, void* workspace, size_t workspace_bytes, int32_t dtype, void* stream,
                  const PrefillAppend* app) {
     if (dtype != PA_DTYPE_F16) return pa::fail(PA_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
-    if (head_dim != kD) return pa::fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (only %d)", fn, head_dim, kD);
-    if (!pick<false, false>(block_size)) return pa::fail(PA_ERR_UNSUPPORTED, "%s: block_size %d", fn, block_size);
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+        return pa::fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (64, 128 or 256)", fn, head_dim);
+    if (!pick<false, false>(head_dim, block_size))
+        return pa::fail(PA_ERR_UNSUPPORTED, "%s: block_size %d", fn, block_size);
     if (num_seqs < 0 || num_tokens < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
         num_blocks <= 0 || max_blocks_per_seq < 0 || max_query_len < 0)
         return pa::fail(PA_ERR_INVALID, "%s: bad sizes (S=%d H=%d Hkv=%d NB=%d W=%d max_q=%d)", fn, num_seqs,
@@ -838,7 +998,8 @@ int prefill_impl(const char* fn, void* out, const void* q, int32_t num_tokens, c
                             (long long)app->stride);
     }
     const int64_t g = num_heads / num_kv_heads;
-    const int64_t row_tiles = ((int64_t)max_query_len * g + kRowsPerGroup - 1) / kRowsPerGroup;
+    const HostGeo hg = host_geo(head_dim);
+    const int64_t row_tiles = ((int64_t)max_query_len * g + hg.rows_per_group - 1) / hg.rows_per_group;
     if (row_tiles > 65535)
         return pa::fail(PA_ERR_INVALID, "%s: max_query_len %d x %lld heads needs %lld row tiles (limit 65535)",
                         fn, max_query_len, (long long)g, (long long)row_tiles);
@@ -850,11 +1011,11 @@ int prefill_impl(const char* fn, void* out, const void* q, int32_t num_tokens, c
                                          num_blocks, len_cap, stream))
             return rc;
     }
-    SplitPlan P = split_plan(num_tokens, num_seqs, num_heads, num_kv_heads, len_cap, max_query_len);
+    SplitPlan P = split_plan(num_tokens, num_seqs, num_heads, num_kv_heads, head_dim, len_cap, max_query_len);
     if (P.num_parts > 1 && (!workspace || workspace_bytes < P.total)) {
         // no room for the partial states: one part per row tile
         P.num_parts = 1;
-        P.tiles_per_part = (int32_t)(len_cap / kKvTile + 1);
+        P.tiles_per_part = (int32_t)(len_cap / hg.kv_tile + 1);
     }
     float* ws_ml = P.num_parts > 1 ? static_cast<float*>(workspace) : nullptr;
     float* ws_acc = P.num_parts > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + P.ml_bytes) : nullptr;
@@ -869,8 +1030,9 @@ int prefill_impl(const char* fn, void* out, const void* q, int32_t num_tokens, c
     const int64_t grid = pairs * row_tiles * P.num_parts;
     if (grid > 0x7fffffff) return pa::fail(PA_ERR_INVALID, "%s: %lld workgroups (limit 2^31 - 1)", fn,
                                               (long long)grid);
-    const PrefillFn fn_main = app ? (stream_kv ? pick<true, true>(block_size) : pick<false, true>(block_size))
-                                  : (stream_kv ? pick<true, false>(block_size) : pick<false, false>(block_size));
+    const PrefillFn fn_main =
+        app ? (stream_kv ? pick<true, true>(head_dim, block_size) : pick<false, true>(head_dim, block_size))
+            : (stream_kv ? pick<true, false>(head_dim, block_size) : pick<false, false>(head_dim, block_size));
     // the cache pointers double as write pointers in append mode: the kernel
     // writes only the new tokens' rows, which no workgroup reads from the
     // cache
@@ -886,10 +1048,11 @@ int prefill_impl(const char* fn, void* out, const void* q, int32_t num_tokens, c
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
     if (P.num_parts > 1) {
-        hipLaunchKernelGGL(prefill_merge_kernel,
+        hipLaunchKernelGGL(pick_merge(head_dim),
                            dim3((unsigned)num_heads, (unsigned)num_seqs,
                                 (unsigned)((max_query_len + kMergeTokens - 1) / kMergeTokens)),
-                           dim3(kD), 0, st, static_cast<_Float16*>(out), (const float*)ws_ml, (const float*)ws_acc,
+                           dim3((unsigned)head_dim), 0, st, static_cast<_Float16*>(out), (const float*)ws_ml,
+                           (const float*)ws_acc,
                            num_tokens, context_lens, query_start, num_heads, num_kv_heads, max_query_len, len_cap,
                            P.tiles_per_part, P.num_parts);
         e = hipGetLastError();

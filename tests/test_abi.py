@@ -148,7 +148,8 @@ def test_default_partition_keeps_the_gpu_busy():
     assert L.pa_decode_default_partition(64, 64, 8, 128, 16, 2048) == 512       # 512 rows x 4
     assert L.pa_decode_default_partition(16, 32, 32, 128, 16, 4096) == 512      # 512 rows x 8
     assert L.pa_decode_default_partition(1, 8, 8, 128, 16, 1000) == 256
-    assert L.pa_decode_default_partition(64, 32, 32, 64, 16, 2048) == 2048      # head_dim 64: vector kernel
+    assert L.pa_decode_default_partition(64, 32, 32, 64, 16, 2048) == 2048      # head_dim 64, one query per KV head
+    assert L.pa_decode_default_partition(256, 64, 8, 64, 16, 2048) == 2048      # head_dim 64 grouped: 512 slots
     assert L.pa_decode_default_partition(64, 32, 7, 128, 16, 2048) == -1
     for args in [(64, 32, 32, 128, 16, 2048), (256, 64, 8, 128, 16, 2048), (1, 8, 8, 128, 16, 1000)]:
         assert L.pa_decode_default_partition(*args) % 128 == 0
@@ -180,7 +181,8 @@ def _prefill_args(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=1), pa.PA_ERR_UNSUPPORTED),
-    (dict(D=64), pa.PA_ERR_UNSUPPORTED),            # the matrix-core prefill serves head_dim 128
+    (dict(D=32), pa.PA_ERR_UNSUPPORTED),            # the matrix-core prefill serves head_dim 64, 128, 256
+    (dict(D=96), pa.PA_ERR_UNSUPPORTED),
     (dict(B=12), pa.PA_ERR_UNSUPPORTED),
     (dict(H=3, Hkv=2), pa.PA_ERR_INVALID),
     (dict(NB=0), pa.PA_ERR_INVALID),
@@ -211,7 +213,7 @@ def _prefill_append_args(key=16, value=16, stride=256, **kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype=1), pa.PA_ERR_UNSUPPORTED),
-    (dict(D=64), pa.PA_ERR_UNSUPPORTED),
+    (dict(D=16), pa.PA_ERR_UNSUPPORTED),
     (dict(B=12), pa.PA_ERR_UNSUPPORTED),
     (dict(H=3, Hkv=2), pa.PA_ERR_INVALID),
     (dict(qs=None), pa.PA_ERR_INVALID),

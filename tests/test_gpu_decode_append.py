@@ -94,9 +94,12 @@ LENS = [0, 1, 2, 15, 16, 17, 33, 128, 129, 256, 257, 383, 512, 513, 777, 1024, 1
 @pytest.mark.parametrize("D,B,H,Hkv", [
     (128, 16, 4, 4),      # one query per KV head: vector kernel
     (128, 1, 2, 2),       # rows of one load in several blocks
-    (64, 4, 4, 2),        # vector kernel, two query heads per KV head
-    (16, 8, 2, 1),
+    (64, 4, 4, 2),        # grouped-query kernel at head_dim 64, two query heads per KV head
+    (16, 8, 2, 1),        # head_dim 16: vector kernel, two query heads per KV head
     (256, 32, 2, 2),
+    (64, 16, 16, 2),      # grouped-query kernel at head_dim 64, 8 query heads per KV head
+    (256, 16, 8, 2),      # grouped-query kernel at head_dim 256
+    (256, 4, 12, 4),      # grouped-query kernel at head_dim 256, tiles across blocks
     (128, 16, 16, 2),     # grouped-query kernel (8 query heads per KV head)
     (128, 8, 8, 4),       # grouped-query kernel, tiles across blocks
     (128, 64, 32, 2),     # grouped-query kernel, 16 query heads per KV head

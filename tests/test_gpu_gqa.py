@@ -1,5 +1,6 @@
-"""GPU parity of grouped-query pa_decode (several query heads per KV head,
-head_dim 128 -> the matrix-core kernel) against the oracle, through the C ABI.
+"""GPU parity of grouped-query pa_decode (2 to 16 query heads per KV head,
+head_dim 64, 128 or 256 -> the matrix-core kernel) against the oracle,
+through the C ABI.
 
 Caches for the small cases are built on the host by the oracle (model slots +
 oracle scatter, NaN in every unused slot) and uploaded."""
@@ -16,18 +17,19 @@ from test_gpu_decode import EDGE_LENS, _gpu_decode, _oracle_cache
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 32, 64, 128])
 @pytest.mark.parametrize("g", [2, 3, 8, 16])
 @pytest.mark.parametrize("P", [0, 128])
-def test_gqa_edge_lengths_match_oracle(B, g, P):
+def test_gqa_edge_lengths_match_oracle(D, B, g, P):
     dev = device()
     Hkv = 2
-    case = workloads.random_case(7000 + 10 * B + g + P, EDGE_LENS, g * Hkv, Hkv, 128, B)
+    case = workloads.random_case(7000 + 10 * B + g + P + D, EDGE_LENS, g * Hkv, Hkv, D, B)
     kc, vc, tables, lens = _oracle_cache(case)
-    say(f"gqa B={B} g={g} P={P} NB={case.num_blocks}")
+    say(f"gqa D={D} B={B} g={g} P={P} NB={case.num_blocks}")
     out = _gpu_decode(dev, case.q, kc, vc, tables, lens, case.scale, partition_size=P)
     ref = oracle.decode(case.q, kc, vc, tables, lens, case.scale)
-    assert_attention_close(out, ref, f"gqa B={B} g={g} P={P}")
+    assert_attention_close(out, ref, f"gqa D={D} B={B} g={g} P={P}")
     assert np.all(bits(out)[0] == 0)                       # n == 0 row is exactly zero
 
 
@@ -43,9 +45,10 @@ def test_gqa_group_shapes(H, Hkv):
     assert_attention_close(out, ref, f"H={H} Hkv={Hkv}")
 
 
-def test_gqa_single_token_is_exact():
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_gqa_single_token_is_exact(D):
     dev = device()
-    case = workloads.random_case(15, [1] * 6, 16, 2, 128, 16)
+    case = workloads.random_case(15, [1] * 6, 16, 2, D, 16)
     kc, vc, tables, lens = _oracle_cache(case)
     out = _gpu_decode(dev, case.q, kc, vc, tables, lens, case.scale)
     for s in range(6):

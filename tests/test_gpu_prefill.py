@@ -36,15 +36,17 @@ def _gpu_prefill(dev, q, kc, vc, tables, lens, qs, scale, max_query_len=None, sp
 LENS = [1, 2, 15, 16, 17, 33, 64, 100, 129, 300]
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("B", [1, 4, 8, 16, 32, 128])
 @pytest.mark.parametrize("H,Hkv", [(2, 2), (8, 2), (6, 3), (4, 4), (8, 4)])
 @pytest.mark.parametrize("chunk", ["full", "chunked", "decode"])
-def test_prefill_matches_oracle(B, H, Hkv, chunk):
+def test_prefill_matches_oracle(D, B, H, Hkv, chunk):
     """10 sequences: with 2 or 3 KV heads the (KV head, sequence) pairs are
     not a multiple of 8 and the grid takes the pair fastest; with 4 they are
-    (40) and the grid is XCD-grouped."""
+    (40) and the grid is XCD-grouped.  head_dim 64 / 128 / 256 (K/V tiles of
+    64, 64 and 32 tokens; 32, 32 and 16 query rows per wave)."""
     dev = device()
-    case = workloads.random_case(900 + B + 10 * H + Hkv, LENS, H, Hkv, 128, B)
+    case = workloads.random_case(900 + B + 10 * H + Hkv + D, LENS, H, Hkv, D, B)
     kc, vc, tables, lens = _oracle_cache(case)
     if chunk == "full":
         ms = list(LENS)
@@ -52,11 +54,11 @@ def test_prefill_matches_oracle(B, H, Hkv, chunk):
         ms = [max(1, n // 3) for n in LENS]
     else:
         ms = [1] * len(LENS)
-    q, qs = _queries(B + H, ms, H, 128)
-    say(f"prefill B={B} H={H}/{Hkv} {chunk}: rows {int(qs[-1])}")
+    q, qs = _queries(B + H, ms, H, D)
+    say(f"prefill D={D} B={B} H={H}/{Hkv} {chunk}: rows {int(qs[-1])}")
     out = _gpu_prefill(dev, q, kc, vc, tables, lens, qs, case.scale)
     ref = oracle.prefill(q, kc, vc, tables, lens, qs, case.scale)
-    assert_attention_close(out, ref, f"prefill B={B} H={H}/{Hkv} {chunk}")
+    assert_attention_close(out, ref, f"prefill D={D} B={B} H={H}/{Hkv} {chunk}")
     if chunk == "decode":                                     # one new token per sequence is decode
         dec = torch.empty_like(out)
         pa.pa_decode(dec, torch.from_numpy(q).to(dev), torch.from_numpy(kc).to(dev), torch.from_numpy(vc).to(dev),
@@ -146,8 +148,8 @@ def test_prefill_rising_scores_move_the_running_maximum():
     assert_attention_close(out, ref, "rising scores")
 
 
-@pytest.mark.parametrize("H,Hkv", [(8, 2), (4, 4), (16, 8)])
-def test_prefill_split_context(H, Hkv):
+@pytest.mark.parametrize("H,Hkv,D", [(8, 2, 128), (4, 4, 128), (16, 8, 128), (8, 2, 64), (8, 2, 256)])
+def test_prefill_split_context(H, Hkv, D):
     """Short chunks over long contexts with few sequences: the context is
     split into parts merged by a second kernel.  Against the oracle, against
     the unsplit kernel (same math, other summation order), bit for bit when
@@ -155,18 +157,18 @@ def test_prefill_split_context(H, Hkv):
     dev = device()
     lens_l = [3000, 2500, 1777]
     ms = [8, 40, 1]
-    case = workloads.random_case(91 + H, lens_l, H, Hkv, 128, 16)
+    case = workloads.random_case(91 + H + D, lens_l, H, Hkv, D, 16)
     kc, vc, tables, lens = _oracle_cache(case)
-    q, qs = _queries(91, ms, H, 128)
+    q, qs = _queries(91, ms, H, D)
     T, W = int(qs[-1]), tables.shape[1]
-    need = pa.pa_prefill_workspace_size(T, 3, H, Hkv, 128, 16, W, max(ms))
+    need = pa.pa_prefill_workspace_size(T, 3, H, Hkv, D, 16, W, max(ms))
     assert need > 0                                                  # this batch splits
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     split = _gpu_prefill(dev, q, kc, vc, tables, lens, qs, case.scale, workspace=ws)
     ref = oracle.prefill(q, kc, vc, tables, lens, qs, case.scale)
-    assert_attention_close(split, ref, f"split H={H}/{Hkv}")
+    assert_attention_close(split, ref, f"split H={H}/{Hkv} D={D}")
     whole = _gpu_prefill(dev, q, kc, vc, tables, lens, qs, case.scale, split=False)
-    assert_attention_close(whole, ref, f"unsplit H={H}/{Hkv}")
+    assert_attention_close(whole, ref, f"unsplit H={H}/{Hkv} D={D}")
     again = _gpu_prefill(dev, q, kc, vc, tables, lens, qs, case.scale, workspace=ws)
     assert np.array_equal(bits(split), bits(again))
     # the same workspace for a smaller batch (first two sequences)
@@ -306,10 +308,11 @@ def _gpu_prefill_append(dev, q, key, value, kc0, vc0, tables, lens, qs, scale, p
     return out, kc, vc
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("B", [1, 4, 16, 128])
 @pytest.mark.parametrize("H,Hkv", [(2, 2), (6, 3), (4, 4), (8, 4)])
 @pytest.mark.parametrize("chunk", ["full", "chunked", "decode"])
-def test_prefill_append_matches_oracle(B, H, Hkv, chunk):
+def test_prefill_append_matches_oracle(D, B, H, Hkv, chunk):
     """pa_prefill_append against the oracle's scatter of the new tokens
     followed by its prefill: the caches bit for bit (every new token written
     once, by the workgroup holding its first query row -- with 3 query heads
@@ -317,7 +320,7 @@ def test_prefill_append_matches_oracle(B, H, Hkv, chunk):
     tolerance.  The new tokens' slots hold NaN before the call, so any read of
     them from the cache would show."""
     dev = device()
-    case = workloads.random_case(700 + B + 10 * H + Hkv, LENS, H, Hkv, 128, B)
+    case = workloads.random_case(700 + B + 10 * H + Hkv + D, LENS, H, Hkv, D, B)
     if chunk == "full":
         ms = list(LENS)
     elif chunk == "chunked":
@@ -325,14 +328,14 @@ def test_prefill_append_matches_oracle(B, H, Hkv, chunk):
     else:
         ms = [1] * len(LENS)
     kc0, vc0, kc1, vc1, key, value, tables, lens = _append_case(case, ms)
-    q, qs = _queries(B + H + 5, ms, H, 128)
-    say(f"prefill_append B={B} H={H}/{Hkv} {chunk}: rows {int(qs[-1])}")
+    q, qs = _queries(B + H + 5, ms, H, D)
+    say(f"prefill_append D={D} B={B} H={H}/{Hkv} {chunk}: rows {int(qs[-1])}")
     out, kc, vc = _gpu_prefill_append(dev, q, key, value, kc0, vc0, tables, lens, qs, case.scale,
                                       pad=24 if B == 16 else 0)
     assert np.array_equal(bits(kc), kc1.view(np.uint16)), "K cache differs from the oracle's scatter"
     assert np.array_equal(bits(vc), vc1.view(np.uint16)), "V cache differs from the oracle's scatter"
     ref = oracle.prefill(q, kc1, vc1, tables, lens, qs, case.scale)
-    assert_attention_close(out, ref, f"prefill_append B={B} H={H}/{Hkv} {chunk}")
+    assert_attention_close(out, ref, f"prefill_append D={D} B={B} H={H}/{Hkv} {chunk}")
     # the same rows through the two-call path on the written cache
     two = _gpu_prefill(dev, q, kc1, vc1, tables, lens, qs, case.scale)
     assert_attention_close(two, ref, "two calls")
