@@ -196,9 +196,15 @@ int pa_decode_append(void *out, const void *q, const void *key,
  * pa_decode without a caller workspace, for callers that cannot allocate
  * device memory (code being captured into a HIP graph, tight serving loops,
  * harnesses that forbid allocation).  The library keeps the workspace in a
- * device array of PA_NOALLOC_SCRATCH_BYTES bytes per GPU, reserved when the
- * library's code is loaded on that GPU and held until the process ends; the
- * call itself allocates nothing.
+ * device array of PA_NOALLOC_SCRATCH_BYTES bytes (1 MiB) per GPU, reserved
+ * when the library's code is loaded on that GPU and held until the process
+ * ends; the call itself allocates nothing.  (The array is kept small: the
+ * HIP runtime was measured to spend about 1.5 us per MiB of such static
+ * device arrays on every blocking host-to-device copy of the process.)
+ * 1 MiB holds the dispatch order of any batch and the partial states of
+ * about 2000 (sequence, head, partition) rows at head_dim 128; the default
+ * partition needs none for batches of at least half a round of
+ * workgroups.
  *
  * Arguments, results and error behaviour are those of pa_decode with
  * workspace = that array.  PA_ERR_INVALID, before anything is enqueued, when
@@ -209,7 +215,7 @@ int pa_decode_append(void *out, const void *q, const void *key,
  * must be serialised by the caller.  Nothing in the array needs to be
  * cleared between calls.
  * ------------------------------------------------------------------------ */
-#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)1 << 20)
 
 int pa_decode_noalloc(void *out, const void *q, const void *k_cache,
                       const void *v_cache, const int32_t *block_tables,
@@ -327,17 +333,20 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
                                 int32_t partition_size);
 
 /* The partition size pa_decode uses when given 0.  With rows =
- * num_seqs x num_heads (x num_kv_heads on the matrix-core path) and slots =
- * the resident workgroups of the kernel that serves these shapes (1024, or
- * 512 on the matrix-core path): P1 when rows x ceil(max_context_len / P1)
- * workgroups fill the slots at least twice and a whole number of times (or
- * leave the last round at least 3/4 full), where P1 is 2048, or
- * max_context_len rounded up to a multiple of 128 when that lies in
- * (2048, 2560] (one partition then covers every context and no merge kernel
- * runs); otherwise the longest of
- * 2048, 1024, 512 and 256 tokens that gives at least four workgroups per
- * slot counting full partitions of a max_context_len sequence; 256 when none
- * does.  -1 for invalid arguments. */
+ * num_seqs x num_heads (x num_kv_heads on the matrix-core path), slots = the
+ * workgroups of the serving kernel resident at once (1024 on the vector
+ * path, 512 on the matrix-core path with blocks of 16 or more tokens) and
+ * cover = max_context_len rounded up to a multiple of 128 (one partition
+ * for every context, no merge kernel):
+ *   - cover when rows fill half a round to one round of slots, or more than
+ *     one round a whole number of times or with the last round at least 3/4
+ *     full;
+ *   - above one round otherwise, the longest of 2048, 1024, 512 and 256
+ *     tokens that gives at least four workgroups per slot counting full
+ *     partitions of a max_context_len sequence (256 when none does);
+ *   - below half a round, the bound cut into enough parts for one workgroup
+ *     per compute unit (256 of them), parts of at least 256 tokens.
+ * -1 for invalid arguments. */
 int32_t pa_decode_default_partition(int32_t num_seqs, int32_t num_heads,
                                     int32_t num_kv_heads, int32_t head_dim,
                                     int32_t block_size,
