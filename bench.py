@@ -76,6 +76,8 @@ def parse():
                    help="decode workloads: 1 writes the new K/V inside the decode call (pa_decode_append), "
                         "0 runs pa_reshape_and_cache then pa_decode")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--compare-default", type=int, default=1,
+                   help="long: also time the library's default partition (0 skips it, e.g. for counter passes)")
     p.add_argument("--cpu-baseline", type=int, default=1, help="0 skips the oracle timing")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="oracle CPU time: whole-layer decodes are repeated until this much has been spent")
@@ -327,7 +329,10 @@ def main():
         bm.set_table(s, w.perm_tables[s, :workloads.ceil_div(n - 1, B)], n - 1)
     seqs = np.arange(S, dtype=np.int64)
     part = args.partition
-    ws_bytes = pa.pa_decode_workspace_size(S, H, Hkv, D, B, width * B, part)
+    if args.workload == "long" and part == 0:
+        part = 512                      # the long-context workload fixes 512-token partitions + the merge kernel
+    ws_bytes = max(pa.pa_decode_workspace_size(S, H, Hkv, D, B, width * B, part),
+                   pa.pa_decode_workspace_size(S, H, Hkv, D, B, width * B, 0))
     workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 
     nbuf = 2
@@ -344,14 +349,15 @@ def main():
 
     kv_per_token = 2 * Hkv * D * 2           # K and V, fp16, one layer
 
-    def decode_call(l):
+    def decode_call(l, p=None):
+        p = part if p is None else p
         if args.fused:
             pa.pa_decode_append(out, q, key, val, kcs[l], vcs[l], d_tables, d_lens, w.scale, B,
-                                max_context_len=width * B, partition_size=part, workspace=workspace,
+                                max_context_len=width * B, partition_size=p, workspace=workspace,
                                 seq_order=d_order)
         else:
             pa.pa_decode(out, q, kcs[l], vcs[l], d_tables, d_lens, w.scale, B, max_context_len=width * B,
-                         partition_size=part, workspace=workspace, seq_order=d_order)
+                         partition_size=p, workspace=workspace, seq_order=d_order)
 
     def step(i):
         b = i % nbuf
@@ -412,6 +418,26 @@ def main():
     torch.cuda.synchronize()
     dec_ms = [sweep_ev[i].elapsed_time(sweep_ev[i + 1]) / L for i in range(K)]
     all_ctx += ctx_last * L * K
+    # the long-context line also times the library's default partition on
+    # the same batch (interleaved with the fixed one, sweeps over the layers)
+    alt = None
+    default_p = pa.pa_decode_default_partition(S, H, Hkv, D, B, width * B)
+    if args.workload == "long" and default_p != part and args.compare_default:
+        t_fixed, t_default = [], []
+        for i in range(max(K // 2, 2)):
+            for p_, acc in ((part, t_fixed), (0, t_default)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for l in range(L):
+                    decode_call(l, p_)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                acc.append(e0.elapsed_time(e1) / L / 1e3)
+        alt = {"partition_size": default_p, "us_per_call_median": round(statistics.median(t_default) * 1e6, 2),
+               "GB_s": round(ctx_last * kv_per_token / statistics.median(t_default) / 1e9, 2),
+               "fixed_partition_us_per_call_median": round(statistics.median(t_fixed) * 1e6, 2)}
+        log(f"[bench] library default partition {default_p}: {alt['us_per_call_median']} us per call = "
+            f"{alt['GB_s']} GB/s (partition {part} interleaved: {alt['fixed_partition_us_per_call_median']} us)")
     dec_avg_s = sum(dec_ms) / len(dec_ms) / 1e3
     kv_per_launch = ctx_last * kv_per_token
     achieved = kv_per_launch / dec_avg_s / 1e9
@@ -479,7 +505,7 @@ def main():
                         "GB_s_from_median_sweep": round(kv_per_launch / (statistics.median(dec_ms) / 1e3) / 1e9, 2)},
         "config": {"workload": wl_name, "batch": S, "block_size": B, "num_heads": H, "num_kv_heads": Hkv,
                    "head_dim": D, "context": ctx_desc, "layers_resident": L, "pool_blocks_per_layer": NB,
-                   "partition_size": part or pa.pa_decode_default_partition(S, H, Hkv, D, B, width * B),
+                   "partition_size": part or default_p,
                    "step": ("host append+tables, H2D, decode order, per layer pa_decode_append (new K/V "
                             "written inside the decode call)" if args.fused else
                             "host append+tables, H2D, decode order, per layer reshape_and_cache + decode")},
@@ -488,6 +514,7 @@ def main():
                      "kernel": "decode call (partition kernel + merge kernel when a context is split)",
                      "algorithmic_bytes_per_call": kv_per_launch, "cached_tokens_per_call": ctx_last},
         "decode_calls": {"count": (W + 2 * K) * L, "cached_tokens_total": all_ctx},
+        "decode_only_library_default_partition": alt,
         "cpu_baseline": cpu,
         "tiny_latency": tiny,
     }

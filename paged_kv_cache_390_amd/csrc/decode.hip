@@ -565,49 +565,67 @@ int64_t grid_rows(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int
     return (int64_t)num_seqs * (uses_mfma(num_heads, num_kv_heads, head_dim, block_size) ? num_kv_heads : num_heads);
 }
 
-// workgroups resident at once: 256 CUs x 4 (vector kernel, 108 VGPRs) or x 2
-// (grouped-query kernel, 232 VGPRs)
+// workgroups resident at once: 256 CUs x 4 (vector kernel, 108 VGPRs) or,
+// for the grouped-query kernel, as many as its registers allow
 int64_t resident_slots(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size) {
-    return 256LL * (uses_mfma(num_heads, num_kv_heads, head_dim, block_size) ? 2 : 4);
+    if (!uses_mfma(num_heads, num_kv_heads, head_dim, block_size)) return 256LL * 4;
+    // the matrix-core kernel's registers: 4 workgroups per CU at head_dim 64
+    // with tiles across blocks, 1 at head_dim 256 with tiles across blocks,
+    // 2 otherwise
+    if (block_size < 16) return 256LL * (head_dim == 64 ? 4 : head_dim == 256 ? 1 : 2);
+    return 256LL * 2;
 }
 
 // Default partition.  Rows are the workgroups one partition index gives
-// (grid_rows), slots the workgroups resident at once (resident_slots).
-//  * Long partitions first: P1 = 2048 tokens, or -- when the bound is at
-//    most 2560 -- the bound rounded up to the partition quantum if that is
-//    longer, so that one partition covers every context.  P1 is taken when
-//    its grid fills the slots a whole number of times, at least twice (or
-//    leaves the last round at least 3/4 full), counting every sequence at
-//    the bound: with the sequences dispatched longest first the drain is
-//    short, and long partitions mean fewer partial states and, when every
-//    context fits, no merge kernel.  (A batch drawn up to 2048 tokens grows
-//    past it by one token per step; at 2048 its few longest sequences would
-//    get a second partition of a few tokens, and every call a merge kernel
-//    of ~4.6 us, 2.7% of the 64 x 32-head call.)
-//  * Otherwise the longest of 2048 / 1024 / 512 / 256 tokens that gives at
-//    least four workgroups per slot, counting full partitions of a longest
-//    sequence (the bound may exceed every actual length).
-// Measured (decode call, KV GB/s): 64 x 32-head batch, U[1, 2048] contexts,
-// 6.29 TB/s at 2048 against 5.99 at 1024; 256 x 8-KV-head batch 6.02
-// against 5.57; 100 requests of 1001..1200 tokens (3.1 rounds at 2048):
-// 512 beats 2048 by 10%; 16 x 32 heads at 4096 tokens: 256..2048 within 3%.
+// (grid_rows), slots the workgroups resident at once (resident_slots), and
+// "cover" the bound rounded up to the partition quantum: one partition for
+// every context, no partial states, no merge kernel.
+//  * At least half a round and at most one round of rows (rows in [slots/2,
+//    slots]): cover.  Every workgroup is resident at once, so nothing waits
+//    behind a long sequence, and splitting only adds the merge.
+//  * More than one round: cover when its workgroups fill the slots a whole
+//    number of times or leave the last round at least 3/4 full; with the
+//    sequences dispatched longest first the drain is then short.  A last
+//    round mostly empty would run its few workgroups alone when the lengths
+//    are alike, so then the longest of 2048 / 1024 / 512 / 256 tokens that
+//    gives at least four workgroups per slot, counting full partitions of a
+//    longest sequence (the bound may exceed every actual length).
+//  * Fewer rows than half a round: the context is cut into enough parts for
+//    one workgroup per compute unit (256), parts of at least 256 tokens.
+// Measured (decode call, same process, interleaved; U[1, bound] contexts
+// unless stated): 64 x 32 heads at bounds 2600 / 3072 / 4096: 2048-token
+// partitions 3.2 / 3.3 / 4.1% slower than cover; 16 x 4096 uniform (half a
+// round): 512 2.6% slower than cover; 32 / 64 sequences of 8 KV heads x 8
+// query heads (half / one round on the matrix-core kernel): 256 / 512 5 / 11%
+// slower than cover; 4 x 4096 uniform (1/8 round): two parts of 2048 take
+// 19% less time than cover; 100 requests of 1001..1200 tokens sharing a
+// 1000-token prompt (3.1 rounds): 512 gives 10% more than cover.  Cover is
+// 5% slower than 512 in one measured case: 16 sequences with contexts
+// U[1, 4096] (the few longest sequences' workgroups then set the pace).
 int32_t default_partition(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                           int32_t block_size, int32_t max_context_len) {
     const int64_t rows = grid_rows(num_seqs, num_heads, num_kv_heads, head_dim, block_size);
     const int64_t slots = resident_slots(num_heads, num_kv_heads, head_dim, block_size);
-    {
-        const int32_t whole = (max_context_len + kPartitionQuantum - 1) / kPartitionQuantum * kPartitionQuantum;
-        const int32_t p1 = max_context_len <= 2560 && whole > 2048 ? whole : 2048;
-        const int64_t wgs = rows * (max_context_len > p1 ? ((int64_t)max_context_len + p1 - 1) / p1 : 1);
-        const int64_t tail = wgs % slots;
-        if (wgs >= 2 * slots && (tail == 0 || 4 * tail >= 3 * slots)) return p1;
+    const int64_t bound = max_context_len > 0 ? max_context_len : 1;
+    const int64_t cover64 = (bound + kPartitionQuantum - 1) / kPartitionQuantum * kPartitionQuantum;
+    const int32_t cover = (int32_t)(cover64 < 0x7fffff80 ? cover64 : 0x7fffff80);
+    if (rows <= 0) return cover;
+    if (2 * rows >= slots && rows <= slots) return cover;
+    if (rows > slots) {
+        const int64_t tail = rows % slots;
+        if (tail == 0 || 4 * tail >= 3 * slots) return cover;
+        const int32_t cands[] = {2048, 1024, 512, 256};
+        for (int32_t p : cands) {
+            const int64_t parts = bound / p > 0 ? bound / p : 1;
+            if (rows * parts >= 4 * slots) return p;
+        }
+        return 256;
     }
-    const int32_t cands[] = {2048, 1024, 512, 256};
-    for (int32_t p : cands) {
-        const int64_t parts = max_context_len / p > 0 ? max_context_len / p : 1;
-        if (rows * parts >= 4 * slots) return p;
-    }
-    return 256;
+    // fewer rows than half a round: one workgroup per compute unit
+    const int64_t parts = (256 + rows - 1) / rows;
+    int64_t p = (bound + parts - 1) / parts;
+    p = (p + kPartitionQuantum - 1) / kPartitionQuantum * kPartitionQuantum;
+    return (int32_t)(p < 256 ? 256 : p);
 }
 
 bool bad_geometry(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,

@@ -124,34 +124,38 @@ def test_workspace_size():
 
 
 def test_default_partition_keeps_the_gpu_busy():
-    """P1 when rows x ceil(max_len / P1) workgroups (rows: sequence x
-    query head, or x KV head on the grouped path; P1 = 2048, or max_len
-    rounded up to a multiple of 128 when that lies in (2048, 2560]) fill the
-    resident slots
-    (1024 for one query per KV head, 512 for groups of 2..16 at head_dim
-    128) at least twice, a whole number of times or with the last round at
-    least 3/4 full; otherwise the longest of 2048/1024/512/256 tokens with
-    >= 4 workgroups per slot, counting full partitions of the longest
-    sequence; 256 when even that is not reached."""
+    """With rows = sequences x query heads (x KV heads on the grouped path)
+    and slots = the workgroups resident at once (1024 for one query per KV
+    head, 512 for groups of 2..16 with blocks of 16 or more): "cover" (the
+    bound rounded up to 128: one partition, no merge) when the rows fill
+    half a round to one round, or more than one round a whole number of
+    times or with the last round at least 3/4 full; otherwise, above one
+    round, the longest of 2048/1024/512/256 tokens with >= 4 workgroups per
+    slot counting full partitions of the longest sequence; below half a
+    round, parts enough for one workgroup per compute unit (>= 256 tokens)."""
     L = pa.lib()
     assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2048) == 2048     # 2048 workgroups = 2 rounds
     assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2049) == 2176     # one partition covers the bound
-    assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2112) == 2176
+    assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2080) == 2176     # the decode benchmark's bound
     assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2560) == 2560
-    assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2561) == 2048     # 4096 = 4 rounds
+    assert L.pa_decode_default_partition(64, 32, 32, 128, 16, 2561) == 2688     # still 2 whole rounds
     assert L.pa_decode_default_partition(256, 64, 8, 128, 16, 2100) == 2176     # grouped: 2048 rows, 512 slots
-    assert L.pa_decode_default_partition(100, 32, 32, 128, 16, 1216) == 512     # 3.125 rounds at 2048
-    assert L.pa_decode_default_partition(120, 32, 32, 128, 16, 1216) == 2048    # 3.75: last round 3/4 full
+    assert L.pa_decode_default_partition(100, 32, 32, 128, 16, 1216) == 512     # 3.125 rounds: last nearly empty
+    assert L.pa_decode_default_partition(120, 32, 32, 128, 16, 1216) == 1280    # 3.75: last round 3/4 full
     assert L.pa_decode_default_partition(112, 32, 32, 128, 16, 1216) == 512     # 3.5: last round half full
-    assert L.pa_decode_default_partition(63, 32, 32, 128, 16, 2048) == 512      # 2016 < 2 rounds; 2016 x 4
+    assert L.pa_decode_default_partition(63, 32, 32, 128, 16, 2048) == 2048     # 1.97 rounds
     assert L.pa_decode_default_partition(256, 64, 8, 128, 16, 2048) == 2048     # grouped: 2048 rows, 512 slots
-    assert L.pa_decode_default_partition(64, 64, 8, 128, 16, 2048) == 512       # 512 rows x 4
-    assert L.pa_decode_default_partition(16, 32, 32, 128, 16, 4096) == 512      # 512 rows x 8
+    assert L.pa_decode_default_partition(64, 64, 8, 128, 16, 2048) == 2048      # grouped: one round
+    assert L.pa_decode_default_partition(32, 64, 8, 128, 16, 2048) == 2048      # grouped: half a round
+    assert L.pa_decode_default_partition(16, 32, 32, 128, 16, 4096) == 4096     # half a round: cover
+    assert L.pa_decode_default_partition(8, 32, 32, 128, 16, 4096) == 4096      # 256 rows: one per compute unit
+    assert L.pa_decode_default_partition(4, 32, 32, 128, 16, 4096) == 2048      # 128 rows: two parts
     assert L.pa_decode_default_partition(1, 8, 8, 128, 16, 1000) == 256
     assert L.pa_decode_default_partition(64, 32, 32, 64, 16, 2048) == 2048      # head_dim 64, one query per KV head
     assert L.pa_decode_default_partition(256, 64, 8, 64, 16, 2048) == 2048      # head_dim 64 grouped: 512 slots
     assert L.pa_decode_default_partition(64, 32, 7, 128, 16, 2048) == -1
-    for args in [(64, 32, 32, 128, 16, 2048), (256, 64, 8, 128, 16, 2048), (1, 8, 8, 128, 16, 1000)]:
+    for args in [(64, 32, 32, 128, 16, 2048), (256, 64, 8, 128, 16, 2048), (1, 8, 8, 128, 16, 1000),
+                 (3, 4, 4, 128, 16, 100000)]:
         assert L.pa_decode_default_partition(*args) % 128 == 0
 
 
