@@ -28,9 +28,12 @@
 //    buffers (32 KiB each) -- no registers hold a tile in flight and no LDS
 //    store instructions run.  Each thread issues 8 such loads per tile (4
 //    rows of K, 4 of V), waited for explicitly before the step's barrier;
-//    one barrier per tile.  A wave's 4 rows of one load
-//    share a table entry (blocks of 4 or more tokens), read a tile ahead
-//    with a scalar load.  The DMA writes lane i's 16 bytes at byte 16i, so
+//    one barrier per tile.  A wave's 4 rows of one load share a table entry
+//    (blocks of 4 or more tokens), read a tile ahead with a scalar load, so
+//    that (outside append mode) such a load is addressed as a scalar base
+//    (block, first row) plus a per-lane offset that is the same for every
+//    tile: no vector instruction computes a load address.  The DMA writes
+//    lane i's 16 bytes at byte 16i, so
 //    bank conflicts are avoided by choosing what each lane loads: position
 //    p of K row r holds the row's 16-byte chunk p ^ (r & 15), of V row r
 //    chunk p ^ 2(r & 3).  Rows past the context or with an id outside the
@@ -41,18 +44,21 @@
 //    registers.  S^T lands with each lane holding 8 scores of one row
 //    (tokens 4j..4j+3 and 16+4j..16+4j+3 of the tile) -- exactly that lane's
 //    A operand of P for a 32-token PV product, so the online softmax (base
-//    2) runs in place and P goes to the matrix core as fp16; the row sum
-//    adds the same rounded weights.  Row max and sum cross the 4 lanes of a
-//    row with v_permlane32_swap / v_permlane16_swap.  Tiles wholly before a
-//    wave's first row and wholly valid skip the masks; the running maximum
-//    moves lazily (only when a tile's exceeds it by a factor above 2^8), so
-//    O is rarely rescaled.
+//    2) runs in place and P goes to the matrix core as fp16.  The row max
+//    crosses the 4 lanes of a row with v_permlane32_swap /
+//    v_permlane16_swap; the row sum is one more product per 32-token slab,
+//    P times an all-ones operand, so it adds exactly the rounded weights
+//    the value products see, and no vector instruction sums them.  Tiles
+//    wholly before a wave's first row and wholly valid skip the masks;
+//    tiles with every token valid take the causal mask only (a compare and
+//    a select per score); the running maximum moves lazily (only when a
+//    tile's exceeds it by a factor above 2^8), so O is rarely rescaled, and
+//    the rescale factor is computed only then.
 //  * PV: output column n of d-tile c is d = 16c + n; the B operand (8
 //    tokens of one V column per lane) comes straight from the row-major V
 //    tile through two LDS transpose reads (ds_read_b64_tr_b16) per d-tile.
 //  * Each wave walks the tiles up to its own last row's position and writes
-//    its rows itself: 16 bytes per row, normalised by the row sums fetched
-//    with a cross-lane shuffle.
+//    its rows itself, normalised by the row sums it holds for them.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -138,7 +144,8 @@ typedef _Float16 half8_t_ __attribute__((ext_vector_type(8)));
 // and sum of its row and its share of the unnormalised output rows.
 template <int D>
 struct Softmax {
-    float m, l;                            // running max (base 2) and sum of row l % 16
+    float m;                               // running max (base 2) of row l % 16
+    float4_t l;                            // running sum of row 4*(l/16) + i in l[i] (any column)
     float4_t o[D / 16];                    // O[row 4*(l/16) + i][d = 16c + l % 16] in o[c][i]
 };
 
@@ -186,6 +193,25 @@ __device__ __forceinline__ void table_entries(int32_t (&e)[PGeo<D>::kStageRows],
     }
 }
 
+// One wave load of 16 bytes per lane from global memory straight into LDS
+// (lane i's bytes land at lds + 16 i), addressed as a uniform 64-bit base
+// plus a 32-bit per-lane offset, so that no vector instruction computes an
+// address.  Issued in inline asm (M0 holds the LDS address; no other code
+// of the kernel uses M0): the compiler does not track these loads, and the
+// kernel's explicit waits order them against the LDS reads.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <bool kStream>
+__device__ __forceinline__ void load_lds_saddr(const void* base, uint32_t lane_off, uint32_t lds_addr) {
+    if constexpr (kStream)
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(lane_off), "s"(base),
+                     "s"(lds_addr) : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(lane_off), "s"(base),
+                     "s"(lds_addr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // Fetch tile k (tokens kKvTile*k ..) from HBM into the LDS buffer `buf`;
 // `e` holds its table entries when B >= kRowsPerLoad (read a step earlier),
 // else every thread looks up its own row.  Rows past the context or with an id outside
@@ -204,6 +230,32 @@ __device__ __forceinline__ void fetch_tile(Staged<D>& st, unsigned char* buf, in
     constexpr int kLoadPolicy = kStream ? 2 : 0;
     PF_GEO(D);
     const int col = lane % kChunks;
+    if constexpr (!kAppend && B >= kRowsPerLoad) {
+        // the wave's rows of load i lie in one block: a uniform base and a
+        // per-lane offset (row within the load, swizzled chunk) that is the
+        // same for every tile
+#pragma unroll
+        for (int i = 0; i < kStageRows; ++i) {
+            const int t0 = stage_token0<D>(k, wave, i);
+            const int32_t phys = e[i];
+            const bool in_pool = (uint32_t)phys < (uint32_t)num_blocks;
+            const int r = stage_token0<D>(0, wave, i) + lane / kChunks;
+            const uint32_t rowb = (uint32_t)((lane / kChunks) * kD * 2);
+            const uint32_t lk = rowb + 16u * (uint32_t)(col ^ (r & kSwzK));
+            const uint32_t lv = rowb + 16u * (uint32_t)(col ^ (2 * (r & 3)));
+            // bytes from the head's first block: the block, then the load's first row in it
+            const uint64_t boff = (uint64_t)(uint32_t)(in_pool ? phys : 0) * (uint64_t)(blk_stride * 2) +
+                                  (uint32_t)((t0 % B) * kD * 2);
+            // a generic address of LDS carries the LDS offset in its low 32 bits
+            const uint32_t lds = (uint32_t)(uintptr_t)buf;
+            load_lds_saddr<kStream>(reinterpret_cast<const char*>(kbase) + boff, lk,
+                                    lds + (uint32_t)(stage_token0<D>(0, wave, i) * kPitch));
+            load_lds_saddr<kStream>(reinterpret_cast<const char*>(vbase) + boff, lv,
+                                    lds + (uint32_t)(kTileBytes + stage_token0<D>(0, wave, i) * kPitchV));
+            st.ok[i] = t0 + lane / kChunks < n && in_pool;
+        }
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < kStageRows; ++i) {
         const int t0 = stage_token0<D>(k, wave, i);        // uniform, a multiple of kRowsPerLoad
@@ -305,14 +357,13 @@ struct Rows {
     int pos;         // its position
 };
 
-typedef _Float16 half2_t_ __attribute__((ext_vector_type(2)));
 
 constexpr float kLazyMax = 8.f;           // log2 slack of the running maximum
 
-// Cross-lane reductions over the four lanes l % 16 + 16 j (j = 0..3) that
+// Cross-lane maximum over the four lanes l % 16 + 16 j (j = 0..3) that
 // hold one row's scores: v_permlane32_swap pairs lanes l and l ^ 32,
 // v_permlane16_swap lanes l and l ^ 16; each returns the two values of the
-// pair in its two results, so max / sum of them is the pair's.
+// pair in its two results, so the maximum of them is the pair's.
 
 __device__ __forceinline__ float row_max4(float x) {
     const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -321,12 +372,6 @@ __device__ __forceinline__ float row_max4(float x) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-__device__ __forceinline__ float row_sum4(float x) {
-    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
 
 typedef short v4s_ __attribute__((ext_vector_type(4)));
 
@@ -405,6 +450,83 @@ __device__ __forceinline__ void tr_reads(v4s_ (&r)[8 * kG], const uint32_t (&a)[
 #undef PF_TR16
 }
 
+// Online softmax of one 16-row group's scores of a tile (kMask as for
+// consume_lds_tile): masks, running maximum, the rescale of O and l when the
+// maximum moved, and the fp16 weights P.
+template <int D, int kMask>
+__device__ __forceinline__ void row_softmax(Softmax<D>& st, half8_t_ (&p)[PGeo<D>::kKvTile / 32],
+                                            float4_t (&s2)[PGeo<D>::kKvTile / 16], const unsigned char* flags,
+                                            int t0, float c_log2, int j, const Rows& rw) {
+    PF_GEO(D);
+    constexpr int NS = kKvTile / 32;
+    // raw scores, -inf where masked; token 16h + 4j + e of the tile is kept
+    // when at or before the row's position: 16h + e <= lim
+    if constexpr (kMask != 0) {
+        const int lim = rw.live ? rw.pos - t0 - 4 * j : -1;
+        if constexpr (kMask == 1) {
+            // in place (a compare and a select per score, the score's own
+            // register): the unmasked and masked tiles then leave the scores
+            // in the same registers, with no copies where they meet
+            const float ninf = -INFINITY;
+#pragma unroll
+            for (int h = 0; h < 2 * NS; ++h)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    asm volatile("v_cmp_le_i32 vcc, %1, %2\n\tv_cndmask_b32 %0, %3, %0, vcc"
+                                 : "+v"(s2[h][e])
+                                 : "i"(16 * h + e), "v"(lim), "v"(ninf)
+                                 : "vcc");
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2 * NS; ++h) {
+                // flags of tokens 16h + 4j .. +3, one byte each
+                const uint32_t fl = *reinterpret_cast<const uint32_t*>(flags + 16 * h + 4 * j);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool keep = ((fl >> (8 * e)) & 0xffu) && 16 * h + e <= lim;
+                    s2[h][e] = keep ? s2[h][e] : -INFINITY;
+                }
+            }
+        }
+    }
+    float mt = s2[0][0];
+#pragma unroll
+    for (int h = 0; h < 2 * NS; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mt = fmaxf(mt, s2[h][e]);
+    mt = row_max4(mt) * c_log2;                 // c > 0: the maximum of the scaled scores
+    // The running maximum moves only when the tile's exceeds it by more than
+    // kLazyMax: the weights stay below 2^kLazyMax (fine in fp16, summed in
+    // fp32) and the rescale of O and l is rare after the first tiles.
+    const float m_new = fmaxf(st.m, mt);
+    const bool bump = m_new > st.m + kLazyMax;  // also the first finite maximum
+    const float m_run = bump ? m_new : st.m;
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    if (__any(bump)) {
+        const float alpha = bump ? fast_exp2(st.m - m_use) : 1.f;
+        float ar[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ar[e] = __shfl(alpha, 4 * j + e);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st.l[e] *= ar[e];
+#pragma unroll
+        for (int c = 0; c < kDTiles; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st.o[c][e] *= ar[e];
+    }
+    st.m = m_run;
+#pragma unroll
+    for (int h = 0; h < 2 * NS; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; e += 2) {
+            // sub-tile u = h / 2 takes halves 2u (k 0..3 of each lane group) and 2u+1 (k 4..7)
+            const float w0 = fast_exp2(__builtin_fmaf(s2[h][e], c_log2, -m_use));
+            const float w1 = fast_exp2(__builtin_fmaf(s2[h][e + 1], c_log2, -m_use));
+            p[h / 2][4 * (h % 2) + e] = (_Float16)w0;
+            p[h / 2][4 * (h % 2) + e + 1] = (_Float16)w1;
+        }
+}
+
 // Consume one LDS tile for the wave's kNT groups of 16 rows on
 // v_mfma_f32_16x16x32_f16.  Every operand read from LDS feeds kNT products.
 //   QK, per 16-token half h: S^T[token][row] = sum_d K[token][d] Q[row][d];
@@ -412,14 +534,22 @@ __device__ __forceinline__ void tr_reads(v4s_ (&r)[8 * kG], const uint32_t (&a)[
 //   PV, per 32-token slab u: k = 32 tokens; lane (n, j) supplies P[row
 //     n][tokens 32u + 4j..4j+3 and 32u + 16+4j..16+4j+3] -- exactly the
 //     scores it holds -- and V rows of the same tokens at column 16c + n for
-//     d-tile c (LDS transpose reads).
-// `interior` (uniform): every token of the tile is valid and at or before
-// the first row's position, so no score is masked.  The exponent of a
-// weight is one FMA of the raw score: c = scale * log2(e) > 0, so the raw
-// maximum times c is the maximum of the scaled scores, and -inf stays -inf.
+//     d-tile c (LDS transpose reads).  One more product per slab with an
+//     all-ones B operand adds each row's weights into the running sum l (a
+//     d-tile whose every column is the row sum), so that no vector
+//     instruction sums them.
+// kMask: 0 = the tile lies wholly at or before the wave's first row and
+// every token is valid, no score is masked; 1 = every token is valid, only
+// the causal mask (and rows past the wave's last) applies; 2 = some token
+// is past the context or behind an id outside the pool: the flags too.
+// (Each case runs its own copy of the softmax, so that differently masked
+// scores are never merged into one set of registers.)
+// The exponent of a weight is one FMA of the raw score: c = scale *
+// log2(e) > 0, so the raw maximum times c is the maximum of the scaled
+// scores, and -inf stays -inf.
 template <int D>
 __device__ __forceinline__ void consume_lds_tile(Softmax<D> (&st)[PGeo<D>::kNT], const unsigned char* buf,
-                                                 const unsigned char* flags, int t0, bool interior,
+                                                 const unsigned char* flags, int t0, int mask,
                                                  const half8_t_ (&qb)[PGeo<D>::kNT][PGeo<D>::kQk], float c_log2,
                                                  int lane, const Rows (&rw)[PGeo<D>::kNT]) {
     PF_GEO(D);
@@ -447,62 +577,20 @@ __device__ __forceinline__ void consume_lds_tile(Softmax<D> (&st)[PGeo<D>::kNT],
     half8_t_ p[kNT][NS];
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
-        // raw scores, -inf where masked
-        float sc[8 * NS];
-        if (interior) {
-#pragma unroll
-            for (int h = 0; h < 2 * NS; ++h)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sc[4 * h + e] = s2[t][h][e];
-        } else {
-#pragma unroll
-            for (int h = 0; h < 2 * NS; ++h) {
-                // flags of tokens 16h + 4j .. +3, one byte each
-                const uint32_t fl = *reinterpret_cast<const uint32_t*>(flags + 16 * h + 4 * j);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int tok = 16 * h + 4 * j + e;
-                    const bool keep = rw[t].live && ((fl >> (8 * e)) & 0xffu) && t0 + tok <= rw[t].pos;
-                    sc[4 * h + e] = keep ? s2[t][h][e] : -INFINITY;
-                }
-            }
-        }
-        float mt = sc[0];
-#pragma unroll
-        for (int i = 1; i < 8 * NS; ++i) mt = fmaxf(mt, sc[i]);
-        mt = row_max4(mt) * c_log2;             // c > 0: the maximum of the scaled scores
-        // The running maximum moves only when the tile's exceeds it by more
-        // than kLazyMax: the weights stay below 2^kLazyMax (fine in fp16,
-        // summed in fp32) and the rescale of O is rare after the first tiles.
-        const float m_new = fmaxf(st[t].m, mt);
-        const bool bump = m_new > st[t].m + kLazyMax;   // also the first finite maximum
-        const float m_run = bump ? m_new : st[t].m;
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        const float alpha = bump ? fast_exp2(st[t].m - m_use) : 1.f;
-        float lt = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8 * NS; i += 2) {
-            // sub-tile u = i / 8 takes halves 2u (k 0..3 of each lane group) and 2u+1 (k 4..7)
-            const float w0 = fast_exp2(__builtin_fmaf(sc[i], c_log2, -m_use));
-            const float w1 = fast_exp2(__builtin_fmaf(sc[i + 1], c_log2, -m_use));
-            const half2_t_ w = {(_Float16)w0, (_Float16)w1};
-            p[t][i / 8][i % 8] = w[0];
-            p[t][i / 8][i % 8 + 1] = w[1];
-            lt = __builtin_amdgcn_fdot2(w, half2_t_{(_Float16)1.f, (_Float16)1.f}, lt, false);  // the rounded weights
-        }
-        lt = row_sum4(lt);
-        st[t].l = st[t].l * alpha + lt;
-        st[t].m = m_run;
-        if (__any(bump)) {
-            float ar[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ar[e] = __shfl(alpha, 4 * j + e);
-#pragma unroll
-            for (int c = 0; c < kDTiles; ++c)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) st[t].o[c][e] *= ar[e];
-        }
+        if (mask == 0)
+            row_softmax<D, 0>(st[t], p[t], s2[t], flags, t0, c_log2, j, rw[t]);
+        else if (mask == 1)
+            row_softmax<D, 1>(st[t], p[t], s2[t], flags, t0, c_log2, j, rw[t]);
+        else
+            row_softmax<D, 2>(st[t], p[t], s2[t], flags, t0, c_log2, j, rw[t]);
     }
+    // the row sums: P times an all-ones operand, for every slab
+    const half8_t_ ones = {(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f,
+                           (_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+#pragma unroll
+        for (int t = 0; t < kNT; ++t) st[t].l = __builtin_amdgcn_mfma_f32_16x16x32_f16(p[t][u], ones, st[t].l, 0, 0, 0);
     // PV with the V operand read by ds_read_b64_tr_b16: within each 16 lanes
     // it hands lane i element i%4 of the 8-byte pieces of lanes i/4 + 4e,
     // e = 0..3.  Lane 4e + q of lane group j points at V[token tb + e][16c +
@@ -662,7 +750,7 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
         st[t].m = -INFINITY;
-        st[t].l = 0.f;
+        st[t].l = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < kDTiles; ++c) st[t].o[c] = float4_t{0.f, 0.f, 0.f, 0.f};
     }
@@ -716,16 +804,15 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
         if constexpr (B >= kRowsPerLoad)
             if (k + 2 < k_end) table_entries<D, B>(e, k + 2, wave, n, trow);
         if (k < my_end) {
-            // uniform: tile below the wave's first row and wholly valid
-            bool interior = k * kKvTile + kKvTile - 1 <= first_pos;
-            if (interior) {
-                bool all_ok = true;          // the flags of tokens 16h + 4*jg .. +3, for every h
+            // uniform: every token of the tile valid; the tile wholly at or
+            // before the wave's first row
+            bool all_ok = true;              // the flags of tokens 16h + 4*jg .. +3, for every h
 #pragma unroll
-                for (int h = 0; h < kKvTile / 16; ++h)
-                    all_ok = all_ok && *reinterpret_cast<const uint32_t*>(cf + 16 * h + 4 * jg) == 0x01010101u;
-                interior = __all(all_ok);
-            }
-            consume_lds_tile<D>(st, cb, cf, k * kKvTile, interior, qb, c_log2, lane, rw);
+            for (int h = 0; h < kKvTile / 16; ++h)
+                all_ok = all_ok && *reinterpret_cast<const uint32_t*>(cf + 16 * h + 4 * jg) == 0x01010101u;
+            const bool tile_ok = __all(all_ok);
+            const bool below = k * kKvTile + kKvTile - 1 <= first_pos;
+            consume_lds_tile<D>(st, cb, cf, k * kKvTile, tile_ok ? (below ? 0 : 1) : 2, qb, c_log2, lane, rw);
         }
         PA_WAIT_VM(0);
         // append mode: the new tokens of tile k this workgroup owns go to the
@@ -753,7 +840,7 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int rr = 4 * jg + e;
-                const float L = __shfl(st[t].l, rr);
+                const float L = st[t].l[e];
                 const float M = __shfl(st[t].m, rr);
                 if (16 * t + rr >= rows) continue;
                 const int rwi = row0 + 16 * t + rr;
@@ -771,13 +858,13 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
     }
 
     // Rows 16t + 4*jg + e of the wave live in this lane's st[t].o[c][e] at
-    // column 16c + nrow; their sums sit in lanes 4*jg + e.
+    // column 16c + nrow, their sums in st[t].l[e].
 #pragma unroll
     for (int t = 0; t < kNT; ++t)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int rr = 4 * jg + e;
-            const float L = __shfl(st[t].l, rr);
+            const float L = st[t].l[e];
             if (16 * t + rr >= rows) continue;
             const int rwi = row0 + 16 * t + rr;
             const int64_t orow = ((int64_t)q0 + rwi / g) * num_heads + (int64_t)kvh * g + rwi % g;

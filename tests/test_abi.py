@@ -242,6 +242,10 @@ def test_prefill_workspace_size():
     per (token, head, context part), two 256-byte aligned regions."""
     L = pa.lib()
     assert L.pa_prefill_workspace_size(15360, 32, 32, 32, 128, 16, 49, 774) == 0        # 32 x 32 x 7 = 7168 workgroups
+    # longer chunks split too while their workgroups fill at most half the 512 resident slots: 300 rows per KV
+    # head are 3 row tiles, 3 x 4 x 3 = 36 workgroups, contexts up to 3008 tokens
+    n3 = L.pa_prefill_workspace_size(561, 3, 4, 4, 128, 16, 188, 300)
+    assert n3 > 0 and n3 % 256 == 0
     n = L.pa_prefill_workspace_size(64, 4, 32, 32, 128, 16, 512, 16)                  # 128 workgroups, 8192 tokens
     parts = n // (64 * 32 * (128 + 2) * 4)
     assert parts >= 2 and n % 256 == 0 and n >= 64 * 32 * parts * (128 + 2) * 4

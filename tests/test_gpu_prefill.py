@@ -148,20 +148,29 @@ def test_prefill_rising_scores_move_the_running_maximum():
     assert_attention_close(out, ref, "rising scores")
 
 
-@pytest.mark.parametrize("H,Hkv,D", [(8, 2, 128), (4, 4, 128), (16, 8, 128), (8, 2, 64), (8, 2, 256)])
-def test_prefill_split_context(H, Hkv, D):
-    """Short chunks over long contexts with few sequences: the context is
-    split into parts merged by a second kernel.  Against the oracle, against
-    the unsplit kernel (same math, other summation order), bit for bit when
+SHORT_CHUNKS = (8, 40, 1)      # one row tile per (KV head, sequence) at most
+LONG_CHUNKS = (300, 260, 1)    # several row tiles, each walking the split context
+
+
+@pytest.mark.parametrize("H,Hkv,D,ms", [(8, 2, 128, SHORT_CHUNKS), (4, 4, 128, SHORT_CHUNKS),
+                                        (16, 8, 128, SHORT_CHUNKS), (8, 2, 64, SHORT_CHUNKS),
+                                        (8, 2, 256, SHORT_CHUNKS), (4, 4, 128, LONG_CHUNKS),
+                                        (8, 2, 128, LONG_CHUNKS), (4, 4, 64, LONG_CHUNKS),
+                                        (8, 2, 256, LONG_CHUNKS)])
+def test_prefill_split_context(H, Hkv, D, ms):
+    """Chunks over long contexts with few sequences: the context is split
+    into parts merged by a second kernel.  Against the oracle, against the
+    unsplit kernel (same math, other summation order), bit for bit when
     repeated, and through one workspace reused by a smaller call."""
     dev = device()
     lens_l = [3000, 2500, 1777]
-    ms = [8, 40, 1]
+    ms = list(ms)
     case = workloads.random_case(91 + H + D, lens_l, H, Hkv, D, 16)
     kc, vc, tables, lens = _oracle_cache(case)
     q, qs = _queries(91, ms, H, D)
     T, W = int(qs[-1]), tables.shape[1]
     need = pa.pa_prefill_workspace_size(T, 3, H, Hkv, D, 16, W, max(ms))
+    say(f"prefill split H={H}/{Hkv} D={D} ms={ms}: workspace {need} bytes")
     assert need > 0                                                  # this batch splits
     ws = torch.empty(need, dtype=torch.uint8, device=dev)
     split = _gpu_prefill(dev, q, kc, vc, tables, lens, qs, case.scale, workspace=ws)
@@ -172,7 +181,8 @@ def test_prefill_split_context(H, Hkv, D):
     again = _gpu_prefill(dev, q, kc, vc, tables, lens, qs, case.scale, workspace=ws)
     assert np.array_equal(bits(split), bits(again))
     # the same workspace for a smaller batch (first two sequences)
-    q2, qs2 = np.ascontiguousarray(q[:48]), np.array([0, 8, 48], np.int32)
+    m01 = ms[0] + ms[1]
+    q2, qs2 = np.ascontiguousarray(q[:m01]), np.array([0, ms[0], m01], np.int32)
     t2, l2 = np.ascontiguousarray(tables[:2]), np.ascontiguousarray(lens[:2])
     small = _gpu_prefill(dev, q2, kc, vc, t2, l2, qs2, case.scale, workspace=ws)
     assert_attention_close(small, oracle.prefill(q2, kc, vc, t2, l2, qs2, case.scale), "split, smaller batch")
@@ -341,14 +351,15 @@ def test_prefill_append_matches_oracle(D, B, H, Hkv, chunk):
     assert_attention_close(two, ref, "two calls")
 
 
-@pytest.mark.parametrize("H,Hkv", [(8, 2), (16, 8)])
-def test_prefill_append_split_context(H, Hkv):
-    """Short chunks over long contexts, context split into parts: each new
-    token is written by the part whose tiles hold it; with and without a
+@pytest.mark.parametrize("H,Hkv,ms", [(8, 2, SHORT_CHUNKS), (16, 8, SHORT_CHUNKS), (4, 4, LONG_CHUNKS),
+                                      (6, 3, LONG_CHUNKS)])
+def test_prefill_append_split_context(H, Hkv, ms):
+    """Chunks over long contexts, context split into parts: each new token
+    is written by the part whose tiles hold it; with and without a
     workspace."""
     dev = device()
     lens_l = [3000, 2500, 1777]
-    ms = [8, 40, 1]
+    ms = list(ms)
     case = workloads.random_case(191 + H, lens_l, H, Hkv, 128, 16)
     kc0, vc0, kc1, vc1, key, value, tables, lens = _append_case(case, ms)
     q, qs = _queries(191, ms, H, 128)
