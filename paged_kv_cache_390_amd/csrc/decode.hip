@@ -569,10 +569,10 @@ int64_t grid_rows(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int
 // for the grouped-query kernel, as many as its registers allow
 int64_t resident_slots(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size) {
     if (!uses_mfma(num_heads, num_kv_heads, head_dim, block_size)) return 256LL * 4;
-    // the matrix-core kernel's registers: 4 workgroups per CU at head_dim 64
-    // with tiles across blocks, 1 at head_dim 256 with tiles across blocks,
-    // 2 otherwise
-    if (block_size < 16) return 256LL * (head_dim == 64 ? 4 : head_dim == 256 ? 1 : 2);
+    // the matrix-core kernel's registers: 4 workgroups per CU at head_dim 64,
+    // 1 at head_dim 256 with tiles across blocks, 2 otherwise
+    if (head_dim == 64) return 256LL * 4;
+    if (block_size < 16 && head_dim == 256) return 256LL * 1;
     return 256LL * 2;
 }
 

@@ -72,15 +72,16 @@ __device__ __forceinline__ half8_t as_h8(u32x4 u) { return __builtin_bit_cast(ha
 
 // Per head_dim: QK MFMAs (= K loads of 16 bytes per lane) per tile, V values
 // per lane and token (= PV d-tiles), and tiles in flight per wave beside the
-// one being consumed (bounded by the 256 VGPRs of 2 waves per SIMD: a tile
-// is D/4 VGPRs, O D/4, Q^T D/8).
+// one being consumed (a tile is D/4 VGPRs, O D/4, Q^T D/8: at head_dim 64
+// two, so that four workgroups fit a CU; above, what the 256 VGPRs of two
+// waves per SIMD leave).
 template <int D>
 struct Geo {
     static constexpr int kQk = D / 32;
     static constexpr int kVpl = D / 16;
     static constexpr int kDT = D / 16;
     static constexpr int kVDw = kVpl / 2;            // dwords of V per lane and token
-    static constexpr int kFlight = D == 64 ? 8 : D == 128 ? 3 : 1;
+    static constexpr int kFlight = D == 64 ? 2 : D == 128 ? 3 : 1;
     // head_dim 256: the Q^T operands (D/8 VGPRs) are read from LDS for each
     // tile instead of held, so that two waves fit a SIMD
     static constexpr bool kQInLds = D >= 256;
@@ -276,8 +277,13 @@ __device__ __forceinline__ void consume_tile(Softmax<D>& st, Tile<D>& t, const Q
 // new_stride + h * D) instead of the cache; the workgroup whose partition
 // holds it folds it in as a one-token tile and writes it into the cache
 // through k_write / v_write.  The cache is read for positions < n - 1 only.
+// Workgroups per CU: 4 at head_dim 64 (two tiles in flight per wave, ~120
+// VGPRs: more resident workgroups hide each one's start and drain better
+// than deeper pipelines -- 8 tiles in flight at 2 workgroups per CU ran 11-14%
+// slower), 2 at 128 (3 tiles in flight; 1 tile at 3 workgroups per CU
+// measured within 1%), 2 at 256 with tiles in one block, 1 otherwise.
 template <int D, int B, bool kAppend>
-__global__ void __launch_bounds__(kThreads, (D >= 256 && B < kTile) ? 1 : 2)
+__global__ void __launch_bounds__(kThreads, D == 64 ? 4 : (D >= 256 && B < kTile) ? 1 : 2)
 decode_gqa_mfma_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, float* __restrict__ ws_acc,
                        const int32_t* __restrict__ order, const _Float16* __restrict__ q, const _Float16* __restrict__ k_cache,
                        const _Float16* __restrict__ v_cache, const int32_t* __restrict__ tables,

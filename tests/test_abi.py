@@ -147,6 +147,9 @@ def test_default_partition_keeps_the_gpu_busy():
     assert L.pa_decode_default_partition(256, 64, 8, 128, 16, 2048) == 2048     # grouped: 2048 rows, 512 slots
     assert L.pa_decode_default_partition(64, 64, 8, 128, 16, 2048) == 2048      # grouped: one round
     assert L.pa_decode_default_partition(32, 64, 8, 128, 16, 2048) == 2048      # grouped: half a round
+    # head_dim 64 on the matrix cores: 4 workgroups per CU, 1024 slots
+    assert L.pa_decode_default_partition(512, 64, 8, 64, 16, 2048) == 2048      # 4096 rows: 4 whole rounds
+    assert L.pa_decode_default_partition(160, 64, 8, 64, 16, 2048) == 512       # 1280 rows: 4 workgroups per slot
     assert L.pa_decode_default_partition(16, 32, 32, 128, 16, 4096) == 4096     # half a round: cover
     assert L.pa_decode_default_partition(8, 32, 32, 128, 16, 4096) == 4096      # 256 rows: one per compute unit
     assert L.pa_decode_default_partition(4, 32, 32, 128, 16, 4096) == 2048      # 128 rows: two parts
