@@ -876,9 +876,13 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
 
 // Merge of the context parts: output row (token i of sequence s, head h)
 // combines the (m, l, O) its row tile's parts left, weighted by exp2(m_p -
-// max m).  One workgroup of D threads (one thread per column) per (head,
-// sequence, 16 tokens).
-constexpr int kMergeTokens = 16;
+// max m).  One thread per (token, column): a 256-thread workgroup covers
+// 256 / D tokens of one (head, sequence), and the z dimension of the grid
+// strides over the tokens.  (With a thread walking 16 tokens in turn, each
+// waiting on the previous one's loads, the merge took ~28 us of a ~110 us
+// chunked-prefill call.)
+constexpr int kMergeThreads = 256;
+constexpr int kMergeGridZ = 65535;
 
 template <int D>
 __global__ void __launch_bounds__(256)
@@ -887,9 +891,10 @@ prefill_merge_kernel(_Float16* __restrict__ out, const float* __restrict__ ws_ml
                      int32_t num_heads, int32_t num_kv_heads, int32_t max_query_len, int64_t len_cap,
                      int32_t tiles_per_part, int32_t num_parts) {
     PF_GEO(D);
+    constexpr int kTok = kMergeThreads / D;      // tokens per workgroup
     const int h = blockIdx.x;
     const int s = blockIdx.y;
-    const int d = threadIdx.x;
+    const int d = threadIdx.x % D;
     const int g = num_heads / num_kv_heads;
     const int32_t q0 = query_start[s];
     const int32_t q1 = query_start[s + 1];
@@ -899,8 +904,7 @@ prefill_merge_kernel(_Float16* __restrict__ out, const float* __restrict__ ws_ml
     if (m > max_query_len || n < m || (int64_t)n > len_cap) return;   // NaN rows, written by the first kernel
     const int base_pos = n - m;
     const int rows_all = m * g;
-    const int i_end = min(m, (int)(blockIdx.z + 1) * kMergeTokens);
-    for (int i = blockIdx.z * kMergeTokens; i < i_end; ++i) {
+    for (int i = (int)blockIdx.z * kTok + (int)threadIdx.x / D; i < m; i += (int)gridDim.z * kTok) {
         // the row tile of this row, and how many parts its workgroups covered
         const int r = i * g + h % g;
         const int grow0 = (r / kRowsPerGroup) * kRowsPerGroup;
@@ -979,6 +983,14 @@ HostGeo host_geo(int32_t d) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// z dimension of the merge kernel's grid: one step per 256 / head_dim
+// tokens, capped (the kernel strides over the rest)
+int64_t merge_grid_z(int32_t max_query_len, int32_t head_dim) {
+    const int64_t tok = kMergeThreads / head_dim;
+    const int64_t z = ((int64_t)max_query_len + tok - 1) / tok;
+    return z < 1 ? 1 : z > kMergeGridZ ? kMergeGridZ : z;
+}
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -1137,8 +1149,8 @@ int prefill_impl(const char* fn, void* out, const void* q, int32_t num_tokens, c
     if (P.num_parts > 1) {
         hipLaunchKernelGGL(pick_merge(head_dim),
                            dim3((unsigned)num_heads, (unsigned)num_seqs,
-                                (unsigned)((max_query_len + kMergeTokens - 1) / kMergeTokens)),
-                           dim3((unsigned)head_dim), 0, st, static_cast<_Float16*>(out), (const float*)ws_ml,
+                                (unsigned)merge_grid_z(max_query_len, head_dim)),
+                           dim3((unsigned)kMergeThreads), 0, st, static_cast<_Float16*>(out), (const float*)ws_ml,
                            (const float*)ws_acc,
                            num_tokens, context_lens, query_start, num_heads, num_kv_heads, max_query_len, len_cap,
                            P.tiles_per_part, P.num_parts);
