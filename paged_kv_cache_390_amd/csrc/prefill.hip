@@ -355,6 +355,7 @@ __device__ __forceinline__ void write_own_rows(const Staged<D>& st, const unsign
 struct Rows {
     bool live;       // the row (l % 16 of its group) exists
     int pos;         // its position
+    int rel;         // pos - 4 * (l / 16)
 };
 
 
@@ -365,11 +366,22 @@ constexpr float kLazyMax = 8.f;           // log2 slack of the running maximum
 // v_permlane16_swap lanes l and l ^ 16; each returns the two values of the
 // pair in its two results, so the maximum of them is the pair's.
 
+__device__ __forceinline__ float max2(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 __device__ __forceinline__ float row_max4(float x) {
     const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const float y = max2(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return max2(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 
@@ -450,55 +462,107 @@ __device__ __forceinline__ void tr_reads(v4s_ (&r)[8 * kG], const uint32_t (&a)[
 #undef PF_TR16
 }
 
-// Online softmax of one 16-row group's scores of a tile (kMask as for
+// Causal and flag masks of the scores of tokens 16h + 4j + 0..3 of a tile
+// (lane group j), in place: a token is kept when 16h + e <= lim, and in mode
+// 2 only when its flag is set too.  One asm block per 16-token half with
+// the mode tested inside it: the compiler sees no branch, so every mode
+// leaves the scores in the registers they came in (a branch here made it
+// copy all 16 scores of a group on every tile).  Mode 2 reads the flag word
+// from LDS and waits for it in the same block.  The scores come from
+// matrix-core products, whose results a vector instruction may read only some
+// cycles after the product issued; the compiler pads its own instructions for
+// this but not those inside inline asm, so the causal path opens with 22 wait
+// states (the most any product here needs) and the flag path's LDS wait
+// covers it.
+#define PF_MASK_H(H)                                                                                  \
+    asm volatile(                                                                                    \
+        "s_cmp_eq_u32 %[mode], 0\n\t"                                                                \
+        "s_cbranch_scc1 3f\n\t"                                                                      \
+        "s_cmp_eq_u32 %[mode], 1\n\t"                                                                \
+        "s_cbranch_scc1 2f\n\t"                                                                      \
+        "ds_read_b32 %[fl], %[fa] offset:%[fo]\n\t"                                                  \
+        "s_waitcnt lgkmcnt(0)\n\t"                                                                   \
+        "v_bfe_u32 %[t], %[fl], 0, 8\n\t"                                                           \
+        "v_cmp_ne_u32 vcc, 0, %[t]\n\t"                                                             \
+        "v_cndmask_b32 %[t], -1, %[lim], vcc\n\t"                                                   \
+        "v_cmp_le_i32 vcc, %[i0], %[t]\n\t"                                                         \
+        "v_cndmask_b32 %0, %[ninf], %0, vcc\n\t"                                                    \
+        "v_bfe_u32 %[t], %[fl], 8, 8\n\t"                                                           \
+        "v_cmp_ne_u32 vcc, 0, %[t]\n\t"                                                             \
+        "v_cndmask_b32 %[t], -1, %[lim], vcc\n\t"                                                   \
+        "v_cmp_le_i32 vcc, %[i1], %[t]\n\t"                                                         \
+        "v_cndmask_b32 %1, %[ninf], %1, vcc\n\t"                                                    \
+        "v_bfe_u32 %[t], %[fl], 16, 8\n\t"                                                          \
+        "v_cmp_ne_u32 vcc, 0, %[t]\n\t"                                                             \
+        "v_cndmask_b32 %[t], -1, %[lim], vcc\n\t"                                                   \
+        "v_cmp_le_i32 vcc, %[i2], %[t]\n\t"                                                         \
+        "v_cndmask_b32 %2, %[ninf], %2, vcc\n\t"                                                    \
+        "v_bfe_u32 %[t], %[fl], 24, 8\n\t"                                                          \
+        "v_cmp_ne_u32 vcc, 0, %[t]\n\t"                                                             \
+        "v_cndmask_b32 %[t], -1, %[lim], vcc\n\t"                                                   \
+        "v_cmp_le_i32 vcc, %[i3], %[t]\n\t"                                                         \
+        "v_cndmask_b32 %3, %[ninf], %3, vcc\n\t"                                                    \
+        "s_branch 3f\n"                                                                              \
+        "2:\n\t"                                                                                    \
+        "s_nop 7\n\t"                                                                               \
+        "s_nop 7\n\t"                                                                               \
+        "s_nop 5\n\t"                                                                               \
+        "v_cmp_le_i32 vcc, %[i0], %[lim]\n\t"                                                       \
+        "v_cndmask_b32 %0, %[ninf], %0, vcc\n\t"                                                    \
+        "v_cmp_le_i32 vcc, %[i1], %[lim]\n\t"                                                       \
+        "v_cndmask_b32 %1, %[ninf], %1, vcc\n\t"                                                    \
+        "v_cmp_le_i32 vcc, %[i2], %[lim]\n\t"                                                       \
+        "v_cndmask_b32 %2, %[ninf], %2, vcc\n\t"                                                    \
+        "v_cmp_le_i32 vcc, %[i3], %[lim]\n\t"                                                       \
+        "v_cndmask_b32 %3, %[ninf], %3, vcc\n"                                                       \
+        "3:"                                                                                         \
+        : "+v"(s2[H][0]), "+v"(s2[H][1]), "+v"(s2[H][2]), "+v"(s2[H][3]), [fl] "=&v"(fl_), [t] "=&v"(t_) \
+        : [mode] "s"(mode), [lim] "v"(lim), [ninf] "v"(ninf), [fa] "v"(fa), [fo] "i"(16 * (H)),       \
+          [i0] "i"(16 * (H)), [i1] "i"(16 * (H) + 1), [i2] "i"(16 * (H) + 2), [i3] "i"(16 * (H) + 3)   \
+        : "vcc", "scc", "memory")
+
+template <int NH>
+__device__ __forceinline__ void mask_scores(float (&s2)[NH][4], int mode, int lim, uint32_t fa) {
+    static_assert(NH == 2 || NH == 4, "16-token halves per tile");
+    const float ninf = -INFINITY;
+    uint32_t fl_, t_;
+    PF_MASK_H(0);
+    PF_MASK_H(1);
+    if constexpr (NH == 4) {
+        PF_MASK_H(2);
+        PF_MASK_H(3);
+    }
+}
+#undef PF_MASK_H
+
+// Online softmax of one 16-row group's scores of a tile (mode as for
 // consume_lds_tile): masks, running maximum, the rescale of O and l when the
 // maximum moved, and the fp16 weights P.
-template <int D, int kMask>
+template <int D>
 __device__ __forceinline__ void row_softmax(Softmax<D>& st, half8_t_ (&p)[PGeo<D>::kKvTile / 32],
-                                            float4_t (&s2)[PGeo<D>::kKvTile / 16], const unsigned char* flags,
-                                            int t0, float c_log2, int j, const Rows& rw) {
+                                            float (&s2)[PGeo<D>::kKvTile / 16][4], const unsigned char* flags,
+                                            int t0, int mode, float c_log2, int j, const Rows& rw) {
     PF_GEO(D);
     constexpr int NS = kKvTile / 32;
     // raw scores, -inf where masked; token 16h + 4j + e of the tile is kept
-    // when at or before the row's position: 16h + e <= lim
-    if constexpr (kMask != 0) {
-        const int lim = rw.live ? rw.pos - t0 - 4 * j : -1;
-        if constexpr (kMask == 1) {
-            // in place (a compare and a select per score, the score's own
-            // register): the unmasked and masked tiles then leave the scores
-            // in the same registers, with no copies where they meet
-            const float ninf = -INFINITY;
+    // when at or before the row's position: 16h + e <= lim = pos - t0 - 4j
+    // (-1 for a row that does not exist)
+    const uint32_t fa = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) unsigned char*)(flags + 4 * j);
+    mask_scores<2 * NS>(s2, __builtin_amdgcn_readfirstlane(mode), rw.live ? rw.rel - t0 : -1, fa);  // mode: uniform
+    // the maximum as v_max3 chains (IEEE-mode fmaxf would first quiet every
+    // operand with a v_max of itself)
+    float mt = max3(s2[0][0], s2[0][1], s2[0][2]);
+    mt = max2(mt, s2[0][3]);
 #pragma unroll
-            for (int h = 0; h < 2 * NS; ++h)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    asm volatile("v_cmp_le_i32 vcc, %1, %2\n\tv_cndmask_b32 %0, %3, %0, vcc"
-                                 : "+v"(s2[h][e])
-                                 : "i"(16 * h + e), "v"(lim), "v"(ninf)
-                                 : "vcc");
-        } else {
-#pragma unroll
-            for (int h = 0; h < 2 * NS; ++h) {
-                // flags of tokens 16h + 4j .. +3, one byte each
-                const uint32_t fl = *reinterpret_cast<const uint32_t*>(flags + 16 * h + 4 * j);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool keep = ((fl >> (8 * e)) & 0xffu) && 16 * h + e <= lim;
-                    s2[h][e] = keep ? s2[h][e] : -INFINITY;
-                }
-            }
-        }
+    for (int h = 1; h < 2 * NS; ++h) {
+        mt = max3(mt, s2[h][0], s2[h][1]);
+        mt = max3(mt, s2[h][2], s2[h][3]);
     }
-    float mt = s2[0][0];
-#pragma unroll
-    for (int h = 0; h < 2 * NS; ++h)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mt = fmaxf(mt, s2[h][e]);
     mt = row_max4(mt) * c_log2;                 // c > 0: the maximum of the scaled scores
     // The running maximum moves only when the tile's exceeds it by more than
     // kLazyMax: the weights stay below 2^kLazyMax (fine in fp16, summed in
     // fp32) and the rescale of O and l is rare after the first tiles.
-    const float m_new = fmaxf(st.m, mt);
+    const float m_new = max2(st.m, mt);
     const bool bump = m_new > st.m + kLazyMax;  // also the first finite maximum
     const float m_run = bump ? m_new : st.m;
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
@@ -558,7 +622,7 @@ __device__ __forceinline__ void consume_lds_tile(Softmax<D> (&st)[PGeo<D>::kNT],
     const int j = lane >> 4;
     const unsigned char* kb = buf;
     const unsigned char* vb = buf + kTileBytes;
-    float4_t s2[kNT][2 * NS];
+    float s2[kNT][2 * NS][4];                 // scores as single floats: masked in place, register by register
 #pragma unroll
     for (int h = 0; h < 2 * NS; ++h) {
         float4_t acc[kNT];
@@ -572,18 +636,13 @@ __device__ __forceinline__ void consume_lds_tile(Softmax<D> (&st)[PGeo<D>::kNT],
             for (int t = 0; t < kNT; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[t][c], acc[t], 0, 0, 0);
         }
 #pragma unroll
-        for (int t = 0; t < kNT; ++t) s2[t][h] = acc[t];
+        for (int t = 0; t < kNT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s2[t][h][e] = acc[t][e];
     }
     half8_t_ p[kNT][NS];
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) {
-        if (mask == 0)
-            row_softmax<D, 0>(st[t], p[t], s2[t], flags, t0, c_log2, j, rw[t]);
-        else if (mask == 1)
-            row_softmax<D, 1>(st[t], p[t], s2[t], flags, t0, c_log2, j, rw[t]);
-        else
-            row_softmax<D, 2>(st[t], p[t], s2[t], flags, t0, c_log2, j, rw[t]);
-    }
+    for (int t = 0; t < kNT; ++t) row_softmax<D>(st[t], p[t], s2[t], flags, t0, mask, c_log2, j, rw[t]);
     // the row sums: P times an all-ones operand, for every slab
     const half8_t_ ones = {(_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f,
                            (_Float16)1.f, (_Float16)1.f, (_Float16)1.f, (_Float16)1.f};
@@ -717,6 +776,7 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
         rw[t].live = 16 * t + nrow < rows;
         const int r = row0 + 16 * t + (rw[t].live ? nrow : 0);
         rw[t].pos = base_pos + r / g;
+        rw[t].rel = rw[t].pos - 4 * jg;
         const _Float16* qrow = q + (((int64_t)q0 + r / g) * num_heads + (int64_t)kvh * g + r % g) * kD;
 #pragma unroll
         for (int c = 0; c < kQk; ++c) {
