@@ -262,8 +262,16 @@ int pa_decode_order(int32_t *seq_order, const int32_t *context_lens,
  *                  workgroups to fill the GPU (few sequences or KV heads,
  *                  short chunks over long contexts) the context is split
  *                  into parts whose partial results it holds, merged by a
- *                  second kernel; without it (NULL or smaller) the context
- *                  is not split.  Contents on entry are ignored; calls
+ *                  second kernel; when it gives more than one round of
+ *                  resident workgroups with at least 8 row tiles (1024
+ *                  query rows at head_dim 64 and 128, 512 at 256) per (KV
+ *                  head, sequence), its first 256 bytes hold the counters
+ *                  from which one round of persistent workgroups takes the
+ *                  row tiles (zeroed by the call itself, in a kernel ahead
+ *                  of the attention on the same stream).  Without it (NULL
+ *                  or smaller) the context is not split and every row tile
+ *                  gets a workgroup of its own; the results are the same
+ *                  bit for bit.  Contents on entry are ignored; calls
  *                  sharing a workspace must be stream-ordered.
  * head_dim 64, 128 or 256 (PA_ERR_UNSUPPORTED otherwise); any num_heads
  * multiple of num_kv_heads.  Runs on the matrix cores
@@ -311,10 +319,11 @@ int pa_prefill_append(void *out, const void *q, int32_t num_tokens,
                       float scale, int32_t max_query_len, void *workspace,
                       size_t workspace_bytes, int32_t dtype, void *stream);
 
-/* Bytes of workspace pa_prefill uses for these sizes: 0 when the batch
- * fills the GPU without splitting the context, else (2 + head_dim) x 4 bytes
- * per (token, head, context part), in two 256-byte aligned regions.  The
- * context bound is max_blocks_per_seq x block_size.  (size_t)-1 for invalid
+/* Bytes of workspace pa_prefill uses for these sizes: when the context is
+ * split, (2 + head_dim) x 4 bytes per (token, head, context part), in two
+ * 256-byte aligned regions; otherwise 256 (the persistent grid's counters)
+ * when the batch has more than 256 row-tile workgroups, else 0.  The context
+ * bound is max_blocks_per_seq x block_size.  (size_t)-1 for invalid
  * arguments. */
 size_t pa_prefill_workspace_size(int32_t num_tokens, int32_t num_seqs,
                                  int32_t num_heads, int32_t num_kv_heads,
