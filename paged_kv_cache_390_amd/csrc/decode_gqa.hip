@@ -33,11 +33,16 @@
 //    the A-operand layout of P for the 16x16x16 PV product, so the online
 //    softmax (running max / sum per query, base 2, log2(e) folded into the
 //    scale) runs in place and P goes to the matrix core as fp16.
-//  * PV: B = V tile.  Output column n of d-tile c is d = (D/16)*n + c, so
-//    lane (n, j) loads the D/16 contiguous values d = (D/16)*n .. of tokens
-//    4j..4j+3 (8, 16 or 32 bytes per token; the four tokens' loads of the
-//    16 lanes read every V row whole), and element c of the four tokens is
-//    the B operand of d-tile c.
+//  * PV: B = V tile.  Output column n of d-tile c is d = (D/16)*n + c up to
+//    head_dim 128, so lane (n, j) loads the D/16 contiguous values d =
+//    (D/16)*n .. of tokens 4j..4j+3 (8 or 16 bytes per token: one load of
+//    the 16 lanes reads the V row whole), and element c of the four tokens
+//    is the B operand of d-tile c.  At head_dim 256 the lane's 16 values are
+//    two runs of 8, d = 128*(c/8) + 8n + c%8 (vcol), so that each of its two
+//    16-byte loads per token reads one contiguous half of the row across the
+//    16 lanes; with one run of 16 values each load read 16-byte pieces 32
+//    bytes apart and the call took 189-193 us instead of 175-177 (128
+//    sequences at g = 8).
 //  * Masking by select: a token past the context, or behind a table entry
 //    outside the pool, gets S = -inf and V = 0, so NaN in unused rows cannot
 //    reach the sums (0 * NaN would).
@@ -118,26 +123,39 @@ struct QOperands<D, true> {
 template <int D>
 struct Tile {
     u32x4 k[Geo<D>::kQk];                   // K row (token n), d = 32c + 8j .. +7
-    uint32_t v[4][Geo<D>::kVDw];            // V rows (tokens 4j + i), d = kVpl*n ..
+    uint32_t v[4][Geo<D>::kVDw];            // V rows (tokens 4j + i), d = vcol(n, c) for c = 0 .. kVpl-1
     bool valid[4];                          // tokens 4j + i: inside the context and the pool
 };
 
 template <int D>
 struct Softmax {
     float m, l;                             // running max (base 2) and sum of query n
-    float4_t o[Geo<D>::kDT];                // O[query 4j + i][d = kVpl*n + c] in o[c][i]
+    float4_t o[Geo<D>::kDT];                // O[query 4j + i][d = vcol(n, c)] in o[c][i]
 };
 
+// Head-dim index of PV output column n of d-tile c.  Up to head_dim 128 a
+// lane's kVpl values are contiguous, d = kVpl*n + c: one load per token
+// covers the whole row across the 16 lanes.  At 256 they are two runs of
+// 8, d = 128*(c/8) + 8n + c%8, so that each 16-byte load of the 16 lanes
+// reads one contiguous 256-byte half of the row; with one run of 16 each
+// load would read 16-byte pieces 32 bytes apart, touching every cache line
+// of the row in both loads.
 template <int D>
-__device__ __forceinline__ void load_v_row(uint32_t (&dst)[Geo<D>::kVDw], const _Float16* src) {
+__device__ __forceinline__ int vcol(int n, int c) {
+    if constexpr (D >= 256) return 128 * (c / 8) + 8 * n + (c % 8);
+    else return Geo<D>::kVpl * n + c;
+}
+
+template <int D>
+__device__ __forceinline__ void load_v_row(uint32_t (&dst)[Geo<D>::kVDw], const _Float16* row, int n) {
     if constexpr (Geo<D>::kVDw == 2) {
-        const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src));
+        const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(row + vcol<D>(n, 0)));
         dst[0] = x[0];
         dst[1] = x[1];
     } else {
 #pragma unroll
         for (int w = 0; w < Geo<D>::kVDw / 4; ++w) {
-            const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + w);
+            const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + vcol<D>(n, 8 * w)));
 #pragma unroll
             for (int e = 0; e < 4; ++e) dst[4 * w + e] = x[e];
         }
@@ -167,7 +185,7 @@ __device__ __forceinline__ void load_tile_block(Tile<D>& t, int t0, int end, int
     for (int i = 0; i < 4; ++i) {
         const int rv = 4 * j + i < lim ? 4 * j + i : lim;
         t.valid[i] = ok && t0 + 4 * j + i < end;
-        load_v_row<D>(t.v[i], vbase + base + rv * D + G::kVpl * n);
+        load_v_row<D>(t.v[i], vbase + base + rv * D, n);
     }
 }
 
@@ -199,7 +217,7 @@ __device__ __forceinline__ void load_tile_rows(Tile<D>& t, int t0, int end, cons
         const bool ok = (uint32_t)phys < (uint32_t)num_blocks;
         t.valid[i] = tv < end && ok;
         const int64_t row = (int64_t)(ok ? phys : 0) * blk_stride + (int64_t)(tc % B) * D;
-        load_v_row<D>(t.v[i], vbase + row + G::kVpl * n);
+        load_v_row<D>(t.v[i], vbase + row, n);
     }
 }
 
@@ -445,13 +463,13 @@ decode_gqa_mfma_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, fl
 #pragma unroll
             for (int c = 0; c < G::kQk; ++c)
                 t.k[c] = nl == 0 ? *reinterpret_cast<const u32x4*>(s_new + 16 * (4 * c + jl)) : z;
-            // V rows of tokens 4j + i (d = kVpl*n ..): token 0 is i = 0 of lane group 0
+            // V rows of tokens 4j + i (d = vcol(n, c)): token 0 is i = 0 of lane group 0
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int w = 0; w < G::kVDw; ++w)
                     t.v[i][w] = i == 0 && jl == 0
-                                    ? *reinterpret_cast<const uint32_t*>(s_new + 2 * D + 2 * G::kVpl * nl + 4 * w)
+                                    ? *reinterpret_cast<const uint32_t*>(s_new + 2 * D + 2 * vcol<D>(nl, 2 * w))
                                     : 0u;
 #pragma unroll
             for (int i = 0; i < 4; ++i) t.valid[i] = ok && jl == 0 && i == 0;
@@ -481,7 +499,7 @@ decode_gqa_mfma_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, fl
 #pragma unroll
         for (int c = 0; c < G::kDT; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s_o[wave][4 * jl + i][G::kVpl * nl + c] = st.o[c][i];
+            for (int i = 0; i < 4; ++i) s_o[wave][4 * jl + i][vcol<D>(nl, c)] = st.o[c][i];
         __syncthreads();
         for (int idx = threadIdx.x; idx < g * D; idx += kThreads) {
             const int qi = idx / D;
@@ -517,7 +535,7 @@ decode_gqa_mfma_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, fl
         // not four (2 x 16 x D floats): waves 2, 3 hand theirs to waves 0,
         // 1, then wave 1 to wave 0; each receiver rescales both states to
         // the larger maximum and adds.  Wave 0 then writes the result from
-        // its registers: lane (n, j) holds O[query 4j + i][d = kVpl*n + c].
+        // its registers: lane (n, j) holds O[query 4j + i][d = vcol(n, c)].
         // (Up to head_dim 128 the one-round merge is faster: measured 1.2%
         // per call on the 256-sequence batch at g = 8.)
         __shared__ float s_m[2][16];
@@ -570,17 +588,17 @@ decode_gqa_mfma_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, fl
 #pragma unroll
                 for (int c = 0; c < G::kDT; ++c)
                     h[c] = bad_len ? (_Float16)NAN : L > 0.f ? (_Float16)(st.o[c][i] / L) : (_Float16)0.f;
-                _Float16* dst = out + head_row * D + G::kVpl * nl;
+                _Float16* dst = out + head_row * D;
 #pragma unroll
                 for (int c = 0; c < G::kDT; c += 4)
-                    *reinterpret_cast<half4_t*>(dst + c) = half4_t{h[c], h[c + 1], h[c + 2], h[c + 3]};
+                    *reinterpret_cast<half4_t*>(dst + vcol<D>(nl, c)) = half4_t{h[c], h[c + 1], h[c + 2], h[c + 3]};
             } else {
                 const int64_t slot = head_row * num_parts + part;
-                float* acc = ws_acc + slot * D + G::kVpl * nl;
+                float* acc = ws_acc + slot * D;
 #pragma unroll
                 for (int c = 0; c < G::kDT; c += 4)
-                    *reinterpret_cast<float4_t*>(acc + c) = float4_t{st.o[c][i], st.o[c + 1][i], st.o[c + 2][i],
-                                                                     st.o[c + 3][i]};
+                    *reinterpret_cast<float4_t*>(acc + vcol<D>(nl, c)) =
+                        float4_t{st.o[c][i], st.o[c + 1][i], st.o[c + 2][i], st.o[c + 3][i]};
                 if (nl == 0) {
                     ws_ml[2 * slot] = M;
                     ws_ml[2 * slot + 1] = L;
