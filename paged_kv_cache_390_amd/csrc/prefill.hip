@@ -120,6 +120,7 @@ struct PGeo {
     static constexpr int kDTiles = D / 16;                     // PV d-tiles (16 output columns each)
     static_assert(kStageRows >= 1 && kKvTile * kChunks == kStageRows * kThreads, "tile rows must split evenly");
     static_assert(kKvTile % 32 == 0 && kDTiles % 4 == 0, "whole PV slabs and d-tile groups");
+    static_assert(kWaves * kRowsPerWave * D * 2 <= kBufBytes, "the output rows of all waves fit one buffer");
 };
 
 // The geometry of PGeo<D> under short names inside a kernel or helper.
@@ -993,20 +994,41 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
     }
 
     // Row 16t + nrow of the wave lives in this lane's st[t].o[c] at columns
-    // 16c + 4*jg .. +3 (one 8-byte store per d-tile), its sum in st[t].l.
+    // 16c + 4*jg .. +3, its sum in st[t].l.  The normalised rows go out
+    // through the wave's own slice of buffer A (free after the walk's last
+    // barrier): written there 8 bytes per lane, read back 16 contiguous
+    // bytes per lane with kChunks lanes per row, so that each store
+    // instruction writes whole rows.  Stored straight from the registers,
+    // every 8-byte piece of a wave instruction fell on a different row: a
+    // write request per lane.  Chunk q of staged row r sits at position
+    // q ^ (r % kChunks), so that the 16 rows of one write and the chunks of
+    // one read fall in distinct banks.
+    {
+        unsigned char* ost = ldsA + wave * (kRowsPerWave * kD * 2);
 #pragma unroll
-    for (int t = 0; t < kNT; ++t) {
-        if (16 * t + nrow >= rows) continue;
-        const int rwi = row0 + 16 * t + nrow;
-        const int64_t orow = ((int64_t)q0 + rwi / g) * num_heads + (int64_t)kvh * g + rwi % g;
-        const float L = st[t].l[0];
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        _Float16* orow_p = out + orow * kD + 4 * jg;
+        for (int t = 0; t < kNT; ++t) {
+            const int r = 16 * t + nrow;
+            const float L = st[t].l[0];
+            const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-        for (int c = 0; c < kDTiles; ++c) {
-            const half4_t h = {(_Float16)(st[t].o[c][0] * inv), (_Float16)(st[t].o[c][1] * inv),
-                               (_Float16)(st[t].o[c][2] * inv), (_Float16)(st[t].o[c][3] * inv)};
-            *reinterpret_cast<half4_t*>(orow_p + 16 * c) = h;
+            for (int c = 0; c < kDTiles; ++c) {
+                const half4_t h = {(_Float16)(st[t].o[c][0] * inv), (_Float16)(st[t].o[c][1] * inv),
+                                   (_Float16)(st[t].o[c][2] * inv), (_Float16)(st[t].o[c][3] * inv)};
+                const int q = 2 * c + (jg >> 1);
+                *reinterpret_cast<half4_t*>(ost + r * (kD * 2) + ((q ^ (r & (kChunks - 1))) << 4) + ((jg & 1) << 3)) =
+                    h;
+            }
+        }
+        constexpr int kRowsPerStore = 64 / kChunks;
+        const int q = lane % kChunks;
+#pragma unroll
+        for (int k = 0; k < kRowsPerWave / kRowsPerStore; ++k) {
+            const int r = k * kRowsPerStore + lane / kChunks;
+            if (r >= rows) continue;
+            const int rwi = row0 + r;
+            const int64_t orow = ((int64_t)q0 + rwi / g) * num_heads + (int64_t)kvh * g + rwi % g;
+            *reinterpret_cast<u32x4*>(out + orow * kD + 8 * q) =
+                *reinterpret_cast<const u32x4*>(ost + r * (kD * 2) + ((q ^ (r & (kChunks - 1))) << 4));
         }
     }
     } while (false);
