@@ -215,6 +215,40 @@ def test_decode_order_of_a_large_batch():
     assert pa.pa_decode_order(torch.zeros(0, dtype=torch.int32, device=dev), bound).numel() == 0
 
 
+def test_decode_at_the_sequence_limit():
+    """65535 sequences, the most a call takes (the grid's second dimension):
+    contexts of 0 to 12 tokens at head_dim 16, block_size 4, the dispatch
+    order computed inside the call; every row against the oracle, the empty
+    ones exactly zero."""
+    dev = device()
+    rng = np.random.default_rng(65535)
+    S = 65535
+    lens_l = rng.integers(0, 13, size=S).tolist()
+    case = workloads.random_case(65535, lens_l, 2, 2, 16, 4)
+    # slots straight from the tables (slot = table[p / B] * B + p % B) and
+    # the oracle's scatter into a NaN-poisoned pool
+    width = max(len(t) for t in case.tables)
+    tables = np.full((S, width), -1, dtype=np.int32)
+    for s_, t in enumerate(case.tables):
+        tables[s_, :len(t)] = t
+    lens = np.asarray(lens_l, dtype=np.int32)
+    seq = np.repeat(np.arange(S), lens)
+    pos = np.arange(int(lens.sum())) - np.repeat(np.cumsum(lens) - lens, lens)
+    slots = (tables[seq, pos // 4].astype(np.int64) * 4 + pos % 4).astype(np.int64)
+    kc = poisoned_cache(case.num_blocks, 2, 4, 16)
+    vc = kc.copy()
+    oracle.reshape_and_cache(case.k_tokens, case.v_tokens, slots, kc, vc)
+    bound = width * 4
+    need = pa.pa_decode_workspace_size(S, 2, 2, 16, 4, bound)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    say(f"decode at the sequence limit: S={S}, workspace {need} bytes")
+    out = _gpu_decode(dev, case.q, kc, vc, tables, lens, case.scale, max_context_len=bound, workspace=ws)
+    ref = oracle.decode(case.q, kc, vc, tables, lens, case.scale)
+    assert_attention_close(out, ref, "65535 sequences")
+    empty = np.asarray(lens_l) == 0
+    assert empty.any() and np.all(bits(out)[empty] == 0)
+
+
 def test_seq_order_entries_outside_the_batch_are_skipped():
     """A sequence the order leaves out keeps its rows untouched; an entry
     outside [0, S) does nothing."""
