@@ -70,7 +70,7 @@ def parse():
     p.add_argument("--batch", type=int, default=0, help="sequences (0: 64 for llama7b, 256 for gqa)")
     p.add_argument("--block-size", type=int, default=16)
     p.add_argument("--head-dim", type=int, default=128,
-                   help="gqa, prefill: head_dim of the batch (64/128/256)")
+                   help="gqa, prefill, prefill-long: head_dim of the batch (64/128/256)")
     p.add_argument("--partition", type=int, default=0, help="decode partition size (0 = library default)")
     p.add_argument("--fused", type=int, default=1,
                    help="decode workloads: 1 writes the new K/V inside the decode call (pa_decode_append), "
@@ -928,7 +928,8 @@ def chunked_bench(args, dev):
 
 def prefill_long_bench(args, dev):
     """Prefill of long full prompts: every token new, causal, at Llama-2-7B
-    heads (32 x 128; one batch at 32 query / 8 KV heads), B = 16, --layers
+    heads (32 x --head-dim, 128 by default; one batch at 32 query / 8 KV
+    heads), B = 16, --layers
     layers resident (default here 4): 32 x 1024, 16 x 2048, 8 x 4096, 4 x
     8192 tokens -- the steady state of the prefill loop, next to the
     short-prompt mix of --workload prefill.  Flops as for that workload:
@@ -939,7 +940,7 @@ def prefill_long_bench(args, dev):
     import paged_kv_cache_390_amd as pa
 
     L = args.layers if args.layers != 32 else 4
-    B, D = args.block_size, 128
+    B, D = args.block_size, args.head_dim
     results = []
     for S, n, H, Hkv in ((32, 1024, 32, 32), (16, 2048, 32, 32), (8, 4096, 32, 32), (4, 8192, 32, 32),
                          (8, 4096, 32, 8)):
