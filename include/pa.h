@@ -263,8 +263,8 @@ int pa_decode_order(int32_t *seq_order, const int32_t *context_lens,
  *                  short chunks over long contexts) the context is split
  *                  into parts whose partial results it holds, merged by a
  *                  second kernel; when it gives more than one round of
- *                  resident workgroups with at least 8 row tiles (1024
- *                  query rows at head_dim 64 and 128, 512 at 256) per (KV
+ *                  resident workgroups with at least 1024 query rows
+ *                  (8 row tiles at head_dim 64 and 128, 16 at 256) per (KV
  *                  head, sequence), its first 256 bytes hold the counters
  *                  from which one round of persistent workgroups takes the
  *                  row tiles (zeroed by the call itself, in a kernel ahead

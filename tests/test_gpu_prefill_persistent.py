@@ -1,8 +1,8 @@
 """GPU checks of the persistent prefill grid.
 
 When a pa_prefill / pa_prefill_append call has more row-tile workgroups than
-the GPU holds at once, at least 8 row tiles per (KV head, sequence) and a
-workspace for the claim counters, one round of
+the GPU holds at once, at least 1024 query rows per (KV head, sequence)
+and a workspace for the claim counters, one round of
 resident workgroups takes the items from per-XCD counters (one counter when
 the (KV head, sequence) pairs are not a multiple of 8).  Each item runs the
 same code as with one workgroup per item, so outputs and cache writes are
@@ -51,7 +51,7 @@ def _setup(name):
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     # more items than any occupancy (at most 3 workgroups per CU) holds at once
     assert items > 3 * cus, (items, cus)
-    assert _row_tiles(lens_l, H, Hkv, rpw) >= 8
+    assert _row_tiles(lens_l, H, Hkv, rpw) * rpw >= 1024                 # query rows per pair
     need = pa.pa_prefill_workspace_size(int(qs[-1]), len(lens_l), H, Hkv, D, B, tables.shape[1], max(lens_l))
     assert need == 256, need                                  # unsplit: the claim counters only
     return dev, case, kc, vc, tables, lens, q, qs, check
@@ -115,7 +115,7 @@ def test_persistent_prefill_append_matches_one_workgroup_per_item(chunked):
     q_h, qs_h = _queries(1400, ms, H, D)
     dev = device()
     assert _items(ms, H, Hkv, 128) > 3 * torch.cuda.get_device_properties(dev).multi_processor_count
-    assert _row_tiles(ms, H, Hkv, 128) >= 8
+    assert _row_tiles(ms, H, Hkv, 128) * 128 >= 1024
     assert pa.pa_prefill_workspace_size(int(qs_h[-1]), len(lens_l), H, Hkv, D, B, tables_h.shape[1], max(ms)) == 256
     say(f"persistent prefill_append chunked={chunked}: rows {int(qs_h[-1])}")
     q, key, val = (torch.from_numpy(x).to(dev) for x in (q_h, key_h, val_h))
