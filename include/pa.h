@@ -263,9 +263,10 @@ int pa_decode_order(int32_t *seq_order, const int32_t *context_lens,
  *                  short chunks over long contexts) the context is split
  *                  into parts whose partial results it holds, merged by a
  *                  second kernel; when it gives more than one round of
- *                  resident workgroups with at least 1024 query rows
- *                  (8 row tiles at head_dim 64 and 128, 16 at 256) per (KV
- *                  head, sequence), its first 256 bytes hold the counters
+ *                  resident workgroups, one query head per KV head and at
+ *                  least 1024 query rows (8 row tiles at head_dim 64 and
+ *                  128, 16 at 256) per (KV head, sequence), its first 256
+ *                  bytes hold the counters
  *                  from which one round of persistent workgroups takes the
  *                  row tiles (zeroed by the call itself, in a kernel ahead
  *                  of the attention on the same stream).  Without it (NULL

@@ -1362,18 +1362,22 @@ int prefill_impl(const char* fn, void* out, const void* q, int32_t num_tokens, c
     PrefillFn fn_main =
         app ? (stream_kv ? pick<true, true>(head_dim, block_size) : pick<false, true>(head_dim, block_size))
             : (stream_kv ? pick<true, false>(head_dim, block_size) : pick<false, false>(head_dim, block_size));
-    // persistent grid: more items than one round of resident workgroups, at
-    // least 1024 query rows per (KV head, sequence) -- 8 row tiles up to
-    // head_dim 128, 16 at 256 -- and room for the claim counters (an unsplit
-    // call's workspace).  Measured against one workgroup per item
-    // (pa_prefill, Llama-2-7B heads): 32 x 1024-token prompts +13%, 16 x
-    // 2048 +8%, 8 x 4096 +3.5%, 4 x 8192 +1% (+7% / +10% at 1024 tokens and
-    // head_dim 256 / 64); on the short-prompt mix (at most 774 tokens, many
-    // row tiles past a prompt's end) -2 to -4% at head_dim 128, -1.5% at
-    // 256, -37% at 64, so fewer rows keep one workgroup per item.
+    // persistent grid: more items than one round of resident workgroups, one
+    // query head per KV head, at least 1024 query rows per (KV head,
+    // sequence) -- 8 row tiles up to head_dim 128, 16 at 256 -- and room for
+    // the claim counters (an unsplit call's workspace).  Measured against one
+    // workgroup per item (pa_prefill, Llama-2-7B heads): 32 x 1024-token
+    // prompts +13%, 16 x 2048 +8%, 8 x 4096 +3.5%, 4 x 8192 +1% (+7% / +10%
+    // at 1024 tokens and head_dim 256 / 64); on the short-prompt mix (at
+    // most 774 tokens, many row tiles past a prompt's end) -2 to -4% at
+    // head_dim 128, -1.5% at 256, -37% at 64, so fewer rows keep one
+    // workgroup per item.  With several query heads per KV head it never
+    // gained: 32 / 8 heads 0 to -1% on 1024-8192-token prompts, -3 to -7% on
+    // 256-774-token ones, 64 / 8 heads -1.4% on 32 x 1024.
     unsigned* claim = nullptr;
     int64_t grid = items;
-    if (P.num_parts == 1 && row_tiles * hg.rows_per_group >= 1024 && workspace && workspace_bytes >= kClaimBytes) {
+    if (P.num_parts == 1 && g == 1 && row_tiles * hg.rows_per_group >= 1024 && workspace &&
+        workspace_bytes >= kClaimBytes) {
         const PrefillFn fn_p = app ? pick_persistent<true>(head_dim, block_size) : pick_persistent<false>(head_dim, block_size);
         const int64_t slots = prefill_slots(reinterpret_cast<const void*>(fn_p)) / 8 * 8;
         if (slots >= 8 && items > slots) {

@@ -1,8 +1,8 @@
 """GPU checks of the persistent prefill grid.
 
 When a pa_prefill / pa_prefill_append call has more row-tile workgroups than
-the GPU holds at once, at least 1024 query rows per (KV head, sequence)
-and a workspace for the claim counters, one round of
+the GPU holds at once, one query head per KV head, at least 1024 query rows
+per (KV head, sequence) and a workspace for the claim counters, one round of
 resident workgroups takes the items from per-XCD counters (one counter when
 the (KV head, sequence) pairs are not a multiple of 8).  Each item runs the
 same code as with one workgroup per item, so outputs and cache writes are
@@ -28,7 +28,7 @@ CASES = {
     "d128 pairs x8": (MIX * 2, 8, 8, 128, 16, 128, [3, 6]),
     "d64 pairs x8": (MIX * 2, 8, 8, 64, 16, 128, [0, 3]),
     "d256 pairs x8": (MIX * 2, 8, 8, 256, 16, 64, [1, 3]),
-    "d128 gqa 32/8": (MIX, 32, 8, 128, 16, 128, [3, 6]),
+    "d128 16 heads": (MIX * 2, 16, 16, 128, 16, 128, [3, 6]),
     "d128 pairs not x8": ([3600, 1500, 200, 2900, 64, 2048, 1000], 4, 4, 128, 32, 128, [4, 6]),
 }
 
@@ -51,7 +51,7 @@ def _setup(name):
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     # more items than any occupancy (at most 3 workgroups per CU) holds at once
     assert items > 3 * cus, (items, cus)
-    assert _row_tiles(lens_l, H, Hkv, rpw) * rpw >= 1024                 # query rows per pair
+    assert H == Hkv and _row_tiles(lens_l, H, Hkv, rpw) * rpw >= 1024    # one query head per KV head, rows per pair
     need = pa.pa_prefill_workspace_size(int(qs[-1]), len(lens_l), H, Hkv, D, B, tables.shape[1], max(lens_l))
     assert need == 256, need                                  # unsplit: the claim counters only
     return dev, case, kc, vc, tables, lens, q, qs, check
@@ -141,12 +141,12 @@ def test_persistent_grid_replays_in_a_hip_graph():
     """The counter reset and the persistent grid captured in one graph,
     replayed three times with eager work between (workspace filled with 0xFF,
     output with NaN): every replay reproduces the eager output bit for bit."""
-    dev, case, kc_h, vc_h, tables_h, lens_h, q_h, qs_h, _ = _setup("d128 gqa 32/8")
+    dev, case, kc_h, vc_h, tables_h, lens_h, q_h, qs_h, _ = _setup("d128 16 heads")
     kc, vc, q = (torch.from_numpy(x).to(dev) for x in (kc_h, vc_h, q_h))
     t, l, qs = (torch.from_numpy(x).to(dev) for x in (tables_h, lens_h, qs_h))
     ws = torch.empty(256, dtype=torch.uint8, device=dev)
     out = torch.empty(q.shape, dtype=torch.float16, device=dev)
-    mq = max(CASES["d128 gqa 32/8"][0])
+    mq = max(CASES["d128 16 heads"][0])
 
     def call():
         pa.pa_prefill(out, q, kc, vc, t, l, qs, case.scale, max_query_len=mq, workspace=ws)
