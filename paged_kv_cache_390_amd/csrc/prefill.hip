@@ -1021,14 +1021,26 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
         }
         constexpr int kRowsPerStore = 64 / kChunks;
         const int q = lane % kChunks;
+        // row row0 + r is query head kvh*g + hd of token tk; r steps by
+        // kRowsPerStore, so (tk, hd) step by (kRowsPerStore / g, kRowsPerStore
+        // % g) with a carry (one division per lane, not one per row)
+        const int rr0 = row0 + lane / kChunks;
+        int tk = rr0 / g, hd = rr0 - (rr0 / g) * g;
+        const int dt = kRowsPerStore / g, dh = kRowsPerStore - dt * g;
 #pragma unroll
         for (int k = 0; k < kRowsPerWave / kRowsPerStore; ++k) {
             const int r = k * kRowsPerStore + lane / kChunks;
-            if (r >= rows) continue;
-            const int rwi = row0 + r;
-            const int64_t orow = ((int64_t)q0 + rwi / g) * num_heads + (int64_t)kvh * g + rwi % g;
-            *reinterpret_cast<u32x4*>(out + orow * kD + 8 * q) =
-                *reinterpret_cast<const u32x4*>(ost + r * (kD * 2) + ((q ^ (r & (kChunks - 1))) << 4));
+            if (r < rows) {
+                const int64_t orow = ((int64_t)q0 + tk) * num_heads + (int64_t)kvh * g + hd;
+                *reinterpret_cast<u32x4*>(out + orow * kD + 8 * q) =
+                    *reinterpret_cast<const u32x4*>(ost + r * (kD * 2) + ((q ^ (r & (kChunks - 1))) << 4));
+            }
+            tk += dt;
+            hd += dh;
+            if (hd >= g) {
+                hd -= g;
+                ++tk;
+            }
         }
     }
     } while (false);
