@@ -28,7 +28,8 @@
 //  * QK: A = K tile (m = token), B = Q^T (n = query head of the group,
 //    zero-padded past g).  The contraction index of MFMA c is mapped onto
 //    head_dim 32c + 8j .. +7 in lane (m, j): one 16-byte load of token m's
-//    row per MFMA operand, no register shuffles.
+//    row per MFMA operand, no register shuffles (at head_dim 64 the tile is
+//    read as whole rows instead and moved into this layout through LDS).
 //  * S^T lands with lane (n, j) holding tokens 4j..4j+3 of query n: exactly
 //    the A-operand layout of P for the 16x16x16 PV product, so the online
 //    softmax (running max / sum per query, base 2, log2(e) folded into the
@@ -90,6 +91,15 @@ struct Geo {
     // head_dim 256: the Q^T operands (D/8 VGPRs) are read from LDS for each
     // tile instead of held, so that two waves fit a SIMD
     static constexpr bool kQInLds = D >= 256;
+    // head_dim 64: K is read with adjacent lanes contiguous (kLpt lanes per
+    // token row, whole 128-byte rows per load) and moved into the QK operand
+    // layout (token lane % 16, 16 bytes per lane group) through the wave's
+    // LDS slice.  Read in the operand layout, each load took 64 bytes of 16
+    // rows, the other half of each line falling to the next load: 176.4 ->
+    // 169.9 us per call on 512 sequences (mean of six runs in turn).  At 128
+    // the same read gained nothing; at 256 its addresses spilled registers.
+    static constexpr bool kKLds = D == 64;
+    static constexpr int kLpt = D / 8;
     static constexpr int kQPitch = D + 8;            // halves per staged Q row (16 bytes of padding)
 };
 
@@ -177,10 +187,21 @@ __device__ __forceinline__ void load_tile_block(Tile<D>& t, int t0, int end, int
     const bool ok = (uint32_t)phys < (uint32_t)num_blocks;
     const int64_t base = (int64_t)(ok ? phys : 0) * blk_stride + (int64_t)(t0 % B) * D;
     const int lim = end - 1 - t0;
-    const int rk = n < lim ? n : lim;
+    if constexpr (G::kKLds) {
+        // load c: token c*(64/kLpt) + lane/kLpt, 16-byte chunk lane % kLpt
 #pragma unroll
-    for (int c = 0; c < G::kQk; ++c)
-        t.k[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + base + rk * D + 32 * c + 8 * j));
+        for (int c = 0; c < G::kQk; ++c) {
+            const int tk = c * (64 / G::kLpt) + lane / G::kLpt;
+            const int rk = tk < lim ? tk : lim;
+            t.k[c] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(kbase + base + rk * D + 8 * (lane % G::kLpt)));
+        }
+    } else {
+        const int rk = n < lim ? n : lim;
+#pragma unroll
+        for (int c = 0; c < G::kQk; ++c)
+            t.k[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + base + rk * D + 32 * c + 8 * j));
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int rv = 4 * j + i < lim ? 4 * j + i : lim;
@@ -223,11 +244,29 @@ __device__ __forceinline__ void load_tile_rows(Tile<D>& t, int t0, int end, cons
 
 // keep[i]: token 4j + i takes part (inside the context and the pool);
 // t.valid[i]: its V row holds data (zeroed by select otherwise).
-template <int D>
+// kKRows: t.k holds K as load_tile_block reads it when Geo<D>::kKLds
+// (whole rows); it goes through the wave's LDS slice `kslice` into the
+// operand layout first.
+template <int D, bool kKRows = false>
 __device__ __forceinline__ void consume_tile(Softmax<D>& st, Tile<D>& t, const QOperands<D>& qb,
-                                             float scale_log2, int lane) {
+                                             float scale_log2, int lane, u32x4* kslice = nullptr) {
     using G = Geo<D>;
     const int j = lane >> 4;
+    if constexpr (kKRows) {
+        // t.k[c] holds token c*(64/kLpt) + lane/kLpt, chunk lane % kLpt: into
+        // the slice (chunk q of token r at position q ^ (r % kLpt), so that the
+        // 16 tokens of one operand read fall in distinct banks), then back as
+        // MFMA c's operand: token lane % 16, chunk 4c + j
+#pragma unroll
+        for (int c = 0; c < G::kQk; ++c) {
+            const int r = c * (64 / G::kLpt) + lane / G::kLpt;
+            const int q = lane % G::kLpt;
+            kslice[r * G::kLpt + (q ^ (r & (G::kLpt - 1)))] = t.k[c];
+        }
+        const int m = lane & 15;
+#pragma unroll
+        for (int c = 0; c < G::kQk; ++c) t.k[c] = kslice[m * G::kLpt + ((4 * c + j) ^ (m & (G::kLpt - 1)))];
+    }
     // S^T = K Q^T: lane holds S^T[token 4j+i][query n]
     float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -394,6 +433,8 @@ decode_gqa_mfma_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, fl
 
     const int ntok = end > start ? end - start : 0;
     const int nsteps = (ntok + kTile - 1) / kTile;
+    __shared__ u32x4 s_kt[kWaves][G::kKLds ? 16 * G::kLpt : 1];   // each wave's K slice (head_dim 64)
+    u32x4* kslice = s_kt[wave];
     if (wave < nsteps) {
         if constexpr (B >= kTile) {
             // One table entry per tile, read with scalar loads a tile ahead of
@@ -426,7 +467,7 @@ decode_gqa_mfma_kernel(_Float16* __restrict__ out, float* __restrict__ ws_ml, fl
                     const int32_t cur = tnext;
                     tnext = entry(stp + (NF + 1) * kWaves);
                     issue(buf[(r + NF) % (NF + 1)], stp + NF * kWaves, cur);
-                    consume_tile<D>(st, buf[r], qb, scale_log2, lane);
+                    consume_tile<D, G::kKLds>(st, buf[r], qb, scale_log2, lane, kslice);
                     stp += kWaves;
                     if (stp >= nsteps) goto walked;
                 }
