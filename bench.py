@@ -753,9 +753,11 @@ def prefill_bench(args, dev):
     --layers layers resident (default here 4).  Each timed call is one
     layer's pa_prefill over every prompt (the K/V already scattered); then
     the whole prompt path per layer -- K/V write and attention -- as
-    pa_reshape_and_cache + pa_prefill and as one pa_prefill_append.
-    Algorithmic flops = sum over heads and new tokens of 4 * D * (causal
-    positions seen); against the dense fp16 matrix-core peak."""
+    pa_reshape_and_cache + pa_prefill and as one pa_prefill_append.  The
+    sequences are dispatched longest first: pa_decode_order once per step,
+    timed with the first layer's call.  Algorithmic flops = sum over heads
+    and new tokens of 4 * D * (causal positions seen); against the dense
+    fp16 matrix-core peak."""
     import numpy as np
     import torch
 
@@ -792,11 +794,18 @@ def prefill_bench(args, dev):
     d_t, d_l, d_q = (torch.from_numpy(x).to(dev) for x in (tables, lens, qs))
     mq = max(lens_l)
     flops = sum(4.0 * D * H * n * (n + 1) / 2 for n in lens_l)
+    # the sequences longest first, computed once per step (inside the first
+    # layer's timed call) and shared by every layer
+    order = torch.empty(S, dtype=torch.int32, device=dev)
+
+    def step_order():
+        pa.pa_decode_order(d_l, mq, out=order)
 
     def call(l):
-        pa.pa_prefill(out, q, kcs[l], vcs[l], d_t, d_l, d_q, 1 / np.sqrt(D), max_query_len=mq)
+        pa.pa_prefill(out, q, kcs[l], vcs[l], d_t, d_l, d_q, 1 / np.sqrt(D), max_query_len=mq, seq_order=order)
 
     for _ in range(max(args.warmup, 3)):
+        step_order()
         for l in range(L):
             call(l)
     torch.cuda.synchronize()
@@ -805,6 +814,8 @@ def prefill_bench(args, dev):
         for l in range(L):
             a, b = ev[i * L + l]
             a.record()
+            if l == 0:
+                step_order()
             call(l)
             b.record()
     torch.cuda.synchronize()
@@ -818,12 +829,16 @@ def prefill_bench(args, dev):
     # attention, as two calls (pa_reshape_and_cache, pa_prefill) or one
     # (pa_prefill_append), in interleaved rounds of passes over the layers
     def two_calls(l):
+        if l == 0:
+            step_order()
         pa.pa_reshape_and_cache(keys[l], vals[l], d_slots, kcs[l], vcs[l])
         call(l)
 
     def fused(l):
+        if l == 0:
+            step_order()
         pa.pa_prefill_append(out, q, keys[l], vals[l], kcs[l], vcs[l], d_t, d_l, d_q, 1 / np.sqrt(D),
-                             max_query_len=mq)
+                             max_query_len=mq, seq_order=order)
 
     path_us = {"two_calls": [], "fused": []}
     for _ in range(max(args.steps // 2, 2)):

@@ -226,7 +226,7 @@ int pa_decode_noalloc(void *out, const void *q, const void *k_cache,
                       int32_t partition_size, const int32_t *seq_order,
                       int32_t dtype, void *stream);
 
-/* Longest-first dispatch order for pa_decode: seq_order (device, int32
+/* Longest-first dispatch order for pa_decode and pa_prefill: seq_order (device, int32
  * [num_seqs], written) becomes a permutation of 0 .. num_seqs - 1 with the
  * sequences sorted by context_lens into 1024 classes of
  * max_context_len / 1024 + 1 tokens, longest class first (order within a
@@ -274,6 +274,14 @@ int pa_decode_order(int32_t *seq_order, const int32_t *context_lens,
  *                  gets a workgroup of its own; the results are the same
  *                  bit for bit.  Contents on entry are ignored; calls
  *                  sharing a workspace must be stream-ordered.
+ *   seq_order      device, int32 [num_seqs], or NULL (index order): the
+ *                  order in which the sequences' row tiles are dispatched,
+ *                  as pa_decode_order writes it from context_lens (longest
+ *                  first, so that no long prompt's row tiles start last and
+ *                  run alone at the end).  Every layer of a step shares one
+ *                  order.  The order never changes a result; an entry
+ *                  outside [0, num_seqs) is skipped, and a sequence the array
+ *                  leaves out keeps its output rows untouched.
  * head_dim 64, 128 or 256 (PA_ERR_UNSUPPORTED otherwise); any num_heads
  * multiple of num_kv_heads.  Runs on the matrix cores
  * (v_mfma_f32_16x16x32_f16, fp32 accumulation).
@@ -285,7 +293,8 @@ int pa_prefill(void *out, const void *q, int32_t num_tokens,
                int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                int32_t head_dim, int32_t block_size, int32_t num_blocks,
                float scale, int32_t max_query_len, void *workspace,
-               size_t workspace_bytes, int32_t dtype, void *stream);
+               size_t workspace_bytes, const int32_t *seq_order,
+               int32_t dtype, void *stream);
 
 /* ------------------------------------------------------------------------
  * pa_reshape_and_cache of the new tokens followed by pa_prefill, in one
@@ -318,7 +327,8 @@ int pa_prefill_append(void *out, const void *q, int32_t num_tokens,
                       int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                       int32_t head_dim, int32_t block_size, int32_t num_blocks,
                       float scale, int32_t max_query_len, void *workspace,
-                      size_t workspace_bytes, int32_t dtype, void *stream);
+                      size_t workspace_bytes, const int32_t *seq_order,
+                      int32_t dtype, void *stream);
 
 /* Bytes of workspace pa_prefill uses for these sizes: when the context is
  * split, (2 + head_dim) x 4 bytes per (token, head, context part), in two

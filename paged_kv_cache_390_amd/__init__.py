@@ -67,13 +67,13 @@ def lib() -> ctypes.CDLL:
                       ctypes.c_int),
         "pa_decode_append": ([P, P, P, P, i64, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P,
                               sz, P, i32, P], ctypes.c_int),
-        "pa_prefill": ([P, P, i32, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, f32, i32, P, sz, i32, P],
+        "pa_prefill": ([P, P, i32, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, f32, i32, P, sz, P, i32, P],
                        ctypes.c_int),
         "pa_decode_order": ([P, P, i32, i32, P], ctypes.c_int),
         "pa_decode_noalloc": ([P, P, P, P, P, i32, P, i32, i32, i32, i32, i32, i32, f32, i32, i32, P, i32, P],
                               ctypes.c_int),
         "pa_prefill_append": ([P, P, i32, P, P, i64, P, P, P, i32, P, P, i32, i32, i32, i32, i32, i32, f32, i32, P, sz,
-                               i32, P], ctypes.c_int),
+                               P, i32, P], ctypes.c_int),
         "pa_prefill_workspace_size": ([i32, i32, i32, i32, i32, i32, i32, i32], sz),
         "pa_decode_workspace_size": ([i32, i32, i32, i32, i32, i32, i32], sz),
         "pa_decode_default_partition": ([i32, i32, i32, i32, i32, i32], i32),
@@ -327,8 +327,8 @@ def pa_decode_append(out, q, key, value, k_cache, v_cache, block_tables, context
 
 def pa_decode_order(context_lens, max_context_len: int, out=None):
     """Longest-first dispatch order of the sequences (int32 device tensor
-    [S]) for pa_decode's seq_order; compute it once per step, after
-    context_lens is final, and pass it to every layer."""
+    [S]) for the seq_order of pa_decode and pa_prefill; compute it once per
+    step, after context_lens is final, and pass it to every layer."""
     torch = _torch()
     _dev_tensor(context_lens, "context_lens", torch.int32, 1)
     S = context_lens.shape[0]
@@ -352,7 +352,7 @@ def pa_prefill_workspace_size(num_tokens: int, num_seqs: int, num_heads: int, nu
 
 
 def _prefill_args(out, q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len, workspace,
-                  split):
+                  split, seq_order):
     torch = _torch()
     _dev_tensor(k_cache, "k_cache", torch.float16, 4)
     _dev_tensor(v_cache, "v_cache", torch.float16, 4)
@@ -380,35 +380,46 @@ def _prefill_args(out, q, k_cache, v_cache, block_tables, context_lens, query_st
                 workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
             _dev_tensor(workspace, "workspace", torch.uint8, 1)
             ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
-    return T, S, H, Hkv, D, B, NB, int(max_query_len), ws_ptr, ws_bytes
+    order_ptr = None
+    if seq_order is not None:
+        _dev_tensor(seq_order, "seq_order", torch.int32, 1)
+        if seq_order.shape[0] != S:
+            raise ValueError("seq_order must have one entry per sequence")
+        order_ptr = seq_order.data_ptr()
+    return T, S, H, Hkv, D, B, NB, int(max_query_len), ws_ptr, ws_bytes, order_ptr
 
 
 def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float,
-               max_query_len: Optional[int] = None, workspace=None, split: bool = True) -> None:
+               max_query_len: Optional[int] = None, workspace=None, split: bool = True, seq_order=None) -> None:
     """Causal attention of the packed new tokens q[T, H, D] over the paged
     cache: sequence s's rows query_start[s] .. query_start[s+1]-1 are its
     last m tokens (K/V already cached), row i at position context_lens[s] -
     m + i.  max_query_len defaults to T.  workspace (uint8 device tensor)
     is allocated when the batch is small enough for the context to be split
-    and none is given; split=False passes none (no split)."""
-    T, S, H, Hkv, D, B, NB, mq, ws_ptr, ws_bytes = _prefill_args(
-        out, q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len, workspace, split)
+    and none is given; split=False passes none (no split).  seq_order (int32
+    device [S], from pa_decode_order over context_lens, once per step)
+    dispatches the sequences longest first; the result is the same."""
+    T, S, H, Hkv, D, B, NB, mq, ws_ptr, ws_bytes, order_ptr = _prefill_args(
+        out, q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len, workspace, split,
+        seq_order)
     _check(lib().pa_prefill(out.data_ptr(), q.data_ptr(), T, k_cache.data_ptr(), v_cache.data_ptr(),
                             block_tables.data_ptr(), block_tables.shape[1], context_lens.data_ptr(),
                             query_start.data_ptr(), S, H, Hkv, D, B, NB, float(scale), mq,
-                            ws_ptr, ws_bytes, PA_DTYPE_F16, _stream(q.device)), "pa_prefill")
+                            ws_ptr, ws_bytes, order_ptr, PA_DTYPE_F16, _stream(q.device)), "pa_prefill")
 
 
 def pa_prefill_append(out, q, key, value, k_cache, v_cache, block_tables, context_lens, query_start, scale: float,
-                      max_query_len: Optional[int] = None, workspace=None, split: bool = True) -> None:
+                      max_query_len: Optional[int] = None, workspace=None, split: bool = True,
+                      seq_order=None) -> None:
     """pa_reshape_and_cache of the new tokens followed by pa_prefill, in one
     call: key/value [T, Hkv, D] (fp16, head_dim contiguous, any 16-byte
     aligned token stride) hold the K/V of the token in the same row of q; each
     is written into the cache at its position's slot of block_tables and
     attended to with the cached ones."""
     torch = _torch()
-    T, S, H, Hkv, D, B, NB, mq, ws_ptr, ws_bytes = _prefill_args(
-        out, q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len, workspace, split)
+    T, S, H, Hkv, D, B, NB, mq, ws_ptr, ws_bytes, order_ptr = _prefill_args(
+        out, q, k_cache, v_cache, block_tables, context_lens, query_start, max_query_len, workspace, split,
+        seq_order)
     _dev_tensor(key, "key", torch.float16, 3, contiguous=False)
     _dev_tensor(value, "value", torch.float16, 3, contiguous=False)
     if tuple(key.shape) != (T, Hkv, D) or tuple(value.shape) != (T, Hkv, D):
@@ -418,7 +429,8 @@ def pa_prefill_append(out, q, key, value, k_cache, v_cache, block_tables, contex
     _check(lib().pa_prefill_append(out.data_ptr(), q.data_ptr(), T, key.data_ptr(), value.data_ptr(), key.stride(0),
                                    k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
                                    block_tables.shape[1], context_lens.data_ptr(), query_start.data_ptr(), S, H, Hkv,
-                                   D, B, NB, float(scale), mq, ws_ptr, ws_bytes, PA_DTYPE_F16, _stream(q.device)),
+                                   D, B, NB, float(scale), mq, ws_ptr, ws_bytes, order_ptr, PA_DTYPE_F16,
+                                   _stream(q.device)),
            "pa_prefill_append")
 
 

@@ -711,7 +711,8 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
                     float* __restrict__ ws_ml, float* __restrict__ ws_acc, int32_t tiles_per_part,
                     int32_t num_parts, int32_t num_seqs, int32_t row_tiles, int32_t xcd_grouped,
                     const _Float16* __restrict__ new_k, const _Float16* __restrict__ new_v, int64_t new_stride,
-                    _Float16* __restrict__ k_write, _Float16* __restrict__ v_write, unsigned* __restrict__ claim) {
+                    _Float16* __restrict__ k_write, _Float16* __restrict__ v_write, unsigned* __restrict__ claim,
+                    const int32_t* __restrict__ seq_order) {
     PF_GEO(D);
     // two stage buffers as distinct objects, so that the compiler can tell
     // the buffer a step reads from the one whose loads are in flight
@@ -727,7 +728,10 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
     // pair, which all walk the same K/V tiles, run together on one XCD and
     // share its L2.  Otherwise the pair is fastest (KV head first).  Either
     // way the last row tile of a pair comes first (the longest causal range
-    // starts earliest) and parts are fastest within a row tile.
+    // starts earliest) and parts are fastest within a row tile.  With
+    // seq_order the pairs' sequences are taken in that order (longest first,
+    // so that no long prompt's row tiles start last and run alone at the
+    // end).
     //
     // Persistent form (claim non-null): the grid is one round of resident
     // workgroups, a multiple of 8, and workgroup b takes items of XCD b % 8
@@ -780,7 +784,8 @@ prefill_mfma_kernel(_Float16* __restrict__ out, const _Float16* __restrict__ q, 
         rp = (uint32_t)item / (uint32_t)pairs;
     }
     const int kvh = (int)(pair % (uint32_t)num_kv_heads);
-    const int s = (int)(pair / (uint32_t)num_kv_heads);
+    const int s = seq_order ? seq_order[pair / (uint32_t)num_kv_heads] : (int)(pair / (uint32_t)num_kv_heads);
+    if ((uint32_t)s >= (uint32_t)num_seqs) break;           // an order entry outside the batch: skipped
     const int rtile = row_tiles - 1 - (int)(rp / (uint32_t)num_parts);
     const int part = (int)(rp % (uint32_t)num_parts);
     // the thread index passed through an opaque instruction on every item,
@@ -1081,11 +1086,14 @@ __global__ void __launch_bounds__(256)
 prefill_merge_kernel(_Float16* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_acc,
                      int32_t num_tokens, const int32_t* __restrict__ lens, const int32_t* __restrict__ query_start,
                      int32_t num_heads, int32_t num_kv_heads, int32_t max_query_len, int64_t len_cap,
-                     int32_t tiles_per_part, int32_t num_parts) {
+                     int32_t tiles_per_part, int32_t num_parts, const int32_t* __restrict__ seq_order) {
     PF_GEO(D);
     constexpr int kTok = kMergeThreads / D;      // tokens per workgroup
     const int h = blockIdx.x;
-    const int s = blockIdx.y;
+    // the sequences the first kernel did (an order entry outside the batch
+    // was skipped there too)
+    const int s = seq_order ? seq_order[blockIdx.y] : (int)blockIdx.y;
+    if ((uint32_t)s >= gridDim.y) return;
     const int d = threadIdx.x % D;
     const int g = num_heads / num_kv_heads;
     const int32_t q0 = query_start[s];
@@ -1121,7 +1129,7 @@ prefill_merge_kernel(_Float16* __restrict__ out, const float* __restrict__ ws_ml
 using PrefillFn = void (*)(_Float16*, const _Float16*, int32_t, const _Float16*, const _Float16*, const int32_t*,
                            int32_t, const int32_t*, const int32_t*, int32_t, int32_t, int32_t, float, int32_t,
                            int64_t, float*, float*, int32_t, int32_t, int32_t, int32_t, int32_t, const _Float16*,
-                           const _Float16*, int64_t, _Float16*, _Float16*, unsigned*);
+                           const _Float16*, int64_t, _Float16*, _Float16*, unsigned*, const int32_t*);
 
 template <int D, bool kStream, bool kAppend>
 PrefillFn pick(int32_t b) {
@@ -1175,7 +1183,7 @@ PrefillFn pick_persistent(int32_t d, int32_t b) {
 }
 
 using MergeFn = void (*)(_Float16*, const float*, const float*, int32_t, const int32_t*, const int32_t*, int32_t,
-                         int32_t, int32_t, int64_t, int32_t, int32_t);
+                         int32_t, int32_t, int64_t, int32_t, int32_t, const int32_t*);
 
 MergeFn pick_merge(int32_t d) {
     switch (d) {
@@ -1309,8 +1317,8 @@ int prefill_impl(const char* fn, void* out, const void* q, int32_t num_tokens, c
                  const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
                  const int32_t* context_lens, const int32_t* query_start, int32_t num_seqs, int32_t num_heads,
                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
-                 int32_t max_query_len, void* workspace, size_t workspace_bytes, int32_t dtype, void* stream,
-                 const PrefillAppend* app) {
+                 int32_t max_query_len, void* workspace, size_t workspace_bytes, const int32_t* seq_order,
+                 int32_t dtype, void* stream, const PrefillAppend* app) {
     if (dtype != PA_DTYPE_F16) return pa::fail(PA_ERR_UNSUPPORTED, "%s: dtype %d", fn, dtype);
     if (head_dim != 64 && head_dim != 128 && head_dim != 256)
         return pa::fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (64, 128 or 256)", fn, head_dim);
@@ -1414,7 +1422,7 @@ int prefill_impl(const char* fn, void* out, const void* q, int32_t num_tokens, c
                        (int32_t)row_tiles, (int32_t)(pairs % 8 == 0), app ? app->key : nullptr,
                        app ? app->value : nullptr, app ? app->stride : (int64_t)0,
                        app ? static_cast<_Float16*>(const_cast<void*>(k_cache)) : nullptr,
-                       app ? static_cast<_Float16*>(const_cast<void*>(v_cache)) : nullptr, claim);
+                       app ? static_cast<_Float16*>(const_cast<void*>(v_cache)) : nullptr, claim, seq_order);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
     if (P.num_parts > 1) {
@@ -1424,7 +1432,7 @@ int prefill_impl(const char* fn, void* out, const void* q, int32_t num_tokens, c
                            dim3((unsigned)kMergeThreads), 0, st, static_cast<_Float16*>(out), (const float*)ws_ml,
                            (const float*)ws_acc,
                            num_tokens, context_lens, query_start, num_heads, num_kv_heads, max_query_len, len_cap,
-                           P.tiles_per_part, P.num_parts);
+                           P.tiles_per_part, P.num_parts, seq_order);
         e = hipGetLastError();
         if (e != hipSuccess) return pa::fail(PA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
     }
@@ -1437,11 +1445,11 @@ extern "C" int pa_prefill(void* out, const void* q, int32_t num_tokens, const vo
                           const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                           const int32_t* query_start, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                           int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
-                          int32_t max_query_len, void* workspace, size_t workspace_bytes, int32_t dtype,
-                          void* stream) {
+                          int32_t max_query_len, void* workspace, size_t workspace_bytes,
+                          const int32_t* seq_order, int32_t dtype, void* stream) {
     return prefill_impl("pa_prefill", out, q, num_tokens, k_cache, v_cache, block_tables, max_blocks_per_seq,
                         context_lens, query_start, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                        scale, max_query_len, workspace, workspace_bytes, dtype, stream, nullptr);
+                        scale, max_query_len, workspace, workspace_bytes, seq_order, dtype, stream, nullptr);
 }
 
 extern "C" int pa_prefill_append(void* out, const void* q, int32_t num_tokens, const void* key, const void* value,
@@ -1449,9 +1457,10 @@ extern "C" int pa_prefill_append(void* out, const void* q, int32_t num_tokens, c
                                  int32_t max_blocks_per_seq, const int32_t* context_lens, const int32_t* query_start,
                                  int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                  int32_t block_size, int32_t num_blocks, float scale, int32_t max_query_len,
-                                 void* workspace, size_t workspace_bytes, int32_t dtype, void* stream) {
+                                 void* workspace, size_t workspace_bytes, const int32_t* seq_order, int32_t dtype,
+                                 void* stream) {
     const PrefillAppend app{static_cast<const _Float16*>(key), static_cast<const _Float16*>(value), kv_token_stride};
     return prefill_impl("pa_prefill_append", out, q, num_tokens, k_cache, v_cache, block_tables, max_blocks_per_seq,
                         context_lens, query_start, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                        scale, max_query_len, workspace, workspace_bytes, dtype, stream, &app);
+                        scale, max_query_len, workspace, workspace_bytes, seq_order, dtype, stream, &app);
 }

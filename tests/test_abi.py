@@ -180,10 +180,11 @@ def test_copy_blocks_rejects_bad_arguments():
 
 def _prefill_args(**kw):
     a = dict(out=16, q=16, T=4, k=16, v=16, tables=16, W=4, lens=16, qs=16, S=1, H=2, Hkv=2, D=128, B=16, NB=8,
-             scale=0.1, maxq=4, ws=None, wsb=0, dtype=0, stream=None)
+             scale=0.1, maxq=4, ws=None, wsb=0, order=None, dtype=0, stream=None)
     a.update(kw)
     return (a["out"], a["q"], a["T"], a["k"], a["v"], a["tables"], a["W"], a["lens"], a["qs"], a["S"], a["H"],
-            a["Hkv"], a["D"], a["B"], a["NB"], a["scale"], a["maxq"], a["ws"], a["wsb"], a["dtype"], a["stream"])
+            a["Hkv"], a["D"], a["B"], a["NB"], a["scale"], a["maxq"], a["ws"], a["wsb"], a["order"], a["dtype"],
+            a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
