@@ -226,9 +226,9 @@ int pa_decode_noalloc(void *out, const void *q, const void *k_cache,
                       int32_t partition_size, const int32_t *seq_order,
                       int32_t dtype, void *stream);
 
-/* Longest-first dispatch order for pa_decode and pa_prefill: seq_order (device, int32
- * [num_seqs], written) becomes a permutation of 0 .. num_seqs - 1 with the
- * sequences sorted by context_lens into 1024 classes of
+/* Longest-first dispatch order for pa_decode and pa_prefill: seq_order
+ * (device, int32 [num_seqs], written) becomes a permutation of 0 ..
+ * num_seqs - 1 with the sequences sorted by context_lens into 1024 classes of
  * max_context_len / 1024 + 1 tokens, longest class first (order within a
  * class unspecified).  Stream-ordered with the calls that use it. */
 int pa_decode_order(int32_t *seq_order, const int32_t *context_lens,
