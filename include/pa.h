@@ -260,7 +260,10 @@ int pa_decode_order(int32_t *seq_order, const int32_t *context_lens,
  *   workspace      device scratch of pa_prefill_workspace_size() bytes,
  *                  16-byte aligned, or NULL.  When the batch gives too few
  *                  workgroups to fill the GPU (few sequences or KV heads,
- *                  short chunks over long contexts) the context is split
+ *                  short chunks over long contexts) and the context bound
+ *                  max_blocks_per_seq * block_size is at least 8 times
+ *                  max_query_len (2 times when the row tiles give at most
+ *                  128 workgroups), the context is split
  *                  into parts whose partial results it holds, merged by a
  *                  second kernel; when it gives more than one round of
  *                  resident workgroups, one query head per KV head and at

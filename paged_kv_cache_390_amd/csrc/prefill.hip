@@ -1228,6 +1228,16 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // more than it brings: on 4 x 8192 cached + 32 new, with 32-token tiles,
 // 512 workgroups ran in 113 us, 768 in 149, 1024 in 147, 2048 in 203.)  The
 // bound on the context is max_blocks_per_seq * block_size (host-known).
+// Only a context long against the new tokens is split: at least 8 times
+// max_query_len, or 2 times when the row tiles give at most 128 workgroups.
+// The partial states cost (2 + D) x 4 bytes per (token, head, part),
+// written and read back, against 4 x D bytes of K/V per (position, KV head)
+// read once.  Measured per call (32 / 32 heads, head_dim 128, split against
+// unsplit): a whole 774 / 1024-token prompt 45.0 / 55.1 against 29.9 / 37.9
+// us (29.9 against 45.1 at 32 / 8 heads), 2 x (2048 positions, 512 new) at
+// 32 / 8 heads 76.9 against 68.2; 512 new over 1536 / 2048 / 4096
+// positions 45.8 / 53.3 / 76.2 against 52.2 / 68.4 / 131.3, 256 over 2048
+// 39.5 against 68.2, 1024 over 8192 198.2 against 255.7.
 // Workspace bytes of the persistent grid's claim counters (8 used).
 constexpr size_t kClaimBytes = 256;
 
@@ -1269,7 +1279,9 @@ SplitPlan split_plan(int32_t num_tokens, int32_t num_seqs, int32_t num_heads, in
     const int64_t min_tiles_per_part = 256 / hg.kv_tile;
     const int64_t wgs = (int64_t)num_kv_heads * num_seqs * P.row_tiles;
     int64_t parts = 1;
-    if (wgs > 0 && 2 * wgs <= 512 && max_tiles >= 2 * min_tiles_per_part) {
+    const int64_t mq = max_query_len > 0 ? max_query_len : 1;
+    const bool long_context = len_cap >= 8 * mq || (len_cap >= 2 * mq && 4 * wgs <= 512);
+    if (wgs > 0 && 2 * wgs <= 512 && max_tiles >= 2 * min_tiles_per_part && long_context) {
         parts = 512 / wgs;
         if (parts > max_tiles / min_tiles_per_part) parts = max_tiles / min_tiles_per_part;
         if (parts * P.row_tiles > 65535) parts = 65535 / P.row_tiles;

@@ -243,13 +243,20 @@ def test_prefill_append_with_nothing_to_do_is_a_no_op():
 
 def test_prefill_workspace_size():
     """256 bytes (the persistent grid's claim counters) when the batch has
-    more than 256 workgroups unsplit; zero when fewer and too short to split;
-    otherwise (2 + D) x 4 bytes per (token, head, context part), two 256-byte
-    aligned regions."""
+    more than 256 workgroups unsplit; zero when fewer and too short to split
+    or when the context bound is short against max_query_len (under 8x, or
+    under 2x with at most 128 workgroups); otherwise (2 + D) x 4 bytes per
+    (token, head, context part), two 256-byte aligned regions."""
     L = pa.lib()
     assert L.pa_prefill_workspace_size(15360, 32, 32, 32, 128, 16, 49, 774) == 256      # 32 x 32 x 7 = 7168 workgroups
     assert L.pa_prefill_workspace_size(2048, 8, 32, 8, 128, 16, 16, 256) == 256         # 8 x 8 x 8 = 512 workgroups
     assert L.pa_prefill_workspace_size(256, 2, 32, 32, 128, 16, 16, 128) == 0           # 64 workgroups, 256 tokens
+    # a whole prompt is not split (its context is no longer than its new tokens): 224 workgroups, nothing kept
+    assert L.pa_prefill_workspace_size(774, 1, 32, 32, 128, 16, 49, 774) == 0
+    assert L.pa_prefill_workspace_size(774, 1, 32, 8, 128, 16, 49, 774) == 0
+    # 512 new over contexts up to 2048 (4x): split at 128 workgroups, not at 256
+    assert L.pa_prefill_workspace_size(512, 1, 32, 32, 128, 16, 128, 512) > 256
+    assert L.pa_prefill_workspace_size(1024, 2, 32, 8, 128, 16, 128, 512) == 0
     # longer chunks split too while their workgroups fill at most half the 512 resident slots: 300 rows per KV
     # head are 3 row tiles, 3 x 4 x 3 = 36 workgroups, contexts up to 3008 tokens
     n3 = L.pa_prefill_workspace_size(561, 3, 4, 4, 128, 16, 188, 300)
